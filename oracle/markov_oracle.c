@@ -23,8 +23,9 @@
  * is done in fp32 with IEEE round-to-nearest-even; the inverse CDF is built in
  * fp64.
  *
- * Parity unpinned: the exact bit pattern of fp32 logf/tanhf (host libm here,
- * the device library on the GPU).  Everything else has a pin in the tests.
+ * Parity unpinned: the exact bit pattern of fp32 tanhf and of the fp64 log
+ * behind the fp32 logarithms (host libm here, the device library on the GPU).
+ * Everything else has a pin in the tests.
  */
 #include <math.h>
 #include <stdint.h>
@@ -110,8 +111,12 @@ float orc_uniform(uint64_t h) {
   return (float)(2 * k + 1) * 0x1p-24f;
 }
 
-/* Standard Gumbel draw -log(-log u) in fp32, as the pages' fp32 noise. */
-float orc_gumbel(float u) { return -logf(-logf(u)); }
+/* Standard Gumbel draw -log(-log u) in fp32, as the pages' fp32 noise.
+ * Each fp32 logarithm is the correctly rounded one: the natural log of the
+ * fp32 argument taken in fp64 and rounded once to fp32 (libm logf is only
+ * faithfully rounded, so two libms would disagree in the last bit). */
+static float orc_log_f32(float x) { return (float)log((double)x); }
+float orc_gumbel(float u) { return -orc_log_f32(-orc_log_f32(u)); }
 
 /* gumbel[row][step][v] for rows x steps x V (contiguous). */
 void orc_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
