@@ -1,0 +1,204 @@
+/*
+ * markov.h -- C ABI of libmarkov, the MI355X (gfx950) DSpark sequential
+ * Markov draft-sampling chain.
+ *
+ * The method (vLLM API page "vllm.models.deepseek_v41.nvidia.specialized_
+ * decode.sampling.sharded_markov", module docstring and its per-call
+ * diagram): after the draft backbone has produced base logits for N draft
+ * positions, the draft tokens are drawn one position at a time.  Position i
+ * adds the low-rank transition bias bf16(markov_head[V, r] . markov_embed
+ * [previous token]) to its base logits, rounds the result into a bf16
+ * draft-logits cache, and samples the token; that token is the previous token
+ * of position i + 1.
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked "device" are HIP device pointers owned by the caller; the
+ *    library never allocates, frees or retains device memory.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *    Calls only enqueue work on it and never synchronise the host (except
+ *    markov_status), so they can be captured in a HIP graph.
+ *  - bf16 tensors are passed as uint16_t bit patterns.  Strides are counted in
+ *    elements.
+ *  - Every call returns a markov_status_t.  On an error nothing is enqueued
+ *    and markov_last_error() gives the reason (a thread-local string).
+ */
+#ifndef LIBMARKOV_MARKOV_H
+#define LIBMARKOV_MARKOV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MARKOV_OK = 0,
+  MARKOV_E_INVAL = -1,       /* a null pointer, bad size, stride or alignment */
+  MARKOV_E_UNSUPPORTED = -2, /* a shape the kernels do not take (reason given) */
+  MARKOV_E_HIP = -3,         /* a HIP runtime call failed (reason given) */
+  MARKOV_E_DEVICE = -4       /* markov_status: the kernel set an error bit */
+} markov_status_t;
+
+/* Sampling modes. */
+#define MARKOV_MODE_GUMBEL 0 /* max of logit / T + gumbel (sharded_markov page) */
+#define MARKOV_MODE_INVCDF 1 /* inverse CDF of softmax(logit / T) (fused_markov page) */
+
+/* Limits of this build. */
+#define MARKOV_MAX_ROWS 64
+#define MARKOV_MAX_STEPS 256
+#define MARKOV_MAX_VOCAB (1 << 24)
+
+/* Device error bits reported by markov_status. */
+#define MARKOV_DEVERR_BAD_TOKEN 1u /* a previous token outside [0, V): row made inert */
+#define MARKOV_DEVERR_TIMEOUT 2u   /* a cross-workgroup wait exceeded its bound */
+#define MARKOV_DEVERR_BAD_STATE 4u /* a state index >= cache_states: row made inert */
+
+/*
+ * markov_workspace_bytes: bytes of device workspace markov_chain_sample needs
+ * for this call shape (rows request rows, `steps` positions, vocabulary
+ * `vocab`, rank dim `rank`, sampling `mode`).  Returns 0 for an unsupported
+ * shape.  Host only.
+ *
+ * The workspace holds the per-position exchange slots of the workgroups (two
+ * halves used by alternate calls) and a small header (call parity, error
+ * word).  The caller allocates it, zeroes it ONCE, and passes the same
+ * pointer and the same workspace_bytes to every later call; the kernel
+ * leaves it ready for the next call, so graph replays need no memset.  One
+ * workspace serves one call at a time: calls that overlap in time (e.g. on
+ * two streams) must use different workspaces.  Size it for the largest call
+ * shape it will serve.
+ */
+size_t markov_workspace_bytes(int rows, int steps, int vocab, int rank, int mode);
+
+/*
+ * markov_noise_fill: the chain's Gumbel noise, gumbel[row][i][v] =
+ * -log(-log(u)) in fp32, u the uniform of a counter-based hash of
+ * (seeds[row], row, i, v) with v the global vocabulary id.
+ *
+ * sharded_markov page, module docstring and fork_noise: the noise depends
+ * on the seeds and positions only, never on the chain, so it is drawn on a
+ * side stream while the draft LM head runs.  The hash is SplitMix64 (Steele,
+ * Lea and Flood, OOPSLA 2014): h = sm(seed); h = sm(h ^ row); h = sm(h ^ i);
+ * h = sm(h ^ v), where sm(x) is one SplitMix64 output for state x; the top
+ * 23 bits k of h give u = (2k + 1) * 2^-24.
+ *
+ *   gumbel  device, fp32 [rows][steps][vocab], contiguous, 16-byte aligned,
+ *           written.
+ *   seeds   device, int64 [rows]; the int64 bits are used as uint64.
+ *   rows in [1, MARKOV_MAX_ROWS], steps in [1, MARKOV_MAX_STEPS], vocab a
+ *   positive multiple of 16 up to MARKOV_MAX_VOCAB.
+ */
+int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
+                      int vocab, void* stream);
+
+/*
+ * markov_chain_sample: the whole N-position chain for `rows` request rows in
+ * one persistent cooperative launch.
+ *
+ * For each row b with state s = state_idx[b] >= 0, starting from
+ * p = prev_tokens[b], for i = 0 .. steps-1 in order
+ * (sharded_markov page, module docstring and per-call diagram;
+ *  muse_spark markov page, FusedMarkovParams and fused_markov_params):
+ *   bias[v]  = bf16( sum_k head[v][k] * embed[p][k] ), fp32 accumulation
+ *   x[v]     = f32(base[b][i][v]) + f32(bias[v])
+ *   x[v]     = x[v] * output_multiplier;
+ *              if soft_cap > 0: x[v] = tanhf(x[v] * (1 / soft_cap)) * soft_cap
+ *   cache[s][i][v] = c[v] = bf16(x[v])                      (round to nearest even)
+ *   MARKOV_MODE_GUMBEL: score[v] = f32(c[v]) / T[b] + gumbel[b][i][v] if
+ *            T[b] > 0, else f32(c[v]); the token is the lowest v whose score
+ *            is NaN if any, else the lowest v of the maximum score.
+ *   MARKOV_MODE_INVCDF (fused_markov page, module docstring): with T[b] > 0,
+ *            the token is drawn by inverse CDF of softmax(f32(c) / T[b]) in
+ *            vocabulary order at u = uniform(hash(seeds[b], b, i)) (the hash
+ *            above without the vocabulary id); NaN and +inf maxima and
+ *            T[b] <= 0 fall back to the argmax rule above.
+ *   draft_tokens[b][i] = token; p = token.
+ * Rows with state_idx[b] < 0 are padding: nothing of theirs is read or
+ * written (muse_spark/sharded_markov pages: padding rows are inert).
+ *
+ *   base_logits     device, bf16 [rows][steps][>= vocab] with row stride
+ *                   base_row_stride and step stride base_step_stride
+ *                   (elements, multiples of 8), 16-byte aligned, read.
+ *   head, embed     device, bf16 [>= vocab][rank], contiguous, 16-byte
+ *                   aligned, read.  head is the Markov w2 (the bias head),
+ *                   embed the Markov w1 (the embedding of the previous token).
+ *   prev_tokens     device, int64 [rows]: each row's anchor token.  A value
+ *                   outside [0, vocab) sets MARKOV_DEVERR_BAD_TOKEN and makes
+ *                   the row inert.
+ *   temperature     device, fp32 [rows].
+ *   seeds           device, int64 [rows]; read in MARKOV_MODE_INVCDF only
+ *                   (may be NULL in MARKOV_MODE_GUMBEL).
+ *   gumbel          device, fp32 [rows][steps][vocab] contiguous, as
+ *                   markov_noise_fill writes it; read in MARKOV_MODE_GUMBEL
+ *                   only (may be NULL in MARKOV_MODE_INVCDF).
+ *   state_idx       device, int64 [rows], or NULL for the identity; negative
+ *                   marks a padding row.  Distinct non-negative entries.
+ *   output_multiplier  fp32 multiplier (1.0f: none); finite.
+ *   soft_cap        fp32 soft cap (0: none); finite, >= 0.
+ *   rows in [1, MARKOV_MAX_ROWS]; steps in [1, MARKOV_MAX_STEPS]; vocab a
+ *   positive multiple of 16 up to MARKOV_MAX_VOCAB; rank 256 or 512;
+ *   mode MARKOV_MODE_GUMBEL or MARKOV_MODE_INVCDF.
+ *   draft_tokens    device, int64 [rows][>= steps], row stride
+ *                   tokens_row_stride, written for non-padding rows.
+ *   cache           device, bf16 [cache_states][steps][>= vocab] with state
+ *                   stride cache_state_stride and step stride
+ *                   cache_step_stride (multiples of 8), 16-byte aligned,
+ *                   written at cache[state_idx[b]][i][0 .. vocab).  A state
+ *                   index >= cache_states sets MARKOV_DEVERR_BAD_STATE and
+ *                   makes the row inert; without state_idx, cache_states must
+ *                   be >= rows.
+ *   workspace       device, markov_workspace_bytes(...) bytes or more,
+ *                   256-byte aligned, zeroed once before the first call.
+ *
+ * Errors: MARKOV_E_INVAL / MARKOV_E_UNSUPPORTED for bad arguments (checked on
+ * the host before anything is enqueued), MARKOV_E_HIP if the launch fails
+ * (e.g. the grid cannot be co-resident).  Device-side conditions (bad anchor
+ * token, a wait that timed out) are reported by markov_status.
+ */
+int markov_chain_sample(const uint16_t* base_logits, int64_t base_row_stride,
+                        int64_t base_step_stride, const uint16_t* head,
+                        const uint16_t* embed, const int64_t* prev_tokens,
+                        const float* temperature, const int64_t* seeds,
+                        const float* gumbel, const int64_t* state_idx,
+                        float output_multiplier, float soft_cap, int rows,
+                        int steps, int vocab, int rank, int mode,
+                        int64_t* draft_tokens, int64_t tokens_row_stride,
+                        uint16_t* cache, int64_t cache_states,
+                        int64_t cache_state_stride, int64_t cache_step_stride,
+                        void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * markov_status: synchronises `stream`, then reads and clears the device
+ * error word of `workspace` (sharded_markov page, DSparkShardedMarkovSampler:
+ * cross-workgroup waits are bounded and report instead of hanging).
+ * Returns MARKOV_OK, or MARKOV_E_DEVICE with the error bits described by
+ * markov_last_error().  After a MARKOV_DEVERR_TIMEOUT the workspace must be
+ * zeroed again before the next call.
+ */
+int markov_status(void* workspace, void* stream);
+
+/* markov_last_error: the reason for the calling thread's last error ("" if
+ * none).  The pointer stays valid until the thread's next libmarkov call. */
+const char* markov_last_error(void);
+
+/*
+ * markov_set_grid: tuning and testing knob.  0 (the default) lets the library
+ * pick the number of persistent workgroups; g > 0 asks for at most g (clamped
+ * to what the device can hold co-resident and to the work available).  The
+ * chain's outputs do not depend on it.  Process-wide; returns the previous
+ * value.
+ */
+int markov_set_grid(int g);
+
+/* markov_grid: the number of workgroups markov_chain_sample would launch for
+ * this shape on the current device under the current markov_set_grid value,
+ * or a negative markov_status_t.  Host only. */
+int markov_grid(int rows, int steps, int vocab, int rank, int mode);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMARKOV_MARKOV_H */

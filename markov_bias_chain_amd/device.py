@@ -1,0 +1,74 @@
+"""Device buffers for one chain call: upload a synthetic workload, allocate
+the outputs and the workspace, and run the two C-ABI calls on torch streams.
+Marshalling only; the arithmetic is in libmarkov.so."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import binding as lm
+from .synth import Workload
+
+
+def to_device_bf16(bits: np.ndarray, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class DeviceChain:
+    """All device tensors of one workload, allocated once (so a HIP graph or
+    a timing loop sees fixed addresses)."""
+
+    def __init__(self, w: Workload, device="cuda", token_fill: int = -7, cache_fill: int = 0xABCD):
+        self.w = w
+        dev = torch.device(device)
+        self.device = dev
+        self.head = to_device_bf16(w.head, dev)
+        self.embed = to_device_bf16(w.embed, dev)
+        self.base = to_device_bf16(w.base, dev)
+        self.prev = torch.from_numpy(w.prev).to(dev)
+        self.seeds = torch.from_numpy(w.seeds).to(dev)
+        self.temperature = torch.from_numpy(w.temperature).to(dev)
+        self.state_idx = None if w.state_idx is None else torch.from_numpy(w.state_idx).to(dev)
+        self.gumbel = torch.empty((w.rows, w.N, w.V), dtype=torch.float32, device=dev) \
+            if w.mode == 0 else None
+        self.tokens = torch.full((w.rows, w.N), token_fill, dtype=torch.int64, device=dev)
+        fill = cache_fill - 0x10000 if cache_fill >= 0x8000 else cache_fill  # as int16 bits
+        self.cache = torch.full((w.states, w.N, w.V), fill, dtype=torch.int16,
+                                device=dev).view(torch.bfloat16)
+        self.workspace = lm.markov_workspace(w.rows, w.N, w.V, w.r, w.mode, device=dev)
+        self.side = torch.cuda.Stream(dev)
+
+    def set_gumbel(self, g: np.ndarray) -> None:
+        """Use the given noise (e.g. drawn by another implementation)."""
+        self.gumbel.copy_(torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)))
+
+    def noise(self, stream=None) -> None:
+        lm.markov_noise_fill(self.gumbel, self.seeds, stream=stream)
+
+    def chain(self, stream=None) -> None:
+        w = self.w
+        lm.markov_chain_sample(
+            self.base, self.head, self.embed, self.prev, self.temperature, self.tokens,
+            self.cache, self.workspace, gumbel=self.gumbel, seeds=self.seeds,
+            state_idx=self.state_idx, output_multiplier=w.mult, soft_cap=w.cap,
+            mode=w.mode, stream=stream)
+
+    def step(self) -> None:
+        """One pass of the hot path: the noise on a side stream forked after
+        the current stream's work and joined before the chain, then the chain."""
+        cur = torch.cuda.current_stream(self.device)
+        if self.w.mode == 0:
+            self.side.wait_stream(cur)
+            self.noise(stream=self.side)
+            cur.wait_stream(self.side)
+        self.chain(stream=cur)
+
+    def results(self):
+        """(tokens int64 [rows, N], cache uint16 [states, N, V]) on the host."""
+        torch.cuda.synchronize(self.device)
+        return self.tokens.cpu().numpy(), bf16_bits(self.cache)

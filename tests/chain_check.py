@@ -1,0 +1,148 @@
+"""Comparison of a chain call's outputs with the CPU oracle.
+
+The walk follows each row position by position with the oracle's own
+tokens.  At every position it checks:
+  * cache: the device row equals the oracle's within one bf16 ulp (adjacent
+    bf16 values), with the same NaN-ness; exact matches are counted;
+  * token: equal to the oracle's.  A different token is accepted only when
+    the device's own cache explains it (the device token is what the
+    sampling rule gives on the device cache, evaluated here in the same fp32
+    precision), the two caches differ, and the oracle's decision margin is
+    within what those cache differences can move; the row's walk then stops,
+    since later positions follow a different previous token.
+For the inverse CDF, a draw whose u * S falls within WINDOW * S of a bin
+edge may also land in the neighbouring bin (fp32 partial sums on the device,
+fp64 on the oracle).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+import oracle
+
+# fp32 blockwise sums of exp: a few dozen roundings of 2^-24 relative to S,
+# bounded well inside 2^-16 (see the derivation in the design notes).
+WINDOW = 2.0**-16
+
+
+def f32(bits):
+    return oracle.bf16_to_f32(bits)
+
+
+def ordinal(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns on a monotone integer line (+0 and -0 both 0)."""
+    b = bits.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def is_nan_bits(bits: np.ndarray) -> np.ndarray:
+    return ((bits & 0x7F80) == 0x7F80) & ((bits & 0x7F) != 0)
+
+
+def pick_max(s: np.ndarray) -> int:
+    """Lowest NaN index, else lowest index of the maximum (numpy argmax
+    returns the first NaN or the first maximum)."""
+    return int(np.argmax(s))
+
+
+def scores(c_bits, T, g):
+    cf = f32(c_bits)
+    if T > 0:
+        s = cf / np.float32(T)
+        if g is not None:
+            s = s + g
+        return s.astype(np.float32)
+    return cf.astype(np.float32)
+
+
+def inv_cdf_bin(c_bits, T, u):
+    """(bin, cdf, t) of the fp64 inverse CDF of softmax(f32(c) / T)."""
+    z = (f32(c_bits) / np.float32(T)).astype(np.float64)
+    e = np.exp(z - z.max())
+    cdf = np.cumsum(e)
+    t = float(u) * cdf[-1]
+    k = int(np.searchsorted(cdf, t, side="right"))
+    return min(k, len(cdf) - 1), cdf, t
+
+
+@dataclasses.dataclass
+class Stats:
+    pairs: int = 0
+    token_match: int = 0
+    mismatches: list = dataclasses.field(default_factory=list)
+    cache_elems: int = 0
+    cache_exact: int = 0
+    walked_rows: int = 0
+
+    def summary(self) -> str:
+        return (f"pairs={self.pairs} token_match={self.token_match} "
+                f"mismatch={len(self.mismatches)} cache_exact={self.cache_exact}/{self.cache_elems}")
+
+
+def walk(w, tok_gpu, cache_gpu, gumbel, rows=None, exact=False) -> Stats:
+    """Walk `rows` (default: all) of workload w; gumbel[rows, N, V] is the
+    noise both sides used (mode 0).  exact=True demands bit-identical caches
+    and tokens."""
+    st = Stats()
+    sidx = np.arange(w.rows) if w.state_idx is None else w.state_idx
+    rows = range(w.rows) if rows is None else rows
+    V = w.V
+    for b in rows:
+        s = int(sidx[b])
+        if s < 0:
+            continue
+        st.walked_rows += 1
+        p = int(w.prev[b])
+        T = float(w.temperature[b])
+        for i in range(w.N):
+            g = gumbel[b, i] if (w.mode == 0 and gumbel is not None) else None
+            u = oracle.uniform(oracle.hash_step(int(w.seeds[b]), b, i)) if w.mode == 1 else 0.0
+            tok_o, c_o, diag = oracle.step(w.base[b, i], w.head, w.embed, p, T, g, u=u,
+                                           mult=w.mult, cap=w.cap, mode=w.mode, with_diag=True)
+            c_g = cache_gpu[s, i, :V]
+            nan_o, nan_g = is_nan_bits(c_o), is_nan_bits(c_g)
+            assert np.array_equal(nan_o, nan_g), f"row {b} step {i}: NaN positions differ"
+            d = np.abs(ordinal(c_o) - ordinal(c_g))
+            d[nan_o] = 0
+            st.cache_elems += V
+            same = (d == 0)
+            st.cache_exact += int(same.sum())
+            if exact:
+                assert same.all(), f"row {b} step {i}: {int((~same).sum())} cache elements differ"
+            else:
+                assert d.max() <= 1, f"row {b} step {i}: cache differs by {int(d.max())} bf16 ulp"
+            t_g = int(tok_gpu[b, i])
+            st.pairs += 1
+            if t_g == tok_o:
+                st.token_match += 1
+                p = tok_o
+                continue
+            assert not exact, f"row {b} step {i}: token {t_g} != oracle {tok_o}"
+            assert 0 <= t_g < V, f"row {b} step {i}: token {t_g} out of range"
+            caches_differ = not same.all()
+            if w.mode == 0 or T <= 0 or diag[3] == 1.0:
+                # Argmax-type decision: the device token must be the rule's
+                # pick on the device cache (+ the same noise), and the oracle's
+                # margin must be within the score change the cache moved.
+                s_g = scores(c_g, T, g if w.mode == 0 else None)
+                s_o = scores(c_o, T, g if w.mode == 0 else None)
+                assert t_g == pick_max(s_g), f"row {b} step {i}: device token is not its own argmax"
+                assert caches_differ, f"row {b} step {i}: identical caches but tokens differ"
+                moved = abs(float(s_o[tok_o]) - float(s_g[tok_o])) + abs(float(s_o[t_g]) - float(s_g[t_g]))
+                margin = float(diag[0]) - float(s_o[t_g])
+                assert margin <= moved + 1e-12, f"row {b} step {i}: margin {margin} > moved {moved}"
+            else:
+                k_g, cdf, t = inv_cdf_bin(c_g, T, u)
+                if t_g != k_g:
+                    edge = cdf[min(t_g, k_g)]
+                    assert abs(t - edge) <= WINDOW * cdf[-1] and abs(t_g - k_g) == 1, \
+                        f"row {b} step {i}: device bin {t_g} vs its own cache's {k_g}"
+                assert caches_differ or diag[2] <= WINDOW, \
+                    f"row {b} step {i}: identical caches, bin {t_g} vs {tok_o}, edge distance {diag[2]}"
+            st.mismatches.append((b, i, tok_o, t_g))
+            break  # later positions would follow a different previous token
+    return st

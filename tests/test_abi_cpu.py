@@ -1,0 +1,121 @@
+"""The C-ABI library loads, exports every symbol include/markov.h declares,
+and rejects bad arguments on the host before any GPU work (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from markov_bias_chain_amd import binding as lm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "markov.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(markov_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_symbols() == sorted(lm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(lm.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_workspace_bytes():
+    # header + two halves of 8-byte keys for N x rows x chunks (512-id chunks at r=256)
+    chunks = -(-129280 // 512)
+    half = -(-(8 * 1 * chunks * 8) // 256) * 256
+    assert lm.markov_workspace_bytes(1, 8, 129280, 256, 0) == 256 + 2 * half
+    # mode 1 adds 4-byte sums and two 8-byte words per (step, row)
+    half1 = -(-(8 * 64 * chunks * 12 + 8 * 64 * 16) // 256) * 256
+    assert lm.markov_workspace_bytes(64, 8, 129280, 256, 1) == 256 + 2 * half1
+    # r=512 chunks hold 256 ids
+    half5 = -(-(16 * 8 * (262144 // 256) * 8) // 256) * 256
+    assert lm.markov_workspace_bytes(8, 16, 262144, 512, 0) == 256 + 2 * half5
+
+
+@pytest.mark.parametrize("args", [
+    (0, 8, 1024, 256, 0),      # rows
+    (65, 8, 1024, 256, 0),
+    (1, 0, 1024, 256, 0),      # steps
+    (1, 257, 1024, 256, 0),
+    (1, 8, 1000, 256, 0),      # vocab % 16
+    (1, 8, 0, 256, 0),
+    (1, 8, 1024, 128, 0),      # rank
+    (1, 8, 1024, 384, 0),
+    (1, 8, 1024, 256, 2),      # mode
+])
+def test_unsupported_shapes(args):
+    lib = lm.load()
+    assert lib.markov_workspace_bytes(*args) == 0
+    assert lib.markov_grid(*args) == lm.MARKOV_E_UNSUPPORTED
+    assert lm.markov_last_error() != ""
+
+
+def _sample(**kw):
+    """markov_chain_sample with fake (never dereferenced) aligned pointers:
+    argument checks run on the host before any HIP call."""
+    lib = lm.load()
+    P = 1 << 20  # a 256-byte aligned dummy address
+    a = dict(base=P, brs=8 * 1024, bss=1024, head=P, embed=P, prev=P, temp=P, seeds=P,
+             gumbel=P, sidx=None, mult=1.0, cap=0.0, rows=1, steps=8, vocab=1024, rank=256,
+             mode=0, tok=P, trs=8, cache=P, states=1, crs=8 * 1024, css=1024, ws=P,
+             wsb=lm.markov_workspace_bytes(1, 8, 1024, 256, 0), stream=None)
+    a.update(kw)
+    return lib.markov_chain_sample(
+        a["base"], a["brs"], a["bss"], a["head"], a["embed"], a["prev"], a["temp"], a["seeds"],
+        a["gumbel"], a["sidx"], a["mult"], a["cap"], a["rows"], a["steps"], a["vocab"],
+        a["rank"], a["mode"], a["tok"], a["trs"], a["cache"], a["states"], a["crs"], a["css"], a["ws"],
+        a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(base=None), lm.MARKOV_E_INVAL),
+    (dict(head=None), lm.MARKOV_E_INVAL),
+    (dict(gumbel=None), lm.MARKOV_E_INVAL),                     # mode 0 needs noise
+    (dict(mode=1, seeds=None, gumbel=None), lm.MARKOV_E_INVAL),  # mode 1 needs seeds
+    (dict(cache=(1 << 20) + 2), lm.MARKOV_E_INVAL),             # unaligned
+    (dict(ws=(1 << 20) + 16), lm.MARKOV_E_INVAL),               # workspace alignment
+    (dict(bss=1000), lm.MARKOV_E_INVAL),                        # step stride < vocab
+    (dict(css=1028), lm.MARKOV_E_INVAL),                        # stride % 8
+    (dict(wsb=64), lm.MARKOV_E_INVAL),                          # workspace too small
+    (dict(cap=-1.0), lm.MARKOV_E_INVAL),
+    (dict(mult=float("inf")), lm.MARKOV_E_INVAL),
+    (dict(states=0), lm.MARKOV_E_INVAL),
+    (dict(rows=2, states=1, trs=8), lm.MARKOV_E_INVAL),          # no state_idx: states >= rows
+    (dict(rank=384), lm.MARKOV_E_UNSUPPORTED),
+    (dict(rows=65), lm.MARKOV_E_UNSUPPORTED),
+])
+def test_invalid_arguments_rejected_on_host(kw, code):
+    assert _sample(**kw) == code
+    assert lm.markov_last_error()
+
+
+def test_noise_fill_rejects_bad_arguments():
+    lib = lm.load()
+    P = 1 << 20
+    assert lib.markov_noise_fill(None, P, 1, 1, 16, None) == lm.MARKOV_E_INVAL
+    assert lib.markov_noise_fill(P + 4, P, 1, 1, 16, None) == lm.MARKOV_E_INVAL
+    assert lib.markov_noise_fill(P, P, 1, 1, 20, None) == lm.MARKOV_E_UNSUPPORTED
+    assert lib.markov_noise_fill(P, P, 0, 1, 16, None) == lm.MARKOV_E_UNSUPPORTED
+
+
+def test_set_grid_roundtrip():
+    old = lm.markov_set_grid(7)
+    assert lm.markov_set_grid(old) == 7
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    w = torch.zeros(4, dtype=torch.float32)
+    s = torch.zeros(1, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        lm.markov_noise_fill(w.view(1, 1, 4), s)

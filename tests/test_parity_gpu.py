@@ -1,0 +1,297 @@
+"""Parity of the HIP chain (through the C ABI) with the CPU oracle.
+
+All inputs are seeded synthetic workloads (markov_bias_chain_amd.synth).
+Mode-0 parity runs both sides on the same Gumbel noise, drawn by the oracle
+on the host and uploaded; the device noise kernel is checked against the
+oracle's noise separately.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import chain_check
+import oracle
+from markov_bias_chain_amd import binding as lm
+from markov_bias_chain_amd import synth
+from markov_bias_chain_amd.device import DeviceChain
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _gpu_and_grid():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    lm.load()
+    old = lm.markov_set_grid(0)
+    yield
+    lm.markov_set_grid(old)
+    torch.cuda.synchronize()
+
+
+def run(w, gumbel=None, grid=0, calls=1):
+    """Run the chain on the device; gumbel (numpy) if given, else the
+    device noise kernel.  Returns (tokens, cache bits, DeviceChain)."""
+    lm.markov_set_grid(grid)
+    d = DeviceChain(w)
+    say(f"  device call: {w.name} V={w.V} r={w.r} rows={w.rows} N={w.N} mode={w.mode} "
+        f"grid={lm.markov_grid(w.rows, w.N, w.V, w.r, w.mode)}")
+    for _ in range(calls):
+        if w.mode == 0:
+            if gumbel is not None:
+                d.set_gumbel(gumbel)
+            else:
+                d.noise()
+        d.chain()
+    lm.markov_status(d.workspace)
+    t, c = d.results()
+    return t, c, d
+
+
+def oracle_noise(w):
+    return oracle.noise_fill(w.seeds, w.N, w.V) if w.mode == 0 else None
+
+
+# ------------------------------------------------------------------ noise --
+
+@pytest.mark.parametrize("rows,N,V", [(1, 4, 8192), (3, 5, 4096), (2, 2, 129280)])
+def test_noise_fill_matches_oracle(rows, N, V):
+    seeds = np.random.default_rng(V).integers(-2**63, 2**63 - 1, size=rows, dtype=np.int64)
+    say(f"  noise rows={rows} N={N} V={V}")
+    g = torch.empty((rows, N, V), dtype=torch.float32, device="cuda")
+    lm.markov_noise_fill(g, torch.from_numpy(seeds).cuda())
+    dev = g.cpu().numpy()
+    ref = oracle.noise_fill(seeds, N, V)
+    same = dev.view(np.int32) == ref.view(np.int32)
+    err = np.abs(dev.astype(np.float64) - ref.astype(np.float64))
+    say(f"  noise bit-exact fraction {same.mean():.9f}, max abs diff {err.max():.3g}")
+    # Both sides round fp64 logs to fp32; they can differ only where an fp64
+    # log lands within an fp64 ulp of an fp32 rounding boundary (~1e-9 per
+    # value).  Such a value is then at most one fp32 ulp of the inner log off,
+    # i.e. |dg| <= 2^-23 + ulp(g).
+    assert same.mean() > 1 - 1e-6
+    assert np.all(err <= 2.0**-22 * (1.0 + np.abs(ref)))
+
+
+# ------------------------------------------------------------ exact chain --
+
+def test_tiny_exact_bit_exact():
+    """Integer-valued weights: every fp32 sum is order-exact, so tokens and
+    cache are bit-identical to the oracle's."""
+    w = synth.workload("tiny_exact")
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    st = chain_check.walk(w, t, c, g, exact=True)
+    say("  " + st.summary())
+    assert st.token_match == st.pairs == w.N
+
+
+def test_tiny_exact_free_running_noise():
+    """Device noise end to end: same tokens as the oracle drawing its own noise."""
+    w = synth.workload("tiny_exact")
+    t, c, _ = run(w)
+    t_o, c_o = oracle.chain(w.base, w.head, w.embed, w.prev, w.temperature, w.seeds)
+    assert np.array_equal(t, t_o)
+    assert np.array_equal(c, c_o)
+
+
+@pytest.mark.parametrize("V,rows,N,T", [
+    (16, 1, 3, 1.0),          # the smallest vocabulary
+    (1040, 3, 2, 0.7),        # ragged: a partial group and chunk
+    (8192 + 48, 2, 5, 0.0),   # greedy, ragged
+    (4096, 64, 1, 1.5),       # the most rows, one step
+])
+def test_exact_small_shapes(V, rows, N, T):
+    w = synth.make(f"exact_V{V}", V, 256, rows, N, seed=V + rows, weights="int",
+                   base_std=2.0, temperature=T)
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    chain_check.walk(w, t, c, g, exact=True)
+
+
+def test_exact_rank512_small():
+    w = synth.make("exact_r512", 4096 + 16, 512, 3, 4, seed=77, weights="int",
+                   base_std=2.0, temperature=[1.0, 0.0, 0.6])
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    chain_check.walk(w, t, c, g, exact=True)
+
+
+# ------------------------------------------------------- named workloads --
+
+def test_dsv41_single_row():
+    w = synth.workload("dsv41_single_row")
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    st = chain_check.walk(w, t, c, g)
+    say("  " + st.summary())
+    assert st.token_match >= 0.999 * st.pairs or len(st.mismatches) <= 1
+
+
+def test_dsv41_eight_rows_capped_with_padding():
+    w = synth.workload("dsv41_eight_rows")
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    assert np.all(t[7] == -7), "the padding row's tokens were written"
+    st = chain_check.walk(w, t, c, g)
+    say("  " + st.summary())
+    assert st.walked_rows == 7
+    assert len(st.mismatches) <= max(1, int(0.001 * st.pairs))
+
+
+def test_invcdf_64rows_sampled():
+    w = synth.workload("dsv41_invcdf_64rows")
+    t, c, _ = run(w)
+    rows = [0, 1, 21, 42, 63]
+    st = chain_check.walk(w, t, c, None, rows=rows)
+    say("  " + st.summary())
+    assert len(st.mismatches) <= 1
+    # every row's tokens are valid ids and every row's cache was written
+    assert t.min() >= 0 and t.max() < w.V
+
+
+def test_large_vocab_stress_nan_and_ties():
+    w = synth.workload("large_vocab_stress")
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    st = chain_check.walk(w, t, c, g, rows=[2, 5, 0])
+    say("  " + st.summary())
+    assert len(st.mismatches) == 0
+    # the injected rules themselves: row 2 even steps pick the lower NaN id,
+    # row 5 picks the NaN on odd steps and the lowest 40.0 tie on even steps
+    for i in range(w.N):
+        b2 = w.base[2, i]
+        nan2 = np.flatnonzero(chain_check.is_nan_bits(b2))
+        if i % 2 == 0:
+            assert t[2, i] == nan2.min()
+        b5 = w.base[5, i]
+        nan5 = np.flatnonzero(chain_check.is_nan_bits(b5))
+        if i % 2 == 1:
+            assert t[5, i] == nan5.min()
+        else:
+            forty = np.flatnonzero(b5 == synth.to_bf16_bits(np.array([40.0]))[0])
+            assert t[5, i] == forty.min()
+
+
+# -------------------------------------------------------------- invariance --
+
+@pytest.mark.parametrize("grid", [1, 7, 64])
+def test_grid_invariance(grid):
+    """The outputs do not depend on the number of workgroups (resident and
+    streamed heads, every chunk-to-workgroup assignment)."""
+    w = synth.make("grid", 20000, 256, 3, 4, seed=5, temperature=[0.7, 0.0, 1.3])
+    g = oracle_noise(w)
+    t0, c0, _ = run(w, gumbel=g)
+    t1, c1, _ = run(w, gumbel=g, grid=grid)
+    assert np.array_equal(t0, t1) and np.array_equal(c0, c1)
+
+
+@pytest.mark.parametrize("grid", [3, 64])
+def test_grid_invariance_invcdf_and_r512(grid):
+    w = synth.make("grid1", 12288, 256, 5, 3, seed=6, temperature=[1.0, 0.0, 0.5, 2.0, 1.0], mode=1)
+    t0, c0, _ = run(w)
+    t1, c1, _ = run(w, grid=grid)
+    assert np.array_equal(t0, t1) and np.array_equal(c0, c1)
+    w = synth.make("grid2", 9000 - 8, 512, 2, 3, seed=7, temperature=1.0)
+    g = oracle_noise(w)
+    t0, c0, _ = run(w, gumbel=g)
+    t1, c1, _ = run(w, gumbel=g, grid=grid)
+    assert np.array_equal(t0, t1) and np.array_equal(c0, c1)
+
+
+def test_repeat_calls_and_alternating_shapes_share_a_workspace():
+    """Back-to-back calls give identical results (the workspace halves are
+    cleared and reused without a memset); a workspace sized for the larger
+    shape also serves a smaller one in between."""
+    big = synth.make("big", 8192, 256, 4, 6, seed=8, temperature=0.8)
+    small = synth.make("small", 2048, 256, 2, 3, seed=9, temperature=0.0)
+    gb, gs = oracle_noise(big), oracle_noise(small)
+    db = DeviceChain(big)
+    ds = DeviceChain(small)
+    ds.workspace = db.workspace  # shared, sized for the larger call
+    db.set_gumbel(gb)
+    ds.set_gumbel(gs)
+    ref_b = ref_s = None
+    say("  repeat calls on one workspace")
+    for k in range(40):
+        db.chain()
+        if k % 3 == 0:
+            ds.chain()
+            ts, cs = ds.results()
+            if ref_s is None:
+                ref_s = (ts.copy(), cs.copy())
+            assert np.array_equal(ts, ref_s[0]) and np.array_equal(cs, ref_s[1])
+        tb, cb = db.results()
+        if ref_b is None:
+            ref_b = (tb.copy(), cb.copy())
+        assert np.array_equal(tb, ref_b[0]) and np.array_equal(cb, ref_b[1])
+    lm.markov_status(db.workspace)
+    chain_check.walk(big, ref_b[0], ref_b[1], gb)
+    chain_check.walk(small, ref_s[0], ref_s[1], gs)
+
+
+def test_padding_rows_are_inert():
+    w = synth.make("pad", 4096, 256, 4, 3, seed=10, temperature=[1.0, 0.6, 0.0, 1.2],
+                   state_idx=[2, -1, 0, 1])
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    assert np.all(t[1] == -7)
+    chain_check.walk(w, t, c, g)
+    # the same rows without the padding row give the same tokens
+    keep = [0, 2, 3]
+    w2 = synth.Workload("nopad", w.V, w.r, 3, w.N, 0, w.head, w.embed, w.base[keep].copy(),
+                        w.prev[keep].copy(), w.seeds[keep].copy(), w.temperature[keep].copy(),
+                        np.array([2, 0, 1]), w.mult, w.cap)
+    t2, c2, _ = run(w2, gumbel=g[keep].copy())
+    assert np.array_equal(t2, t[keep])
+    assert np.array_equal(c2, c)
+
+
+def test_bad_previous_token_reported_and_row_inert():
+    w = synth.make("bad", 2048, 256, 2, 2, seed=11, temperature=1.0)
+    w.prev = np.array([5, 2048], dtype=np.int64)
+    d = DeviceChain(w)
+    d.set_gumbel(oracle_noise(w))
+    d.chain()
+    with pytest.raises(lm.MarkovError):
+        lm.markov_status(d.workspace)
+    t, _ = d.results()
+    assert np.all(t[1] == -7) and np.all(t[0] >= 0)
+    lm.markov_status(d.workspace)  # cleared
+
+
+# ----------------------------------------------------------- sampling law --
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_sampling_law_chi_square_v16(mode):
+    """V=16, head = 0, logits 0.25 j - 2, T = 1: ~10^5 device draws against
+    the exact softmax (df 15, p = 1e-3 critical value 37.70)."""
+    V, rows, N = 16, 64, 8
+    logits = (0.25 * np.arange(V) - 2).astype(np.float32)
+    w = synth.make("chi", V, 256, rows, N, seed=12, weights="zero", temperature=1.0, mode=mode)
+    w.base[:] = synth.to_bf16_bits(logits)
+    d = DeviceChain(w)
+    counts = np.zeros(V)
+    rng = np.random.default_rng(13)
+    say(f"  chi-square mode {mode}")
+    for _ in range(196):
+        d.seeds.copy_(torch.from_numpy(rng.integers(-2**63, 2**63 - 1, rows, dtype=np.int64)))
+        if mode == 0:
+            d.noise()
+        d.chain()
+        counts += np.bincount(d.tokens.cpu().numpy().ravel(), minlength=V)
+    lm.markov_status(d.workspace)
+    p = np.exp(logits.astype(np.float64))
+    p /= p.sum()
+    exp = counts.sum() * p
+    chi2 = float(((counts - exp) ** 2 / exp).sum())
+    say(f"  chi2 = {chi2:.2f} over {int(counts.sum())} draws")
+    assert chi2 < 37.70
