@@ -188,12 +188,13 @@ static int64_t orc_pick_max(const float* s, int V, double* diag) {
  *            token = lowest NaN id, else lowest id of max s    [SM], [MS]
  *   mode 1:  inverse CDF of softmax(cache / T) at u            [FM] docstring
  *
- * gumbel may be NULL in mode 1 (unused).  Returns the token.
+ * gumbel may be NULL in mode 1 (unused).  bias_out (optional, [V]) receives
+ * the bf16 bias for diagnostics.  Returns the token.
  */
 int64_t orc_step(const uint16_t* base, const uint16_t* head,
                  const uint16_t* embed, int V, int r, int64_t prev, float T,
                  const float* gumbel, float u, float mult, float cap, int mode,
-                 uint16_t* cache, double* diag) {
+                 uint16_t* cache, double* diag, uint16_t* bias_out) {
   double* e = (double*)malloc(sizeof(double) * (size_t)r);
   float* s = (float*)malloc(sizeof(float) * (size_t)V);
   for (int k = 0; k < r; ++k)
@@ -204,7 +205,9 @@ int64_t orc_step(const uint16_t* base, const uint16_t* head,
     double dot = 0.0;
     const uint16_t* hv = head + (size_t)v * r;
     for (int k = 0; k < r; ++k) dot += (double)orc_bf16_to_f32(hv[k]) * e[k];
-    float bias = orc_bf16_to_f32(orc_bf16_round(dot));
+    uint16_t bias_bits = orc_bf16_round(dot);
+    if (bias_out) bias_out[v] = bias_bits; /* diagnostic copy of the bias */
+    float bias = orc_bf16_to_f32(bias_bits);
     float x = orc_bf16_to_f32(base[v]) + bias;
     x = x * mult;
     if (cap > 0.0f) x = tanhf(x * inv_cap) * cap;
@@ -326,7 +329,7 @@ int orc_chain(const uint16_t* base, int64_t base_rs, int64_t base_ss,
       }
       p = orc_step(base + row * base_rs + i * base_ss, head, embed, V, r, p,
                    temperature[row], gi, u, mult, cap, mode,
-                   cache + state * cache_rs + i * cache_ss, NULL);
+                   cache + state * cache_rs + i * cache_ss, NULL, NULL);
       tokens[(size_t)row * N + i] = p;
     }
   }

@@ -63,7 +63,7 @@ def _load():
                 ctypes.c_int64,
                 [_u16p, _u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
                  ctypes.c_float, _f32p, ctypes.c_float, ctypes.c_float,
-                 ctypes.c_float, ctypes.c_int, _u16p, _f64p],
+                 ctypes.c_float, ctypes.c_int, _u16p, _f64p, _u16p],
             ),
             "orc_chain": (
                 ctypes.c_int,
@@ -152,8 +152,8 @@ def noise_fill(seeds: np.ndarray, steps: int, vocab: int) -> np.ndarray:
 
 
 def step(base_row, head, embed, prev, temperature, gumbel_row=None, u=0.0,
-         mult=1.0, cap=0.0, mode=0, with_diag=False):
-    """One position of one row: returns (token, cache_row[, diag])."""
+         mult=1.0, cap=0.0, mode=0, with_diag=False, with_bias=False):
+    """One position of one row: returns (token, cache_row[, diag][, bias])."""
     base_row = _c(base_row, np.uint16)
     head = _c(head, np.uint16)
     embed = _c(embed, np.uint16)
@@ -162,13 +162,17 @@ def step(base_row, head, embed, prev, temperature, gumbel_row=None, u=0.0,
     g = None if gumbel_row is None else _c(gumbel_row, np.float32)
     cache = np.empty(V, dtype=np.uint16)
     diag = np.zeros(DIAG, dtype=np.float64)
+    bias = np.empty(V, dtype=np.uint16) if with_bias else None
     tok = _load().orc_step(
         _ptr(base_row, _u16p), _ptr(head, _u16p), _ptr(embed, _u16p), V, r,
         int(prev), float(temperature), _ptr(g, _f32p), float(u), float(mult),
-        float(cap), int(mode), _ptr(cache, _u16p), _ptr(diag, _f64p))
+        float(cap), int(mode), _ptr(cache, _u16p), _ptr(diag, _f64p), _ptr(bias, _u16p))
+    out = (int(tok), cache)
     if with_diag:
-        return int(tok), cache, diag
-    return int(tok), cache
+        out += (diag,)
+    if with_bias:
+        out += (bias,)
+    return out
 
 
 def chain(base, head, embed, prev_tokens, temperature, seeds, gumbel=None,

@@ -2,8 +2,15 @@
 
 The walk follows each row position by position with the oracle's own
 tokens.  At every position it checks:
-  * cache: the device row equals the oracle's within one bf16 ulp (adjacent
-    bf16 values), with the same NaN-ness; exact matches are counted;
+  * cache: the same NaN-ness, and every value within the bound the bias
+    tolerance implies.  The device bias is an fp32 sum rounded to bf16, the
+    oracle's the exact sum rounded once, so the two biases may differ by one
+    bf16 ulp of the bias; x = base + bias then moves by at most that times
+    |multiplier| (the soft cap's slope is at most 1), and each side rounds
+    x to bf16 once: |c_dev - c_orc| <= ulp(bias) |mult| + ulp(c).  Where base
+    and bias nearly cancel this exceeds one ulp of the tiny c, so "one bf16
+    ulp" alone would be the wrong test.  Exact and within-one-ulp counts are
+    reported;
   * token: equal to the oracle's.  A different token is accepted only when
     the device's own cache explains it (the device token is what the
     sampling rule gives on the device cache, evaluated here in the same fp32
@@ -37,6 +44,14 @@ def ordinal(bits: np.ndarray) -> np.ndarray:
     b = bits.astype(np.int32)
     mag = b & 0x7FFF
     return np.where(b & 0x8000, -mag, mag)
+
+
+def bf16_spacing(x: np.ndarray) -> np.ndarray:
+    """Gap from |x| to the next larger bf16 value (2^-133 at least)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.where(a > 0, np.maximum(e, -126.0), -126.0)
+    return np.exp2(e - 7)
 
 
 def is_nan_bits(bits: np.ndarray) -> np.ndarray:
@@ -76,11 +91,13 @@ class Stats:
     mismatches: list = dataclasses.field(default_factory=list)
     cache_elems: int = 0
     cache_exact: int = 0
+    cache_one_ulp: int = 0
     walked_rows: int = 0
 
     def summary(self) -> str:
         return (f"pairs={self.pairs} token_match={self.token_match} "
-                f"mismatch={len(self.mismatches)} cache_exact={self.cache_exact}/{self.cache_elems}")
+                f"mismatch={len(self.mismatches)} cache_exact={self.cache_exact}/{self.cache_elems} "
+                f"within_1ulp={self.cache_one_ulp}")
 
 
 def walk(w, tok_gpu, cache_gpu, gumbel, rows=None, exact=False) -> Stats:
@@ -101,8 +118,9 @@ def walk(w, tok_gpu, cache_gpu, gumbel, rows=None, exact=False) -> Stats:
         for i in range(w.N):
             g = gumbel[b, i] if (w.mode == 0 and gumbel is not None) else None
             u = oracle.uniform(oracle.hash_step(int(w.seeds[b]), b, i)) if w.mode == 1 else 0.0
-            tok_o, c_o, diag = oracle.step(w.base[b, i], w.head, w.embed, p, T, g, u=u,
-                                           mult=w.mult, cap=w.cap, mode=w.mode, with_diag=True)
+            tok_o, c_o, diag, bias_o = oracle.step(w.base[b, i], w.head, w.embed, p, T, g, u=u,
+                                                   mult=w.mult, cap=w.cap, mode=w.mode,
+                                                   with_diag=True, with_bias=True)
             c_g = cache_gpu[s, i, :V]
             nan_o, nan_g = is_nan_bits(c_o), is_nan_bits(c_g)
             assert np.array_equal(nan_o, nan_g), f"row {b} step {i}: NaN positions differ"
@@ -111,10 +129,19 @@ def walk(w, tok_gpu, cache_gpu, gumbel, rows=None, exact=False) -> Stats:
             st.cache_elems += V
             same = (d == 0)
             st.cache_exact += int(same.sum())
+            st.cache_one_ulp += int((d <= 1).sum())
             if exact:
                 assert same.all(), f"row {b} step {i}: {int((~same).sum())} cache elements differ"
             else:
-                assert d.max() <= 1, f"row {b} step {i}: cache differs by {int(d.max())} bf16 ulp"
+                fo = f32(c_o).astype(np.float64)
+                fg = f32(c_g).astype(np.float64)
+                fin = ~nan_o & np.isfinite(fo) & np.isfinite(fg)
+                assert np.array_equal(fo[~nan_o & ~fin], fg[~nan_o & ~fin]), f"row {b} step {i}: infinities differ"
+                bound = (bf16_spacing(f32(bias_o)) * abs(w.mult)
+                         + bf16_spacing(np.maximum(np.abs(fo), np.abs(fg))))
+                bad = fin & (np.abs(fo - fg) > bound)
+                assert not bad.any(), (f"row {b} step {i}: {int(bad.sum())} cache values beyond the "
+                                       f"bias-implied bound, e.g. v={int(np.flatnonzero(bad)[0])}")
             t_g = int(tok_gpu[b, i])
             st.pairs += 1
             if t_g == tok_o:

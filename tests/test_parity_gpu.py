@@ -125,6 +125,31 @@ def test_exact_rank512_small():
     chain_check.walk(w, t, c, g, exact=True)
 
 
+def test_bias_within_one_bf16_ulp_random_weights():
+    """With base = 0 and no transform the cache holds the bias itself: the
+    device's fp32-accumulated bias is within one bf16 ulp of the oracle's
+    exactly summed bias on random N(0, 0.02) weights at full vocabulary."""
+    w = synth.make("bias", 129280, 256, 2, 2, seed=31, temperature=[0.0, 0.0])
+    w.base[:] = 0
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    exact = total = 0
+    for b in range(w.rows):
+        p = int(w.prev[b])
+        for i in range(w.N):
+            tok_o, _, bias_o = oracle.step(w.base[b, i], w.head, w.embed, p, 0.0, g[b, i],
+                                           with_bias=True)
+            d = np.abs(chain_check.ordinal(bias_o) - chain_check.ordinal(c[b, i]))
+            assert d.max() <= 1, f"row {b} step {i}: bias differs by {int(d.max())} ulp"
+            exact += int((d == 0).sum())
+            total += d.size
+            if int(t[b, i]) != tok_o:
+                break
+            p = tok_o
+    say(f"  bias bit-exact {exact}/{total}")
+    assert exact > 0.99 * total
+
+
 # ------------------------------------------------------- named workloads --
 
 def test_dsv41_single_row():
