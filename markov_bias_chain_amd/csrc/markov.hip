@@ -55,13 +55,10 @@ namespace {
 constexpr int kWaves = 8;                  // waves per workgroup
 constexpr int kThreads = kWaves * 64;      // 512 threads, one workgroup per CU
 constexpr int kSlots = 32;                 // 16-byte head vectors per lane per group
-constexpr int kSub = 8;                    // slots per sub-batch of the butterfly
-constexpr int kRowPass = 8;                // request rows per register pass
+constexpr int kAhead = 8;                  // request rows whose next-step inputs are prefetched
 constexpr int kHeader = 256;               // workspace header bytes
 constexpr int kMaxPollPerLane = 16;        // slots one lane polls (<= 1024 per row)
 constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // ----------------------------------------------------------- bf16 helpers --
 
@@ -284,100 +281,73 @@ __device__ inline HalfLayout half_layout(unsigned char* half, int rows, int N, i
   return L;
 }
 
-// The lane's dot products for one group and up to kRowPass request rows,
-// as one finished row sum per lane (the row given by row_in_group()).
+// ------------------------------------------------------------ bias GEMV --
+// The bias of a group of RPG = 16384 / r head rows for up to 16 request rows
+// is a [RPG x r] . [r x 16] product on the matrix cores:
+// v_mfma_f32_16x16x32_bf16 computes D[16 x 16] += A[16 x 32] . B[32 x 16]
+// with fp32 accumulation (products of bf16 are exact in fp32).  Operand
+// layouts (lane l of the wave): A[i][k] in lane i + 16 (k / 8), element
+// k % 8; B[k][j] in lane j + 16 (k / 8); D[i][j] in lane j + 16 (i / 4),
+// element i % 4.
 //
-// Lane layout of a group (32 slots of 16 bytes per lane = 32 KiB of head):
-// slot s, lane l hold bf16 elements [8*kseg, 8*kseg + 8) of group row
-// (64*s + l) / (r/8), kseg = (64*s + l) % (r/8).  One slot is 1 KiB of
-// consecutive head bytes, so every load instruction is fully coalesced.
-//
-// Reduction: per sub-batch of 8 slots, a transposing butterfly over lane
-// bits 0..2 halves the values at each level (the lane keeps one half and
-// trades the other with its partner), leaving slot 8q + (l & 7) partially
-// summed; plain xor-adds over the remaining k-segment bits finish the sum,
-// and lanes with ((l >> 3) & 3) == q keep it.  So lane l ends with slot
-// (l & 31): row 2 (l & 31) + (l >> 5) for r = 256, row (l & 31) for r = 512
-// (lanes 32..63 then hold duplicates).  The summation order depends only on
-// the lane layout, not on the grid, so the bias is grid-invariant.
-template <int R>
-__device__ __forceinline__ int row_in_group(int lane) {
-  if constexpr (R == 256) return 2 * (lane & 31) + (lane >> 5);
-  else return lane & 31;
-}
+// A group is 32 tiles of 16 rows x 32 k (MT = RPG / 16 row tiles by
+// KT = r / 32 k tiles); tile (t, kt) is slot t * KT + kt, 16 bytes per lane:
+// lane l holds head[16 t + (l & 15)][32 kt + 8 (l >> 4) + 0..7], so every
+// load instruction reads 16 rows x 64 contiguous bytes.  B for k tile kt is
+// the request rows' embeddings at the same k offsets, read from LDS.  The
+// sums depend only on the group's rows and the embeddings, never on the
+// grid, so the bias is grid-invariant.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRowPass = 16;  // request rows per MFMA pass (the N of the tile)
 
 template <int R>
-__device__ __forceinline__ float butterfly8(const float (&a)[kSub], int lane, int q, float prev) {
-  const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
-  float a1[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    float keep = b0 ? a[2 * m + 1] : a[2 * m];
-    float send = b0 ? a[2 * m] : a[2 * m + 1];
-    a1[m] = keep + xshf<1>(send);
-  }
-  float a2[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    float keep = b1 ? a1[2 * m + 1] : a1[2 * m];
-    float send = b1 ? a1[2 * m] : a1[2 * m + 1];
-    a2[m] = keep + xshf<2>(send);
-  }
-  float keep = b2 ? a2[1] : a2[0];
-  float send = b2 ? a2[0] : a2[1];
-  float x = keep + xshf<4>(send);
-  x += xshf<8>(x);
-  x += xshf<16>(x);
-  if constexpr (R == 512) x += xshf<32>(x);
-  return (((lane >> 3) & 3) == q) ? x : prev;
-}
-
-__device__ __forceinline__ float dot8(uint4 h, uint4 e, float acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h.x), __builtin_bit_cast(bf16x2_t, e.x), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h.y), __builtin_bit_cast(bf16x2_t, e.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h.z), __builtin_bit_cast(bf16x2_t, e.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, h.w), __builtin_bit_cast(bf16x2_t, e.w), acc, false);
-  return acc;
-}
-
-template <int R>
-__device__ __forceinline__ uint4 load_head_slot(const uint16_t* __restrict__ head, int g, int s, int lane, int V) {
-  constexpr int kseg_n = R / 8;
-  const int c = s * 64 + lane;
-  const int row = g * (16384 / R) + c / kseg_n;
-  const int kseg = c % kseg_n;
+__device__ __forceinline__ uint4 load_head_tile(const uint16_t* __restrict__ head, int g, int s,
+                                                int lane, int V) {
+  constexpr int KT = R / 32;
+  const int t = s / KT, kt = s - (s / KT) * KT;
+  const int row = g * (16384 / R) + 16 * t + (lane & 15);
   if (row >= V) return make_uint4(0, 0, 0, 0);
-  return *reinterpret_cast<const uint4*>(head + (size_t)row * R + kseg * 8);
+  return *reinterpret_cast<const uint4*>(head + (size_t)row * R + 32 * kt + 8 * (lane >> 4));
 }
 
-// Dot products of one group with the embeddings of rows [b0, b0 + nb).
-// FROM_REGS: the group's head is `h` (resident); otherwise it is streamed
-// from memory, 8 slots at a time, once per row pass.
-template <int R, bool FROM_REGS, int NH>
-__device__ __forceinline__ void group_dots(const uint4 (&h)[NH], const uint16_t* __restrict__ head,
-                                           int g, int V, const uint4* __restrict__ s_e,
-                                           const int* __restrict__ s_active, int b0, int nb,
-                                           int lane, float (&val)[kRowPass]) {
-  constexpr int kseg_n = R / 8;
-  const int kseg = lane % kseg_n;
+// Row stride (floats) of a wave's bias tile in LDS: RPG + 4 keeps the 16
+// request rows' 16-byte writes on different banks.
+template <int R>
+constexpr int bias_stride() { return 16384 / R + 4; }
+
+// Row stride (16-byte vectors) of the embeddings in LDS: r/8 + 1 keeps the
+// 16 request rows' reads of one k tile on different banks.
+template <int R>
+constexpr int emb_stride() { return R / 8 + 1; }
+
+// sb[j * bias_stride + row] = sum_k head[row][k] * embed_row(b0 + j)[k] for
+// j < nb; rows beyond nb get nothing.
+template <int R>
+__device__ __forceinline__ void group_bias(const uint4 (&h)[kSlots], const uint4* __restrict__ s_e,
+                                           int b0, int nb, int lane, float* __restrict__ sb) {
+  constexpr int KT = R / 32, MT = kSlots / KT, ES = emb_stride<R>();
+  const int j = lane & 15;
+  const bool jv = j < nb;
+  f32x4_t acc[MT];
 #pragma unroll
-  for (int q = 0; q < kSlots / kSub; ++q) {
-    uint4 hs[kSub];
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < kSub; ++s) {
-      if constexpr (FROM_REGS) hs[s] = h[q * kSub + s];
-      else hs[s] = load_head_slot<R>(head, g, q * kSub + s, lane, V);
-    }
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint4 e = jv ? s_e[(b0 + j) * ES + 4 * kt + (lane >> 4)] : make_uint4(0, 0, 0, 0);
+    const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, e);
 #pragma unroll
-    for (int bi = 0; bi < kRowPass; ++bi) {
-      if (bi < nb && s_active[b0 + bi]) {
-        const uint4 e = s_e[(b0 + bi) * kseg_n + kseg];
-        float a[kSub];
+    for (int t = 0; t < MT; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, h[t * KT + kt]), bv,
+                                                        acc[t], 0, 0, 0);
+  }
+  if (jv) {
 #pragma unroll
-        for (int s = 0; s < kSub; ++s) a[s] = dot8(hs[s], e, 0.0f);
-        val[bi] = butterfly8<R>(a, lane, q, val[bi]);
-      }
-    }
+    for (int t = 0; t < MT; ++t)
+      *reinterpret_cast<float4*>(sb + j * bias_stride<R>() + 16 * t + 4 * (lane >> 4)) =
+          make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
   }
 }
 
@@ -389,6 +359,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   constexpr int RPG = 16384 / R;       // head rows per group
   constexpr int CHUNK = kWaves * RPG;  // vocab ids per chunk
   constexpr int KSEG = R / 8;          // 16-byte segments per head row
+  constexpr int ES = emb_stride<R>();  // LDS row stride of the embeddings
+  constexpr int BS = bias_stride<R>(); // LDS row stride of a wave's bias tile
 
   __shared__ int s_state[MARKOV_MAX_ROWS];
   __shared__ int s_active[MARKOV_MAX_ROWS];
@@ -398,9 +370,12 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   __shared__ uint64_t s_dec[MARKOV_MAX_ROWS];
   __shared__ uint64_t s_key[kWaves][MARKOV_MAX_ROWS];
   __shared__ float s_wsum[kWaves][MARKOV_MAX_ROWS];
+  __shared__ float s_bias[kWaves][kRowPass * BS];  // each wave's [16][RPG] bias tile
+  __shared__ uint16_t s_inb[kWaves][kRowPass][64];  // a pass's base logits (bf16 bits) per lane
+  __shared__ float s_ing[kWaves][kRowPass][64];     // a pass's noise per lane
   __shared__ int s_abort;
   __shared__ uint32_t s_parity;
-  extern __shared__ uint4 s_e[];  // [rows][KSEG] 16-byte vectors of the current embeddings
+  extern __shared__ uint4 s_e[];  // [rows][ES] 16-byte vectors of the current embeddings
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -409,14 +384,18 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   const int rows = p.rows, N = p.N, V = p.V, G = p.G, NC = p.NC, NG = p.NG;
   uint32_t* header = reinterpret_cast<uint32_t*>(p.ws);
   const uint64_t deadline = now_ticks() + kTimeoutTicks;
+  // In the epilogue lane l owns group row lr (r = 512 groups have 32 rows:
+  // lanes 32..63 have none).
+  const int lr = (R == 256) ? lane : (lane & 31);
+  const bool lane_owns = (R == 256) || lane < 32;
 
   // ---- prologue: rows, parity, the resident head into VGPRs.
-  uint4 h[RES ? kSlots : 1];
+  uint4 h[kSlots];
   if constexpr (RES) {
     const int g0 = wg * kWaves + wave;  // this wave's group
 #pragma unroll
     for (int s = 0; s < kSlots; ++s)
-      h[s] = g0 < NG ? load_head_slot<R>(p.head, g0, s, lane, V) : make_uint4(0, 0, 0, 0);
+      h[s] = g0 < NG ? load_head_tile<R>(p.head, g0, s, lane, V) : make_uint4(0, 0, 0, 0);
   }
   if (tid == 0) {
     s_parity = ld_agent32(header);
@@ -456,56 +435,107 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   for (int k = tid; k < rows * KSEG; k += kThreads) {
     const int b = k / KSEG, seg = k - b * KSEG;
     if (s_active[b])
-      s_e[k] = *reinterpret_cast<const uint4*>(p.embed + (size_t)s_tok[b] * R + seg * 8);
+      s_e[b * ES + seg] = *reinterpret_cast<const uint4*>(p.embed + (size_t)s_tok[b] * R + seg * 8);
   }
   __syncthreads();
 
+  // Base logit (bf16 bits) and noise of row b at step i, vocab id v: a
+  // uniform row pointer plus a 32-bit lane offset.
+  auto load_in = [&](int i, int b, int v, uint32_t& bl, float& gl) {
+    const uint16_t* brow = p.base + ((long long)b * p.base_rs + (long long)i * p.base_ss);
+    bl = brow[(unsigned)v];
+    gl = 0.0f;
+    if (MODE == 0 && s_T[b] > 0.0f) {
+      const float* grow = p.gumbel + ((size_t)b * N + i) * (size_t)V;
+      gl = grow[(unsigned)v];
+    }
+  };
+  // With a resident head and at most kAhead rows, the next step's base logits
+  // and noise (which do not depend on the winner) are loaded while the
+  // current step's exchange is in flight.
+  const bool ahead = RES && rows <= kAhead;
+  const int v_res = (wg * kWaves + wave) * RPG + lr;
+  const bool own_res = (wg * kWaves + wave) < NG && v_res < V && lane_owns;
+  uint32_t nbl[kAhead / 2];  // two bf16 base logits per register
+  float ngl[kAhead];
+  auto prefetch = [&](int i) {
+#pragma unroll
+    for (int bi = 0; bi < kAhead; ++bi) {
+      uint32_t bv = 0;
+      ngl[bi] = 0.0f;
+      if (bi < rows && s_active[bi] && own_res) load_in(i, bi, v_res, bv, ngl[bi]);
+      if (bi & 1) nbl[bi / 2] |= bv << 16;
+      else nbl[bi / 2] = bv;
+    }
+  };
+  if (ahead) prefetch(0);
+
+  float* sb = s_bias[wave];
   for (int i = 0; i < N; ++i) {
-    // ---- local work: dots, epilogue, keys for every chunk of this workgroup.
+    // ---- local work: bias, epilogue, keys for every chunk of this workgroup.
     if (lane == 0)
       for (int b = 0; b < rows; ++b) s_key[wave][b] = kNoCandidate;
     for (int j = 0; wg + j * G < NC; ++j) {
       const int c = wg + j * G;
       const int g = c * kWaves + wave;
-      const int v = g * RPG + row_in_group<R>(lane);
-      const bool own = g < NG && v < V && (R == 256 || lane < 32);
+      const int v = g * RPG + lr;
+      const bool own = g < NG && v < V && lane_owns;
+      if constexpr (!RES) {
+        // Stream this group's head (all 32 tiles in flight at once).
+#pragma unroll
+        for (int s2 = 0; s2 < kSlots; ++s2)
+          h[s2] = g < NG ? load_head_tile<R>(p.head, g, s2, lane, V) : make_uint4(0, 0, 0, 0);
+      }
       for (int b0 = 0; b0 < rows; b0 += kRowPass) {
         const int nb = rows - b0 < kRowPass ? rows - b0 : kRowPass;
-        // Issue this pass's base and noise loads before the dot products.
-        uint32_t bl[kRowPass];
-        float gl[kRowPass];
+        // This pass's base and noise, staged in LDS for the epilogue loop:
+        // prefetched during the last exchange, or issued now so that the
+        // MFMAs cover their latency.
+        if (ahead) {
 #pragma unroll
-        for (int bi = 0; bi < kRowPass; ++bi) {
-          bl[bi] = 0;
-          gl[bi] = 0.0f;
-          if (bi < nb && s_active[b0 + bi] && own) {
-            const int b = b0 + bi;
-            bl[bi] = p.base[b * p.base_rs + i * p.base_ss + v];
-            if (MODE == 0 && s_T[b] > 0.0f) gl[bi] = p.gumbel[((size_t)b * N + i) * V + v];
+          for (int bi = 0; bi < kAhead; ++bi) {
+            if (bi < nb) {
+              s_inb[wave][bi][lane] = (uint16_t)(nbl[bi / 2] >> (16 * (bi & 1)));
+              s_ing[wave][bi][lane] = ngl[bi];
+            }
+          }
+          group_bias<R>(h, s_e, b0, nb, lane, sb);
+        } else {
+          uint32_t bl[kRowPass];
+          float gl[kRowPass];
+#pragma unroll
+          for (int bi = 0; bi < kRowPass; ++bi) {
+            bl[bi] = 0;
+            gl[bi] = 0.0f;
+            if (bi < nb && s_active[b0 + bi] && own) load_in(i, b0 + bi, v, bl[bi], gl[bi]);
+          }
+          group_bias<R>(h, s_e, b0, nb, lane, sb);
+#pragma unroll
+          for (int bi = 0; bi < kRowPass; ++bi) {
+            if (bi < nb) {
+              s_inb[wave][bi][lane] = (uint16_t)bl[bi];
+              s_ing[wave][bi][lane] = gl[bi];
+            }
           }
         }
-        float val[kRowPass];
-#pragma unroll
-        for (int bi = 0; bi < kRowPass; ++bi) val[bi] = 0.0f;
-        group_dots<R, RES>(h, p.head, g, V, s_e, s_active, b0, nb, lane, val);
-#pragma unroll
-        for (int bi = 0; bi < kRowPass; ++bi) {
+        for (int bi = 0; bi < nb; ++bi) {
           const int b = b0 + bi;
-          if (!(bi < nb && s_active[b])) continue;
+          if (!s_active[b]) continue;
           const float T = s_T[b];
           uint64_t key = kNoCandidate;
           float z = 0.0f;
           if (own) {
-            const float bias = bf16_to_f32(f32_to_bf16(val[bi]));
-            float x = __fadd_rn(bf16_to_f32(bl[bi]), bias);
+            const float bias = bf16_to_f32(f32_to_bf16(sb[bi * BS + lr]));
+            float x = __fadd_rn(bf16_to_f32(s_inb[wave][bi][lane]), bias);
             x = __fmul_rn(x, p.mult);
             if (p.has_cap) x = __fmul_rn(tanhf(__fmul_rn(x, p.inv_cap)), p.cap);
             const uint32_t cb = f32_to_bf16(x);
-            p.cache[(long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss + v] = (uint16_t)cb;
+            uint16_t* crow = p.cache + ((long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss);
+            crow[(unsigned)v] = (uint16_t)cb;
             const float cf = bf16_to_f32(cb);
             if (T > 0.0f) {
               z = __fdiv_rn(cf, T);
-              if (MODE == 0) z = __fadd_rn(z, gl[bi]);
+              if (MODE == 0) z = __fadd_rn(z, s_ing[wave][bi][lane]);
             } else {
               z = cf;
             }
@@ -550,6 +580,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         __syncthreads();
       }
     }
+    if (MODE == 1 && ahead && i + 1 < N) prefetch(i + 1);
     if (MODE == 0) {
       __syncthreads();
       for (int b = tid; b < rows; b += kThreads) {
@@ -558,6 +589,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         for (int w = 0; w < kWaves; ++w) K = umax64(K, s_key[w][b]);
         st_agent(L.keys + ((size_t)i * rows + b) * NC + wg, K);
       }
+      if (ahead && i + 1 < N) prefetch(i + 1);
     }
 
     // ---- grid-wide exchange.
@@ -570,13 +602,15 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         for (;;) {
           bool all = true;
           best = kNoCandidate;
+          for (int k0 = 0; k0 < G; k0 += 256) {  // 4 slots per lane per batch
 #pragma unroll
-          for (int k = 0; k < kMaxPollPerLane; ++k) {
-            const int idx = lane + 64 * k;
-            if (idx < G) {
-              const uint64_t x = ld_agent(slots + idx);
-              all = all && (x != 0);
-              best = umax64(best, x);
+            for (int k = 0; k < 4; ++k) {
+              const int idx = k0 + lane + 64 * k;
+              if (idx < G) {
+                const uint64_t x = ld_agent(slots + idx);
+                all = all && (x != 0);
+                best = umax64(best, x);
+              }
             }
           }
           if (__all(all)) break;
@@ -825,7 +859,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           // A winner is always a valid id; the clamp only keeps the gather in
           // bounds should that ever fail.
           const uint32_t t = (uint32_t)s_tok[b] < (uint32_t)V ? (uint32_t)s_tok[b] : 0u;
-          s_e[k] = *reinterpret_cast<const uint4*>(p.embed + (size_t)t * R + seg * 8);
+          s_e[b * ES + seg] = *reinterpret_cast<const uint4*>(p.embed + (size_t)t * R + seg * 8);
         }
       }
       __syncthreads();
@@ -900,7 +934,7 @@ int prepare_kernels() {
         for (bool res : {false, true}) {
           hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, res),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             MARKOV_MAX_ROWS * 512 * 2);
+                                             MARKOV_MAX_ROWS * (512 / 8 + 1) * 16);
           if (e != hipSuccess && err == hipSuccess) err = e;
         }
   });
@@ -917,7 +951,7 @@ int pick_grid(int rows, int rank, int mode, const Shape& sh, int* grid, bool* re
   int cus = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return fail(MARKOV_E_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
-  const size_t shmem = (size_t)rows * rank * 2;
+  const size_t shmem = (size_t)rows * (rank / 8 + 1) * 16;
   long long g = cus;  // one workgroup per CU: the grid never exceeds the CUs
   if (g > sh.NC) g = sh.NC;
   const int ov = g_grid_override.load();
@@ -1033,12 +1067,17 @@ int markov_chain_sample(const uint16_t* base_logits, int64_t base_row_stride, in
   p.ws_half = ((workspace_bytes - kHeader) / 2) & ~(size_t)255;
 
   void* args[] = {&p};
-  const size_t shmem = (size_t)rows * rank * 2;
+  const size_t shmem = (size_t)rows * (rank / 8 + 1) * 16;
   const void* kern = kernel_for(rank, mode, res);
   rc = prepare_kernels();
   if (rc != MARKOV_OK) return rc;
-  hipError_t e = hipLaunchCooperativeKernel(kern, dim3(G), dim3(kThreads), args, (unsigned)shmem,
-                                            (hipStream_t)stream);
+  // A regular launch: the grid is at most one workgroup per CU and the
+  // kernel's resources admit only one per CU, so on an otherwise idle device
+  // every workgroup is resident at once; every cross-workgroup wait is
+  // bounded, so a grid that is not co-resident ends with
+  // MARKOV_DEVERR_TIMEOUT instead of hanging.
+  hipError_t e = hipLaunchKernel(kern, dim3(G), dim3(kThreads), args, (unsigned)shmem,
+                                 (hipStream_t)stream);
   if (e != hipSuccess) return fail(MARKOV_E_HIP, "chain launch (grid %d): %s", G, hipGetErrorString(e));
   return MARKOV_OK;
 }

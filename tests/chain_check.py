@@ -165,8 +165,10 @@ def walk(w, tok_gpu, cache_gpu, gumbel, rows=None, exact=False) -> Stats:
             else:
                 k_g, cdf, t = inv_cdf_bin(c_g, T, u)
                 if t_g != k_g:
-                    edge = cdf[min(t_g, k_g)]
-                    assert abs(t - edge) <= WINDOW * cdf[-1] and abs(t_g - k_g) == 1, \
+                    # every edge between the two bins lies within the window of u*S
+                    lo, hi = min(t_g, k_g), max(t_g, k_g)
+                    edges = cdf[lo:hi]
+                    assert np.all(np.abs(t - edges) <= WINDOW * cdf[-1]), \
                         f"row {b} step {i}: device bin {t_g} vs its own cache's {k_g}"
                 assert caches_differ or diag[2] <= WINDOW, \
                     f"row {b} step {i}: identical caches, bin {t_g} vs {tok_o}, edge distance {diag[2]}"
