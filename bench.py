@@ -1,0 +1,193 @@
+"""Benchmark of the Markov draft-sampling chain on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the Gumbel noise
+fill on a side stream (forked after the current stream's work and joined
+before the chain) and the persistent chain kernel.  The default workload is
+the DeepSeek-V4.1-sized single request row: V=129280, r=256 (a 66 MB bf16
+head), rows=1, N=8 draft positions, T=0.7, synthetic inputs.
+
+Prints ONE JSON line.  `value` is draft tokens/s over the timed steps
+(back to back, inputs resident in HBM).  `roofline` is for the chain kernel:
+algorithmic bytes per launch (head once, base logits, noise, cache writes,
+embedding rows, tokens) over its average launch duration measured with HIP
+events on the stream it runs on.  Cold calls (a 512 MiB write between calls
+evicts the L2s and the MALL, outside the timed interval) are reported too.
+`cpu_baseline` times the CPU oracle on the same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes one chain call must move at minimum (padding rows excluded)."""
+    real = w.real_rows
+    head = w.V * w.r * 2
+    base = real * w.N * w.V * 2
+    noise = real * w.N * w.V * 4 if w.mode == 0 else 0
+    cache = real * w.N * w.V * 2
+    embed = real * w.N * w.r * 2
+    tokens = real * w.N * 8
+    return dict(head=head, base=base, noise=noise, cache=cache, embed=embed, tokens=tokens,
+                total=head + base + noise + cache + embed + tokens)
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    """The oracle as it stands (single-threaded C), timed on whole calls of
+    the same workload, with its own noise, for about budget_s seconds."""
+    import numpy as np
+
+    import oracle
+
+    g = oracle.noise_fill(w.seeds, w.N, w.V) if w.mode == 0 else None
+    calls = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.chain(w.base, w.head, w.embed, w.prev, w.temperature, w.seeds, gumbel=g,
+                     state_idx=w.state_idx, mult=w.mult, cap=w.cap, mode=w.mode)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    tokens = calls * w.real_rows * w.N
+    del np
+    return {"value": tokens / el, "unit": "draft tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{calls} full calls of the {w.name} workload (oracle noise included, "
+                      f"{el:.1f} s, single thread on {os.cpu_count()} online cores)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dsv41_single_row")
+    ap.add_argument("--cold", type=int, default=50, help="cold calls timed after the main loop")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 8-row figures")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the chain is not sharded across GPUs here)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from markov_bias_chain_amd import binding, synth
+    from markov_bias_chain_amd.device import DeviceChain
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def measure(w, steps, warmup, cold_calls):
+        d = DeviceChain(w, device=dev)
+        stream = torch.cuda.current_stream(dev)
+        for _ in range(warmup):
+            d.step()
+        torch.cuda.synchronize()
+        binding.markov_status(d.workspace)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            if w.mode == 0:
+                d.side.wait_stream(stream)
+                d.noise(stream=d.side)
+                stream.wait_stream(d.side)
+            ev[k][0].record(stream)
+            d.chain(stream=stream)
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        binding.markov_status(d.workspace)
+        chain_ms = [a.elapsed_time(b) for a, b in ev]
+        # cold calls: evict L2s and MALL with a 512 MiB write before each call
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_ms = []
+        for k in range(cold_calls):
+            if w.mode == 0:
+                d.noise(stream=stream)
+            scratch.fill_(k & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            d.chain(stream=stream)
+            b.record(stream)
+            b.synchronize()
+            cold_ms.append(a.elapsed_time(b))
+        binding.markov_status(d.workspace)
+        del scratch, d
+        torch.cuda.empty_cache()
+        return wall, chain_ms, cold_ms
+
+    w = synth.workload(args.workload)
+    wall, chain_ms, cold_ms = measure(w, args.steps, args.warmup, args.cold)
+    tok_per_step = w.real_rows * w.N
+    ms_per_step = wall * 1e3 / args.steps
+    ab = algorithmic_bytes(w)
+    chain_us = statistics.mean(chain_ms) * 1e3
+    chain_us_med = statistics.median(chain_ms) * 1e3
+    cold_us_med = statistics.median(cold_ms) * 1e3 if cold_ms else None
+    achieved = ab["total"] / (chain_us * 1e-6) / 1e9
+    result = {
+        "metric": "µs/call & draft tokens/s, V=129280 r=256 N=8 rows=1/8; head GB/s vs HBM peak",
+        "value": tok_per_step / (ms_per_step * 1e-3),
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "V": w.V, "r": w.r, "rows": w.rows, "N": w.N,
+                   "mode": "gumbel" if w.mode == 0 else "invcdf",
+                   "grid": binding.markov_grid(w.rows, w.N, w.V, w.r, w.mode),
+                   "step": "noise fill on a side stream + chain kernel"},
+        "chain_us_per_call": {"warm_mean": chain_us, "warm_median": chain_us_med,
+                              "warm_p10": sorted(chain_ms)[len(chain_ms) // 10] * 1e3,
+                              "warm_p90": sorted(chain_ms)[len(chain_ms) * 9 // 10] * 1e3,
+                              "cold_median": cold_us_med},
+        "head_GBps": {"warm": ab["head"] / (chain_us_med * 1e-6) / 1e9,
+                      "cold": ab["head"] / (cold_us_med * 1e-6) / 1e9 if cold_us_med else None},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "chain_kernel", "bytes_per_launch": ab["total"]},
+    }
+    if cold_us_med:
+        ach_c = ab["total"] / (cold_us_med * 1e-6) / 1e9
+        result["roofline_cold"] = {"achieved": ach_c, "frac": ach_c / HBM_PEAK_GBPS}
+    if not args.no_extra and args.workload == "dsv41_single_row":
+        w8 = synth.workload("dsv41_eight_rows")
+        _, c8, k8 = measure(w8, 50, 10, 20)
+        us8 = statistics.median(c8) * 1e3
+        result["rows8"] = {"workload": w8.name, "chain_us_warm_median": us8,
+                           "chain_us_cold_median": statistics.median(k8) * 1e3,
+                           "draft_tokens_per_s": w8.real_rows * w8.N / (us8 * 1e-6),
+                           "head_GBps_warm": algorithmic_bytes(w8)["head"] / (us8 * 1e-6) / 1e9}
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
