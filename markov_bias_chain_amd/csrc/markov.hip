@@ -132,6 +132,50 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Reductions over a whole wave on the DPP/readlane path (no LDS-latency
+// swizzles): fold within each 16-lane row with quad permutes and row
+// mirrors, then combine the four rows' lanes 0, 16, 32, 48 through scalars.
+// Each result is the same value in every lane.
+__device__ __forceinline__ float row_fold_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
+  return x;
+}
+__device__ __forceinline__ float row_fold_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+__device__ __forceinline__ float lanes_0_16_32_48(float x, bool is_max) {
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return is_max ? fmaxf(fmaxf(a, b), fmaxf(c, d)) : (a + b) + (c + d);
+}
+__device__ __forceinline__ float wave_sum_fast(float x) { return lanes_0_16_32_48(row_fold_sum(x), false); }
+
+__device__ __forceinline__ uint32_t row_fold_umax(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false));
+  const uint32_t a = __builtin_amdgcn_readlane((int)x, 0), b = __builtin_amdgcn_readlane((int)x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane((int)x, 32), d = __builtin_amdgcn_readlane((int)x, 48);
+  return max(max(a, b), max(c, d));
+}
+// Maximum of a 64-bit value over the wave (high word first, then the low
+// word among the lanes that hold the high maximum).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  const uint32_t hi = row_fold_umax((uint32_t)(k >> 32));
+  const uint32_t lo = row_fold_umax((uint32_t)(k >> 32) == hi ? (uint32_t)k : 0u);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // ------------------------------------------------------ packed (score, id) --
 // A total order on fp32 scores with NaN above everything ([MS] module
 // docstring: the lowest NaN id wins, else the lowest id of the maximum); +0
@@ -158,6 +202,19 @@ __device__ __forceinline__ uint64_t make_key(float s, uint32_t v) {
 }
 
 __device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
+
+// The wave's best (score, id) under the sampling rule, where lane order is
+// id order: the lowest valid lane with a NaN score, else the lowest valid
+// lane holding the maximum (+0 and -0 equal).  `id0` is lane 0's id and
+// lane l's id is id0 + l.  Returns kNoCandidate if no lane is valid.
+__device__ __forceinline__ uint64_t wave_best(float s, bool valid, uint32_t id0) {
+  const uint64_t nan_lanes = __ballot(valid && isnan(s));
+  if (nan_lanes) return ((uint64_t)0xFFFFFFFFu << 32) | (0xFFFFFFFFu - (id0 + (uint32_t)__builtin_ctzll(nan_lanes)));
+  const float m = lanes_0_16_32_48(row_fold_max(valid ? s : -INFINITY), true);
+  const uint64_t at_max = __ballot(valid && s == m);
+  if (!at_max) return kNoCandidate;
+  return make_key(m, id0 + (uint32_t)__builtin_ctzll(at_max));
+}
 
 // ------------------------------------------------------------ SplitMix64 --
 // Steele, Lea and Flood (OOPSLA 2014): one output of the generator whose
@@ -522,7 +579,6 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           const int b = b0 + bi;
           if (!s_active[b]) continue;
           const float T = s_T[b];
-          uint64_t key = kNoCandidate;
           float z = 0.0f;
           if (own) {
             const float bias = bf16_to_f32(f32_to_bf16(sb[bi * BS + lr]));
@@ -539,9 +595,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             } else {
               z = cf;
             }
-            key = make_key(z, (uint32_t)v);
           }
-          const uint64_t wk = wave_max_key(key);
+          const uint64_t wk = wave_best(z, own, (uint32_t)(g * RPG));
           if (MODE == 0) {
             if (lane == 0 && wk > s_key[wave][b]) s_key[wave][b] = wk;
           } else {
@@ -549,7 +604,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             const float m = ord_score((uint32_t)(wk >> 32));
             float e = 0.0f;
             if (own && wk != kNoCandidate && isfinite(m) && !isnan(z)) e = expf(z - m);
-            const float ws = wave_sum(e);
+            const float ws = wave_sum_fast(e);
             if (lane == 0) {
               s_key[wave][b] = wk;
               s_wsum[wave][b] = ws;
@@ -594,14 +649,23 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
 
     // ---- grid-wide exchange.
     if (MODE == 0) {
-      // Every workgroup reads every workgroup's key; wave w serves rows w, w+8, ...
+      // Every workgroup reads every workgroup's key; wave w serves rows w,
+      // w+8, ...  While it polls, the wave fetches the embedding row of the
+      // best key seen so far: that key is almost always the final winner
+      // (unless the workgroup holding the winner is the last to publish), so
+      // the next step's embedding is usually in flight before the exchange
+      // ends.  The row goes straight into the LDS embedding buffer, which no
+      // wave reads again in this step.
       for (int b = wave; b < rows; b += kWaves) {
         if (!s_active[b]) continue;
         const uint64_t* slots = L.keys + ((size_t)i * rows + b) * NC;
+        const bool next = i + 1 < N;
         uint64_t best = kNoCandidate;
+        uint32_t spec = 0xFFFFFFFFu;
+        uint4 ev = make_uint4(0, 0, 0, 0);
         for (;;) {
           bool all = true;
-          best = kNoCandidate;
+          uint64_t mine = kNoCandidate;
           for (int k0 = 0; k0 < G; k0 += 256) {  // 4 slots per lane per batch
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -609,11 +673,17 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
               if (idx < G) {
                 const uint64_t x = ld_agent(slots + idx);
                 all = all && (x != 0);
-                best = umax64(best, x);
+                mine = umax64(mine, x);
               }
             }
           }
+          best = wave_max_u64(mine);
           if (__all(all)) break;
+          const uint32_t cand = key_id(best);
+          if (next && best != kNoCandidate && cand != spec && cand < (uint32_t)V) {
+            spec = cand;
+            if (lane < KSEG) ev = *reinterpret_cast<const uint4*>(p.embed + (size_t)cand * R + lane * 8);
+          }
           if (now_ticks() > deadline) {
             if (lane == 0) {
               s_abort = 1;
@@ -623,8 +693,13 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           }
           __builtin_amdgcn_s_sleep(1);
         }
-        best = wave_max_key(best);
-        if (lane == 0) s_tok[b] = (int)key_id(best);
+        uint32_t win = key_id(best);
+        if (win >= (uint32_t)V) win = 0;  // only after a timeout
+        if (next) {
+          if (win != spec && lane < KSEG) ev = *reinterpret_cast<const uint4*>(p.embed + (size_t)win * R + lane * 8);
+          if (lane < KSEG) s_e[b * ES + lane] = ev;
+        }
+        if (lane == 0) s_tok[b] = (int)win;
       }
     } else {
       // H2: the leader workgroup of each row (b % G) finds the chunk that
@@ -852,7 +927,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     if (wg == 0)
       for (int b = tid; b < rows; b += kThreads)
         if (s_active[b]) p.tokens[(long long)b * p.tok_rs + i] = s_tok[b];
-    if (i + 1 < N) {
+    if (MODE == 1 && i + 1 < N) {
       for (int k = tid; k < rows * KSEG; k += kThreads) {
         const int b = k / KSEG, seg = k - b * KSEG;
         if (s_active[b]) {
