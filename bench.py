@@ -9,9 +9,10 @@ head), rows=1, N=8 draft positions, T=0.7, synthetic inputs.
 Prints ONE JSON line.  `value` is draft tokens/s over the timed steps
 (back to back, inputs resident in HBM).  `roofline` is for the chain kernel:
 algorithmic bytes per launch (head once, base logits, noise, cache writes,
-embedding rows, tokens) over its average launch duration measured with HIP
-events on the stream it runs on.  Cold calls (a 512 MiB write between calls
-evicts the L2s and the MALL, outside the timed interval) are reported too.
+embedding rows, tokens) over its average launch duration, measured with HIP
+events on the stream it runs on around `steps` back-to-back chain launches.
+Cold calls (a 1 GiB read between calls evicts the L2s and the 256 MB MALL
+with clean lines, outside the timed interval) are reported too.
 `cpu_baseline` times the CPU oracle on the same workload on this host.
 """
 
@@ -78,6 +79,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the 8-row figures")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 256 MiB device-to-device copy (a known-size kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -118,13 +122,23 @@ def main() -> int:
         wall = time.perf_counter() - t0
         binding.markov_status(d.workspace)
         chain_ms = [a.elapsed_time(b) for a, b in ev]
-        # cold calls: evict L2s and MALL with a 512 MiB write before each call
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        # the chain alone, back to back: the average launch duration
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            d.chain(stream=stream)
+        b.record(stream)
+        b.synchronize()
+        b2b_ms = a.elapsed_time(b) / steps
+        binding.markov_status(d.workspace)
+        # cold calls: evict the L2s and the MALL by reading 1 GiB before each call
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        sink = torch.empty((), dtype=torch.float32, device=dev)
         cold_ms = []
         for k in range(cold_calls):
             if w.mode == 0:
                 d.noise(stream=stream)
-            scratch.fill_(k & 0xFF)
+            torch.sum(scratch, out=sink)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             d.chain(stream=stream)
@@ -134,14 +148,22 @@ def main() -> int:
         binding.markov_status(d.workspace)
         del scratch, d
         torch.cuda.empty_cache()
-        return wall, chain_ms, cold_ms
+        return wall, chain_ms, cold_ms, b2b_ms
+
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     w = synth.workload(args.workload)
-    wall, chain_ms, cold_ms = measure(w, args.steps, args.warmup, args.cold)
+    wall, chain_ms, cold_ms, b2b_ms = measure(w, args.steps, args.warmup, args.cold)
     tok_per_step = w.real_rows * w.N
     ms_per_step = wall * 1e3 / args.steps
     ab = algorithmic_bytes(w)
-    chain_us = statistics.mean(chain_ms) * 1e3
+    chain_us = b2b_ms * 1e3
     chain_us_med = statistics.median(chain_ms) * 1e3
     cold_us_med = statistics.median(cold_ms) * 1e3 if cold_ms else None
     achieved = ab["total"] / (chain_us * 1e-6) / 1e9
@@ -162,7 +184,9 @@ def main() -> int:
                    "mode": "gumbel" if w.mode == 0 else "invcdf",
                    "grid": binding.markov_grid(w.rows, w.N, w.V, w.r, w.mode),
                    "step": "noise fill on a side stream + chain kernel"},
-        "chain_us_per_call": {"warm_mean": chain_us, "warm_median": chain_us_med,
+        "chain_us_per_call": {"back_to_back_mean": chain_us,
+                              "warm_event_mean": statistics.mean(chain_ms) * 1e3,
+                              "warm_median": chain_us_med,
                               "warm_p10": sorted(chain_ms)[len(chain_ms) // 10] * 1e3,
                               "warm_p90": sorted(chain_ms)[len(chain_ms) * 9 // 10] * 1e3,
                               "cold_median": cold_us_med},
@@ -177,7 +201,7 @@ def main() -> int:
         result["roofline_cold"] = {"achieved": ach_c, "frac": ach_c / HBM_PEAK_GBPS}
     if not args.no_extra and args.workload == "dsv41_single_row":
         w8 = synth.workload("dsv41_eight_rows")
-        _, c8, k8 = measure(w8, 50, 10, 20)
+        _, c8, k8, _ = measure(w8, 50, 10, 20)
         us8 = statistics.median(c8) * 1e3
         result["rows8"] = {"workload": w8.name, "chain_us_warm_median": us8,
                            "chain_us_cold_median": statistics.median(k8) * 1e3,
