@@ -30,6 +30,24 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+KERNEL_SRC = os.path.join(ROOT, "markov_bias_chain_amd", "csrc", "markov.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "chain_kernel_dsv41_single_row_pmc.md")
+
+
+def measured_traffic():
+    """HBM-side bytes per chain launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source (else None)."""
+    import hashlib
+
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and " " not in line.split(": ")[0])
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    if fields.get("kernel_source_sha256_prefix", "").strip() != sha:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def algorithmic_bytes(w) -> dict:
@@ -193,7 +211,8 @@ def main() -> int:
         "head_GBps": {"warm": ab["head"] / (chain_us_med * 1e-6) / 1e9,
                       "cold": ab["head"] / (cold_us_med * 1e-6) / 1e9 if cold_us_med else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic() if args.workload == "dsv41_single_row" else None,
                      "kernel": "chain_kernel", "bytes_per_launch": ab["total"]},
     }
     if cold_us_med:
