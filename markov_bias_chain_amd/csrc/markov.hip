@@ -410,8 +410,10 @@ __device__ __forceinline__ void group_bias(const uint4 (&h)[kSlots], const uint4
 
 // RES: every workgroup owns exactly one chunk (G == NC) and keeps its head in
 // VGPRs for the whole launch.  !RES: workgroups stride over the chunks and
-// stream the head from memory at every step.
-template <int R, int MODE, bool RES>
+// stream the head from memory at every step.  SMALL (with RES): at most
+// kAhead request rows, whose next-step inputs are prefetched in registers
+// (and, in mode 0, whose exchange is overlapped with the next step).
+template <int R, int MODE, bool RES, bool SMALL>
 __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   constexpr int RPG = 16384 / R;       // head rows per group
   constexpr int CHUNK = kWaves * RPG;  // vocab ids per chunk
@@ -431,6 +433,9 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   __shared__ uint16_t s_inb[kWaves][kRowPass][64];  // a pass's base logits (bf16 bits) per lane
   __shared__ float s_ing[kWaves][kRowPass][64];     // a pass's noise per lane
   __shared__ int s_abort;
+  __shared__ int s_miss;
+  __shared__ int s_spec[kAhead];
+  __shared__ int s_done[kAhead];
   __shared__ uint32_t s_parity;
   extern __shared__ uint4 s_e[];  // [rows][ES] 16-byte vectors of the current embeddings
 
@@ -510,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // With a resident head and at most kAhead rows, the next step's base logits
   // and noise (which do not depend on the winner) are loaded while the
   // current step's exchange is in flight.
-  const bool ahead = RES && rows <= kAhead;
+  constexpr bool ahead = RES && SMALL;
   const int v_res = (wg * kWaves + wave) * RPG + lr;
   const bool own_res = (wg * kWaves + wave) < NG && v_res < V && lane_owns;
   uint32_t nbl[kAhead / 2];  // two bf16 base logits per register
@@ -528,7 +533,9 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   if (ahead) prefetch(0);
 
   float* sb = s_bias[wave];
-  for (int i = 0; i < N; ++i) {
+  // Local work of step i: bias, epilogue, keys for every chunk of this
+  // workgroup (mode 1 also publishes each chunk's partials).
+  auto local_work = [&](int i) {
     // ---- local work: bias, epilogue, keys for every chunk of this workgroup.
     if (lane == 0)
       for (int b = 0; b < rows; ++b) s_key[wave][b] = kNoCandidate;
@@ -548,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // This pass's base and noise, staged in LDS for the epilogue loop:
         // prefetched during the last exchange, or issued now so that the
         // MFMAs cover their latency.
-        if (ahead) {
+        if constexpr (ahead) {
 #pragma unroll
           for (int bi = 0; bi < kAhead; ++bi) {
             if (bi < nb) {
@@ -635,16 +642,136 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         __syncthreads();
       }
     }
+  };
+
+  // Publication of the workgroup's best key per row (mode 0).
+  auto publish = [&](int i) {
+    for (int b = tid; b < rows; b += kThreads) {
+      if (!s_active[b]) continue;
+      uint64_t K = kNoCandidate;
+      for (int w = 0; w < kWaves; ++w) K = umax64(K, s_key[w][b]);
+      st_agent(L.keys + ((size_t)i * rows + b) * NC + wg, K);
+    }
+  };
+
+  // Speculation (mode 0, resident head, at most kAhead rows, so wave b
+  // serves row b): phase A polls step i's slots until at least 7/8 have
+  // arrived, takes the best key so far as the winner and puts its embedding
+  // in LDS; step i+1's local work then runs on that embedding while the
+  // remaining slots land; phase B polls until every slot has arrived and
+  // confirms the winner.
+  // A wrong guess (the winner's workgroup published last) reloads the right
+  // embedding and step i+1's local work is recomputed: its cache stores are
+  // overwritten and its keys were never published.
+  constexpr bool speculate = MODE == 0 && ahead;
+  auto slot_wait_abort = [&]() {
+    if (lane == 0) {
+      s_abort = 1;
+      __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  auto phase_a = [&](int i) {
+    const int b = wave;
+    if (b >= rows || !s_active[b]) return;
+    const uint64_t* slots = L.keys + ((size_t)i * rows + b) * NC;
+    uint64_t best = kNoCandidate;
+    bool all = false;
+    for (;;) {
+      uint64_t x[4];
+      uint64_t mine = kNoCandidate;
+      int arrived = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int idx = lane + 64 * k;
+        x[k] = idx < G ? ld_agent(slots + idx) : ~0ull;
+        if (idx < G) mine = umax64(mine, x[k]);
+        arrived += __popcll(__ballot(idx < G && x[k] != 0));
+      }
+      best = wave_max_u64(mine);
+      all = arrived == G;
+      if (all || 8 * arrived >= 7 * G) break;
+      if (now_ticks() > deadline) {
+        slot_wait_abort();
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    uint32_t spec = key_id(best);
+    if (spec >= (uint32_t)V) spec = 0;  // only if nothing arrived (timeout)
+    if (lane < KSEG) s_e[b * ES + lane] = *reinterpret_cast<const uint4*>(p.embed + (size_t)spec * R + lane * 8);
+    if (lane == 0) {
+      s_spec[b] = (int)spec;
+      s_done[b] = all;
+    }
+  };
+  auto phase_b = [&](int i) {
+    const int b = wave;
+    if (b >= rows || !s_active[b]) return;
+    const uint32_t spec = (uint32_t)s_spec[b];
+    uint32_t fin = spec;
+    if (!s_done[b]) {
+      const uint64_t* slots = L.keys + ((size_t)i * rows + b) * NC;
+      uint64_t best = kNoCandidate;
+      for (;;) {
+        bool all = true;
+        uint64_t mine = kNoCandidate;
+        mine = kNoCandidate;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int idx = lane + 64 * k;
+          const uint64_t xv = idx < G ? ld_agent(slots + idx) : ~0ull;
+          all = all && xv != 0;
+          if (idx < G) mine = umax64(mine, xv);
+        }
+        best = wave_max_u64(mine);
+        if (__all(all)) break;
+        if (now_ticks() > deadline) {
+          slot_wait_abort();
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      fin = key_id(best);
+      if (fin >= (uint32_t)V) fin = 0;  // only after a timeout
+    }
+    if (fin != spec) {
+      if (lane < KSEG) s_e[b * ES + lane] = *reinterpret_cast<const uint4*>(p.embed + (size_t)fin * R + lane * 8);
+      if (lane == 0) s_miss = 1;
+    }
+    if (lane == 0) s_tok[b] = (int)fin;
+  };
+
+  // The step loop.  With speculation the local work of step i+1 runs between
+  // phase A and phase B of step i's exchange, so the loop body starts with
+  // the local work of step i and then confirms step i-1 if it is pending; a
+  // wrong guess repeats the body for the same step.
+  int i = 0;
+  bool pending = false;  // step i-1's exchange awaits phase B
+  for (;;) {
+    local_work(i);
+    if (pending) {
+      phase_b(i - 1);
+      __syncthreads();
+      if (s_abort) break;
+      if (wg == 0)
+        for (int b = tid; b < rows; b += kThreads)
+          if (s_active[b]) p.tokens[(long long)b * p.tok_rs + (i - 1)] = s_tok[b];
+      pending = false;
+      if (s_miss) continue;  // redo step i on the confirmed embedding
+    }
     if (MODE == 1 && ahead && i + 1 < N) prefetch(i + 1);
     if (MODE == 0) {
       __syncthreads();
-      for (int b = tid; b < rows; b += kThreads) {
-        if (!s_active[b]) continue;
-        uint64_t K = kNoCandidate;
-        for (int w = 0; w < kWaves; ++w) K = umax64(K, s_key[w][b]);
-        st_agent(L.keys + ((size_t)i * rows + b) * NC + wg, K);
-      }
+      publish(i);
       if (ahead && i + 1 < N) prefetch(i + 1);
+      if (speculate && i + 1 < N) {
+        if (tid == 0) s_miss = 0;
+        phase_a(i);
+        __syncthreads();
+        pending = true;
+        ++i;
+        continue;
+      }
     }
 
     // ---- grid-wide exchange.
@@ -660,7 +787,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         if (!s_active[b]) continue;
         const uint64_t* slots = L.keys + ((size_t)i * rows + b) * NC;
         const bool next = i + 1 < N;
-        uint64_t best = kNoCandidate;
+            uint64_t best = kNoCandidate;
         uint32_t spec = 0xFFFFFFFFu;
         uint4 ev = make_uint4(0, 0, 0, 0);
         for (;;) {
@@ -939,6 +1066,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       }
       __syncthreads();
     }
+    if (++i >= N) break;
   }
   // Every workgroup has read the parity by now (all published the last step).
   if (wg == 0 && tid == 0 && !s_abort) st_agent32(header, parity ^ 1u);
@@ -989,13 +1117,15 @@ int check_shape(int rows, int steps, int vocab, int rank, int mode, Shape* sh) {
   return MARKOV_OK;
 }
 
-const void* kernel_for(int rank, int mode, bool res) {
-  if (rank == 256) {
-    if (mode == 0) return res ? (const void*)chain_kernel<256, 0, true> : (const void*)chain_kernel<256, 0, false>;
-    return res ? (const void*)chain_kernel<256, 1, true> : (const void*)chain_kernel<256, 1, false>;
-  }
-  if (mode == 0) return res ? (const void*)chain_kernel<512, 0, true> : (const void*)chain_kernel<512, 0, false>;
-  return res ? (const void*)chain_kernel<512, 1, true> : (const void*)chain_kernel<512, 1, false>;
+template <int R, int MODE>
+const void* kernel_variant(bool res, bool small) {
+  if (!res) return (const void*)chain_kernel<R, MODE, false, false>;
+  return small ? (const void*)chain_kernel<R, MODE, true, true> : (const void*)chain_kernel<R, MODE, true, false>;
+}
+
+const void* kernel_for(int rank, int mode, bool res, bool small) {
+  if (rank == 256) return mode == 0 ? kernel_variant<256, 0>(res, small) : kernel_variant<256, 1>(res, small);
+  return mode == 0 ? kernel_variant<512, 0>(res, small) : kernel_variant<512, 1>(res, small);
 }
 
 // Dynamic LDS above the default per-launch limit is opted into once per
@@ -1006,8 +1136,8 @@ int prepare_kernels() {
   std::call_once(once, [] {
     for (int rank : {256, 512})
       for (int mode : {0, 1})
-        for (bool res : {false, true}) {
-          hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, res),
+        for (int v = 0; v < 3; ++v) {
+          hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, v > 0, v == 2),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              MARKOV_MAX_ROWS * (512 / 8 + 1) * 16);
           if (e != hipSuccess && err == hipSuccess) err = e;
@@ -1034,7 +1164,8 @@ int pick_grid(int rows, int rank, int mode, const Shape& sh, int* grid, bool* re
   if (g > 64 * kMaxPollPerLane) g = 64 * kMaxPollPerLane;
   const bool resident = (g == sh.NC);
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel_for(rank, mode, resident), kThreads, shmem);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel_for(rank, mode, resident, rows <= kAhead),
+                                                    kThreads, shmem);
   if (e != hipSuccess) return fail(MARKOV_E_HIP, "occupancy query: %s", hipGetErrorString(e));
   if (per_cu < 1) return fail(MARKOV_E_HIP, "the chain kernel does not fit on a compute unit");
   *grid = (int)g;
@@ -1143,7 +1274,7 @@ int markov_chain_sample(const uint16_t* base_logits, int64_t base_row_stride, in
 
   void* args[] = {&p};
   const size_t shmem = (size_t)rows * (rank / 8 + 1) * 16;
-  const void* kern = kernel_for(rank, mode, res);
+  const void* kern = kernel_for(rank, mode, res, rows <= kAhead);
   rc = prepare_kernels();
   if (rc != MARKOV_OK) return rc;
   // A regular launch: the grid is at most one workgroup per CU and the
