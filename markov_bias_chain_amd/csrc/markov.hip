@@ -56,6 +56,7 @@ constexpr int kWaves = 8;                  // waves per workgroup
 constexpr int kThreads = kWaves * 64;      // 512 threads, one workgroup per CU
 constexpr int kSlots = 32;                 // 16-byte head vectors per lane per group
 constexpr int kAhead = 8;                  // request rows whose next-step inputs are prefetched
+constexpr int kOrdStride = 68;             // LDS row stride (words) of a wave's per-row lane tile
 constexpr int kHeader = 256;               // workspace header bytes
 constexpr int kMaxPollPerLane = 16;        // slots one lane polls (<= 1024 per row)
 constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz
@@ -65,6 +66,14 @@ constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }
+
+// fp32 -> bf16 with the gfx950 conversion instruction (v_cvt_pk_bf16_f32):
+// round to nearest even, NaN stays NaN; on this device it agrees with
+// f32_to_bf16 below for every fp32 bit pattern (checked exhaustively).
+__device__ __forceinline__ uint32_t f32_to_bf16_hw(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to_bf16_hw(f)); }
 
 // fp32 -> bf16, round to nearest even; NaN -> quiet NaN 0x7FC0.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
@@ -136,13 +145,6 @@ __device__ __forceinline__ float wave_sum(float x) {
 // swizzles): fold within each 16-lane row with quad permutes and row
 // mirrors, then combine the four rows' lanes 0, 16, 32, 48 through scalars.
 // Each result is the same value in every lane.
-__device__ __forceinline__ float row_fold_max(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
-  return x;
-}
 __device__ __forceinline__ float row_fold_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
@@ -150,14 +152,14 @@ __device__ __forceinline__ float row_fold_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
   return x;
 }
-__device__ __forceinline__ float lanes_0_16_32_48(float x, bool is_max) {
+__device__ __forceinline__ float lanes_0_16_32_48_sum(float x) {
   const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
   const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
   const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
   const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
-  return is_max ? fmaxf(fmaxf(a, b), fmaxf(c, d)) : (a + b) + (c + d);
+  return (a + b) + (c + d);
 }
-__device__ __forceinline__ float wave_sum_fast(float x) { return lanes_0_16_32_48(row_fold_sum(x), false); }
+__device__ __forceinline__ float wave_sum_fast(float x) { return lanes_0_16_32_48_sum(row_fold_sum(x)); }
 
 __device__ __forceinline__ uint32_t row_fold_umax(uint32_t x) {
   x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));
@@ -197,24 +199,7 @@ __device__ __forceinline__ float ord_score(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-__device__ __forceinline__ uint64_t make_key(float s, uint32_t v) {
-  return ((uint64_t)score_ord(s) << 32) | (uint32_t)(0xFFFFFFFFu - v);
-}
-
 __device__ __forceinline__ uint32_t key_id(uint64_t k) { return 0xFFFFFFFFu - (uint32_t)k; }
-
-// The wave's best (score, id) under the sampling rule, where lane order is
-// id order: the lowest valid lane with a NaN score, else the lowest valid
-// lane holding the maximum (+0 and -0 equal).  `id0` is lane 0's id and
-// lane l's id is id0 + l.  Returns kNoCandidate if no lane is valid.
-__device__ __forceinline__ uint64_t wave_best(float s, bool valid, uint32_t id0) {
-  const uint64_t nan_lanes = __ballot(valid && isnan(s));
-  if (nan_lanes) return ((uint64_t)0xFFFFFFFFu << 32) | (0xFFFFFFFFu - (id0 + (uint32_t)__builtin_ctzll(nan_lanes)));
-  const float m = lanes_0_16_32_48(row_fold_max(valid ? s : -INFINITY), true);
-  const uint64_t at_max = __ballot(valid && s == m);
-  if (!at_max) return kNoCandidate;
-  return make_key(m, id0 + (uint32_t)__builtin_ctzll(at_max));
-}
 
 // ------------------------------------------------------------ SplitMix64 --
 // Steele, Lea and Flood (OOPSLA 2014): one output of the generator whose
@@ -431,7 +416,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   __shared__ float s_wsum[kWaves][MARKOV_MAX_ROWS];
   __shared__ float s_bias[kWaves][kRowPass * BS];  // each wave's [16][RPG] bias tile
   __shared__ uint16_t s_inb[kWaves][kRowPass][64];  // a pass's base logits (bf16 bits) per lane
-  __shared__ float s_ing[kWaves][kRowPass][64];     // a pass's noise per lane
+  __shared__ __align__(16) uint32_t s_ing[kWaves][kRowPass][kOrdStride];  // a pass's noise bits per lane, then score ordinals
   __shared__ int s_abort;
   __shared__ int s_miss;
   __shared__ int s_spec[kAhead];
@@ -560,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           for (int bi = 0; bi < kAhead; ++bi) {
             if (bi < nb) {
               s_inb[wave][bi][lane] = (uint16_t)(nbl[bi / 2] >> (16 * (bi & 1)));
-              s_ing[wave][bi][lane] = ngl[bi];
+              s_ing[wave][bi][lane] = __float_as_uint(ngl[bi]);
             }
           }
           group_bias<R>(h, s_e, b0, nb, lane, sb);
@@ -578,39 +563,71 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           for (int bi = 0; bi < kRowPass; ++bi) {
             if (bi < nb) {
               s_inb[wave][bi][lane] = (uint16_t)bl[bi];
-              s_ing[wave][bi][lane] = gl[bi];
+              s_ing[wave][bi][lane] = __float_as_uint(gl[bi]);
             }
           }
+        }
+        // Epilogue.  (1) Per request row, every lane turns its bias into the
+        // cache value and the score, stored as an order-preserving ordinal
+        // in the wave's LDS tile (0 = no candidate; the noise slot of the
+        // same lane is reused).  (2) All rows are reduced at once: lane
+        // (r = l & 15, quarter l >> 4) folds 16 ordinals of row r, then the
+        // four quarters combine.  (3) Per row one compare and ballot find the
+        // lowest lane holding the maximum; lane order is vocab order, so that
+        // is the lowest id of the maximum (or of the NaNs, which order first).
+        uint32_t* so = &s_ing[wave][0][0];  // all accesses are 32-bit words
+        for (int bi = 0; bi < nb; ++bi) {
+          const int b = b0 + bi;
+          uint32_t ord = 0;
+          if (s_active[b] && own) {
+            const float T = s_T[b];
+            const float bias = bf16_round(sb[bi * BS + lr]);
+            float x = __fadd_rn(bf16_to_f32(s_inb[wave][bi][lane]), bias);
+            x = __fmul_rn(x, p.mult);
+            if (p.has_cap) x = __fmul_rn(tanhf(__fmul_rn(x, p.inv_cap)), p.cap);
+            const uint32_t cb = f32_to_bf16_hw(x);
+            uint16_t* crow = p.cache + ((long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss);
+            crow[(unsigned)v] = (uint16_t)cb;
+            const float cf = bf16_to_f32(cb);
+            float z = cf;
+            if (T > 0.0f) {
+              if (T != 1.0f) z = __fdiv_rn(cf, T);  // c / 1 is exact
+              if (MODE == 0) z = __fadd_rn(z, __uint_as_float(so[bi * kOrdStride + lane]));
+            }
+            ord = score_ord(z);
+          }
+          so[bi * kOrdStride + lane] = ord;
+        }
+        uint32_t rmax;
+        {
+          const uint4* q4 = reinterpret_cast<const uint4*>(so + (lane & 15) * kOrdStride + 16 * (lane >> 4));
+          rmax = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint4 t4 = q4[k];
+            rmax = max(rmax, max(max(t4.x, t4.y), max(t4.z, t4.w)));
+          }
+          rmax = max(rmax, (uint32_t)xsh16((int)rmax));
+          rmax = max(rmax, (uint32_t)xsh32((int)rmax));
         }
         for (int bi = 0; bi < nb; ++bi) {
           const int b = b0 + bi;
           if (!s_active[b]) continue;
-          const float T = s_T[b];
-          float z = 0.0f;
-          if (own) {
-            const float bias = bf16_to_f32(f32_to_bf16(sb[bi * BS + lr]));
-            float x = __fadd_rn(bf16_to_f32(s_inb[wave][bi][lane]), bias);
-            x = __fmul_rn(x, p.mult);
-            if (p.has_cap) x = __fmul_rn(tanhf(__fmul_rn(x, p.inv_cap)), p.cap);
-            const uint32_t cb = f32_to_bf16(x);
-            uint16_t* crow = p.cache + ((long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss);
-            crow[(unsigned)v] = (uint16_t)cb;
-            const float cf = bf16_to_f32(cb);
-            if (T > 0.0f) {
-              z = __fdiv_rn(cf, T);
-              if (MODE == 0) z = __fadd_rn(z, s_ing[wave][bi][lane]);
-            } else {
-              z = cf;
-            }
-          }
-          const uint64_t wk = wave_best(z, own, (uint32_t)(g * RPG));
+          const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)rmax, bi);
+          const uint32_t mine = so[bi * kOrdStride + lane];
+          const uint64_t hit = __ballot(m != 0 && mine == m);
+          const uint64_t wk = hit ? (((uint64_t)m << 32) | (0xFFFFFFFFu - (uint32_t)(g * RPG + __builtin_ctzll(hit))))
+                                  : kNoCandidate;
           if (MODE == 0) {
             if (lane == 0 && wk > s_key[wave][b]) s_key[wave][b] = wk;
           } else {
             // Per-wave softmax partial relative to the wave's own maximum.
-            const float m = ord_score((uint32_t)(wk >> 32));
+            const float mw = ord_score(m);
             float e = 0.0f;
-            if (own && wk != kNoCandidate && isfinite(m) && !isnan(z)) e = expf(z - m);
+            if (mine != 0 && m != 0 && isfinite(mw)) {
+              const float z = ord_score(mine);
+              if (!isnan(z)) e = expf(z - mw);
+            }
             const float ws = wave_sum_fast(e);
             if (lane == 0) {
               s_key[wave][b] = wk;
