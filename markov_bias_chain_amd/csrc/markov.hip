@@ -293,33 +293,48 @@ struct ChainParams {
   unsigned long long ws_half;  // bytes per parity half
 };
 
-// Workspace half layout (slot arrays of one parity):
+// Workspace half layout (slot arrays of one parity; every slot is written at
+// most once per call, and 0 means "not written yet"):
 //   keys [N][rows][NC] u64     candidate keys (mode 0: one per workgroup,
 //                               mode 1: one per chunk)
-//   sums [N][rows][NC] u32     mode 1: sum of exp(z - chunk max), sign bit set
-//   dec  [N][rows]     u64     mode 1: the leader's decision for the row
-//   tok  [N][rows]     u64     mode 1: the owner's token for the row
+//   mode 0 with at most kAhead rows (speculative publication):
+//   fix  [N][rows][NC] u64     a key recomputed after a wrong guess
+//   tags [N][rows][NC] u32     1 + the previous token the key was computed for
+//   mode 1:
+//   dec  [N][rows]     u64     the leader's decision for the row
+//   tok  [N][rows]     u64     the owner's token for the row
+//   sums [N][rows][NC] u32     sum of exp(z - chunk max), sign bit set
+// (64-bit arrays first, so that every array is aligned to its element size.)
 struct HalfLayout {
   uint64_t* keys;
-  uint32_t* sums;
+  uint64_t* fix;
+  uint32_t* tags;
   uint64_t* dec;
   uint64_t* tok;
+  uint32_t* sums;
 };
 
+__host__ __device__ inline bool speculative_rows(int rows, int mode) { return mode == 0 && rows <= kAhead; }
+
 __host__ __device__ inline size_t half_bytes_needed(int rows, int N, int NC, int mode) {
-  size_t slots = (size_t)N * rows * NC;
+  const size_t slots = (size_t)N * rows * NC;
   size_t b = slots * 8;
-  if (mode == 1) b += slots * 4 + (size_t)N * rows * 16;
+  if (mode == 1) b += (size_t)N * rows * 16 + slots * 4;
+  else if (speculative_rows(rows, mode)) b += slots * 12;
   return (b + 255) & ~(size_t)255;
 }
 
-__device__ inline HalfLayout half_layout(unsigned char* half, int rows, int N, int NC) {
+__device__ inline HalfLayout half_layout(unsigned char* half, int rows, int N, int NC, int mode) {
   HalfLayout L;
-  size_t slots = (size_t)N * rows * NC;
+  const size_t slots = (size_t)N * rows * NC;
   L.keys = reinterpret_cast<uint64_t*>(half);
-  L.sums = reinterpret_cast<uint32_t*>(half + slots * 8);
-  L.dec = reinterpret_cast<uint64_t*>(half + slots * 12);
+  L.fix = L.keys + slots;
+  L.tags = reinterpret_cast<uint32_t*>(L.fix + slots);
+  L.dec = L.keys + slots;
   L.tok = L.dec + (size_t)N * rows;
+  L.sums = reinterpret_cast<uint32_t*>(L.tok + (size_t)N * rows);
+  if (!speculative_rows(rows, mode)) L.fix = nullptr, L.tags = nullptr;
+  if (mode != 1) L.dec = L.tok = nullptr, L.sums = nullptr;
   return L;
 }
 
@@ -393,12 +408,68 @@ __device__ __forceinline__ void group_bias(const uint4 (&h)[kSlots], const uint4
   }
 }
 
+// One request row: the same products on the vector ALU with v_dot2c_f32_bf16
+// (two bf16 products added to an fp32 accumulator), so that the bias of
+// group row lr ends in lane lr without a trip through LDS.  Lane l holds
+// partial sums over k in {32 kt + 8 (l >> 4) .. + 7} for rows 16 t + (l & 15);
+// a reduce-scatter across the four 16-lane quarters (v_permlane32_swap and
+// v_permlane16_swap) adds the quarters and leaves row 16 q + (l & 15) in the
+// lanes of quarter q.  e_row is the request row's embedding in LDS.
+template <int R>
+__device__ __forceinline__ float one_row_bias(const uint4 (&h)[kSlots], const uint4* __restrict__ e_row,
+                                              int lane) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  constexpr int KT = R / 32, MT = kSlots / KT;
+  const int q = lane >> 4;
+  float acc[MT][2];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t][0] = acc[t][1] = 0.0f;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint4 e = e_row[4 * kt + q];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint4 hv = h[t * KT + kt];
+      float a = acc[t][kt & 1];
+      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.x), __builtin_bit_cast(bf16x2_t, e.x), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.y), __builtin_bit_cast(bf16x2_t, e.y), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.z), __builtin_bit_cast(bf16x2_t, e.z), a, false);
+      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.w), __builtin_bit_cast(bf16x2_t, e.w), a, false);
+      acc[t][kt & 1] = a;
+    }
+  }
+  // permlane32_swap(a, b) gives lanes 0..31 (a[l], a[l + 32]) and lanes
+  // 32..63 (b[l - 32], b[l]); permlane16_swap pairs quarters 0/1 and 2/3 the
+  // same way.
+  if constexpr (MT == 4) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0][0] + acc[0][1]),
+                                                     __float_as_uint(acc[2][0] + acc[2][1]), false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[1][0] + acc[1][1]),
+                                                     __float_as_uint(acc[3][0] + acc[3][1]), false, false);
+    // lanes 0..31 now hold rows t = 0, 1 (k0, k1), lanes 32..63 rows t = 2, 3
+    const float k0 = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
+    const float k1 = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
+    const auto s2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
+    return __uint_as_float(s2[0]) + __uint_as_float(s2[1]);
+  } else {
+    static_assert(MT == 2, "r = 512 groups have two row tiles");
+    const auto s0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[0][0] + acc[0][1]),
+                                                     __float_as_uint(acc[1][0] + acc[1][1]), false, false);
+    // quarters 0 and 2 hold row tile 0, quarters 1 and 3 row tile 1
+    const float u = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(u), false, false);
+    return __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
+  }
+}
+
 // RES: every workgroup owns exactly one chunk (G == NC) and keeps its head in
 // VGPRs for the whole launch.  !RES: workgroups stride over the chunks and
 // stream the head from memory at every step.  SMALL (with RES): at most
 // kAhead request rows, whose next-step inputs are prefetched in registers
-// (and, in mode 0, whose exchange is overlapped with the next step).
-template <int R, int MODE, bool RES, bool SMALL>
+// (and, in mode 0, whose exchange is overlapped with the next step).  ONE
+// (with SMALL, mode 0): a single request row, whose bias and epilogue stay in
+// registers.
+template <int R, int MODE, bool RES, bool SMALL, bool ONE>
 __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   constexpr int RPG = 16384 / R;       // head rows per group
   constexpr int CHUNK = kWaves * RPG;  // vocab ids per chunk
@@ -419,8 +490,11 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   __shared__ __align__(16) uint32_t s_ing[kWaves][kRowPass][kOrdStride];  // a pass's noise bits per lane, then score ordinals
   __shared__ int s_abort;
   __shared__ int s_miss;
-  __shared__ int s_spec[kAhead];
-  __shared__ int s_done[kAhead];
+  __shared__ int s_spec[kAhead];   // phase A's guess of the row's winner
+  __shared__ int s_done[kAhead];   // phase A already saw every slot valid
+  __shared__ int s_use[kAhead];    // the token whose embedding s_e holds
+  __shared__ int s_conf[kAhead];   // the last confirmed token of the row
+  __shared__ int s_rmiss[kAhead];  // the row's guess was wrong this step
   __shared__ uint32_t s_parity;
   extern __shared__ uint4 s_e[];  // [rows][ES] 16-byte vectors of the current embeddings
 
@@ -466,6 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     s_active[b] = active;
     s_T[b] = p.temp[b];
     s_tok[b] = active ? (int)tok : 0;
+    if (b < kAhead) s_use[b] = s_conf[b] = s_tok[b];
   }
   __syncthreads();
   const uint32_t parity = s_parity & 1u;
@@ -477,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     for (size_t k = (size_t)wg * kThreads + tid; k < n16; k += (size_t)G * kThreads)
       other[k] = make_uint4(0, 0, 0, 0);
   }
-  const HalfLayout L = half_layout(half, rows, N, NC);
+  const HalfLayout L = half_layout(half, rows, N, NC, MODE);
   // Embeddings of the anchor tokens.
   for (int k = tid; k < rows * KSEG; k += kThreads) {
     const int b = k / KSEG, seg = k - b * KSEG;
@@ -534,6 +609,34 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
 #pragma unroll
         for (int s2 = 0; s2 < kSlots; ++s2)
           h[s2] = g < NG ? load_head_tile<R>(p.head, g, s2, lane, V) : make_uint4(0, 0, 0, 0);
+      }
+      if constexpr (ONE) {
+        // Lane lr's vocab id v: bias, cache value and score ordinal in
+        // registers; one wave maximum and a ballot give the lowest id of the
+        // maximum (or of the NaNs, which order first).
+        const float bsum = one_row_bias<R>(h, s_e, lane);
+        uint32_t ord = 0;
+        if (s_active[0] && own) {
+          const float T = s_T[0];
+          float x = __fadd_rn(bf16_to_f32(nbl[0] & 0xFFFFu), bf16_round(bsum));
+          x = __fmul_rn(x, p.mult);
+          if (p.has_cap) x = __fmul_rn(tanhf(__fmul_rn(x, p.inv_cap)), p.cap);
+          const uint32_t cb = f32_to_bf16_hw(x);
+          uint16_t* crow = p.cache + ((long long)s_state[0] * p.cache_rs + (long long)i * p.cache_ss);
+          crow[(unsigned)v] = (uint16_t)cb;
+          float z = bf16_to_f32(cb);
+          if (T > 0.0f) {
+            if (T != 1.0f) z = __fdiv_rn(z, T);  // c / 1 is exact
+            z = __fadd_rn(z, ngl[0]);
+          }
+          ord = score_ord(z);
+        }
+        const uint32_t m = row_fold_umax(ord);
+        const uint64_t hit = __ballot(m != 0 && ord == m);
+        if (lane == 0)
+          s_key[wave][0] = hit ? (((uint64_t)m << 32) | (0xFFFFFFFFu - (uint32_t)(g * RPG + __builtin_ctzll(hit))))
+                               : kNoCandidate;
+        continue;
       }
       for (int b0 = 0; b0 < rows; b0 += kRowPass) {
         const int nb = rows - b0 < kRowPass ? rows - b0 : kRowPass;
@@ -661,48 +764,80 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     }
   };
 
-  // Publication of the workgroup's best key per row (mode 0).
+  // Speculation (mode 0, resident head, at most kAhead rows, so wave b
+  // serves row b).  Phase A of step i polls step i's slots until at least
+  // 7/8 are valid, takes the best key so far as the winner and puts its
+  // embedding in LDS; the local work of step i+1 runs on it at once and is
+  // published with a tag: 1 + the token whose embedding it used.  Phase B of
+  // step i then waits, while step i+1's keys travel, until every slot of
+  // step i is valid and confirms the winner.  A slot is valid when its tag
+  // names the confirmed previous token; otherwise the publisher guessed wrong
+  // and its fix slot (written once it found out) holds the recomputed key.
+  // On a wrong guess a workgroup reloads the embedding, redoes step i+1's
+  // local work (overwriting its cache stores) and writes the fix slots.
+  constexpr bool speculate = MODE == 0 && ahead;
+
+  // Publication of the workgroup's best key per row (mode 0): row b by
+  // thread b, or with speculation by lane 0 of wave b (the wave that also
+  // runs the row's phases A and B, so its tag is read in program order).
+  auto row_key = [&](int b) {
+    uint64_t K = kNoCandidate;
+    for (int w = 0; w < kWaves; ++w) K = umax64(K, s_key[w][b]);
+    return K;
+  };
   auto publish = [&](int i) {
-    for (int b = tid; b < rows; b += kThreads) {
-      if (!s_active[b]) continue;
-      uint64_t K = kNoCandidate;
-      for (int w = 0; w < kWaves; ++w) K = umax64(K, s_key[w][b]);
-      st_agent(L.keys + ((size_t)i * rows + b) * NC + wg, K);
+    if constexpr (speculate) {
+      const int b = wave;
+      if (lane == 0 && b < rows && s_active[b]) {
+        const size_t slot = ((size_t)i * rows + b) * NC + wg;
+        st_agent(L.keys + slot, row_key(b));
+        st_agent32(L.tags + slot, (uint32_t)s_use[b] + 1u);
+      }
+    } else {
+      for (int b = tid; b < rows; b += kThreads)
+        if (s_active[b]) st_agent(L.keys + ((size_t)i * rows + b) * NC + wg, row_key(b));
     }
   };
-
-  // Speculation (mode 0, resident head, at most kAhead rows, so wave b
-  // serves row b): phase A polls step i's slots until at least 7/8 have
-  // arrived, takes the best key so far as the winner and puts its embedding
-  // in LDS; step i+1's local work then runs on that embedding while the
-  // remaining slots land; phase B polls until every slot has arrived and
-  // confirms the winner.
-  // A wrong guess (the winner's workgroup published last) reloads the right
-  // embedding and step i+1's local work is recomputed: its cache stores are
-  // overwritten and its keys were never published.
-  constexpr bool speculate = MODE == 0 && ahead;
+  auto publish_fix = [&](int i) {
+    const int b = wave;
+    if (lane == 0 && b < rows && s_active[b] && s_rmiss[b])
+      st_agent(L.fix + ((size_t)i * rows + b) * NC + wg, row_key(b));
+  };
   auto slot_wait_abort = [&]() {
     if (lane == 0) {
       s_abort = 1;
       __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
+  // A slot judged against the row's confirmed previous token (want = 1 +
+  // that token): the key if its tag matches, else the fix slot; 0 while the
+  // slot is not valid yet.  Each word is written once per call, so a key
+  // and tag that are both nonzero are final.
+  auto valid_key = [&](size_t slot, uint32_t want) -> uint64_t {
+    const uint64_t k = ld_agent(L.keys + slot);
+    const uint32_t t = ld_agent32(L.tags + slot);
+    if (k == 0 || t == 0) return 0;
+    return t == want ? k : ld_agent(L.fix + slot);
+  };
+  auto load_embedding = [&](int b, uint32_t tok) {
+    if (lane < KSEG) s_e[b * ES + lane] = *reinterpret_cast<const uint4*>(p.embed + (size_t)tok * R + lane * 8);
+  };
   auto phase_a = [&](int i) {
     const int b = wave;
     if (b >= rows || !s_active[b]) return;
-    const uint64_t* slots = L.keys + ((size_t)i * rows + b) * NC;
+    const size_t slot0 = ((size_t)i * rows + b) * NC;
+    const uint32_t want = (uint32_t)s_conf[b] + 1u;
     uint64_t best = kNoCandidate;
     bool all = false;
     for (;;) {
-      uint64_t x[4];
       uint64_t mine = kNoCandidate;
       int arrived = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int idx = lane + 64 * k;
-        x[k] = idx < G ? ld_agent(slots + idx) : ~0ull;
-        if (idx < G) mine = umax64(mine, x[k]);
-        arrived += __popcll(__ballot(idx < G && x[k] != 0));
+        const uint64_t x = idx < G ? valid_key(slot0 + idx, want) : 0;
+        mine = umax64(mine, x);
+        arrived += __popcll(__ballot(x != 0));
       }
       best = wave_max_u64(mine);
       all = arrived == G;
@@ -715,30 +850,35 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     }
     uint32_t spec = key_id(best);
     if (spec >= (uint32_t)V) spec = 0;  // only if nothing arrived (timeout)
-    if (lane < KSEG) s_e[b * ES + lane] = *reinterpret_cast<const uint4*>(p.embed + (size_t)spec * R + lane * 8);
+    load_embedding(b, spec);
     if (lane == 0) {
       s_spec[b] = (int)spec;
+      s_use[b] = (int)spec;
       s_done[b] = all;
     }
   };
-  auto phase_b = [&](int i) {
+  // Phase B of step i; last: the final step (no phase A before it, no next
+  // embedding to correct).
+  auto phase_b = [&](int i, bool last) {
     const int b = wave;
     if (b >= rows || !s_active[b]) return;
     const uint32_t spec = (uint32_t)s_spec[b];
     uint32_t fin = spec;
-    if (!s_done[b]) {
-      const uint64_t* slots = L.keys + ((size_t)i * rows + b) * NC;
+    if (last || !s_done[b]) {
+      const size_t slot0 = ((size_t)i * rows + b) * NC;
+      const uint32_t want = (uint32_t)s_conf[b] + 1u;
       uint64_t best = kNoCandidate;
       for (;;) {
         bool all = true;
         uint64_t mine = kNoCandidate;
-        mine = kNoCandidate;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int idx = lane + 64 * k;
-          const uint64_t xv = idx < G ? ld_agent(slots + idx) : ~0ull;
-          all = all && xv != 0;
-          if (idx < G) mine = umax64(mine, xv);
+          if (idx < G) {
+            const uint64_t x = valid_key(slot0 + idx, want);
+            all = all && x != 0;
+            mine = umax64(mine, x);
+          }
         }
         best = wave_max_u64(mine);
         if (__all(all)) break;
@@ -751,339 +891,356 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       fin = key_id(best);
       if (fin >= (uint32_t)V) fin = 0;  // only after a timeout
     }
-    if (fin != spec) {
-      if (lane < KSEG) s_e[b * ES + lane] = *reinterpret_cast<const uint4*>(p.embed + (size_t)fin * R + lane * 8);
-      if (lane == 0) s_miss = 1;
+    const bool miss = !last && fin != spec;
+    if (miss) load_embedding(b, fin);
+    if (lane == 0) {
+      s_tok[b] = (int)fin;
+      s_conf[b] = (int)fin;
+      s_rmiss[b] = miss;
+      if (miss) {
+        s_use[b] = (int)fin;
+        s_miss = 1;
+      }
     }
-    if (lane == 0) s_tok[b] = (int)fin;
   };
-
-  // The step loop.  With speculation the local work of step i+1 runs between
-  // phase A and phase B of step i's exchange, so the loop body starts with
-  // the local work of step i and then confirms step i-1 if it is pending; a
-  // wrong guess repeats the body for the same step.
-  int i = 0;
-  bool pending = false;  // step i-1's exchange awaits phase B
-  for (;;) {
-    local_work(i);
-    if (pending) {
-      phase_b(i - 1);
-      __syncthreads();
-      if (s_abort) break;
-      if (wg == 0)
-        for (int b = tid; b < rows; b += kThreads)
-          if (s_active[b]) p.tokens[(long long)b * p.tok_rs + (i - 1)] = s_tok[b];
-      pending = false;
-      if (s_miss) continue;  // redo step i on the confirmed embedding
-    }
-    if (MODE == 1 && ahead && i + 1 < N) prefetch(i + 1);
-    if (MODE == 0) {
-      __syncthreads();
-      publish(i);
-      if (ahead && i + 1 < N) prefetch(i + 1);
-      if (speculate && i + 1 < N) {
-        if (tid == 0) s_miss = 0;
-        phase_a(i);
-        __syncthreads();
-        pending = true;
-        ++i;
-        continue;
-      }
-    }
-
-    // ---- grid-wide exchange.
-    if (MODE == 0) {
-      // Every workgroup reads every workgroup's key; wave w serves rows w,
-      // w+8, ...  While it polls, the wave fetches the embedding row of the
-      // best key seen so far: that key is almost always the final winner
-      // (unless the workgroup holding the winner is the last to publish), so
-      // the next step's embedding is usually in flight before the exchange
-      // ends.  The row goes straight into the LDS embedding buffer, which no
-      // wave reads again in this step.
-      for (int b = wave; b < rows; b += kWaves) {
-        if (!s_active[b]) continue;
-        const uint64_t* slots = L.keys + ((size_t)i * rows + b) * NC;
-        const bool next = i + 1 < N;
-            uint64_t best = kNoCandidate;
-        uint32_t spec = 0xFFFFFFFFu;
-        uint4 ev = make_uint4(0, 0, 0, 0);
-        for (;;) {
-          bool all = true;
-          uint64_t mine = kNoCandidate;
-          for (int k0 = 0; k0 < G; k0 += 256) {  // 4 slots per lane per batch
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const int idx = k0 + lane + 64 * k;
-              if (idx < G) {
-                const uint64_t x = ld_agent(slots + idx);
-                all = all && (x != 0);
-                mine = umax64(mine, x);
-              }
-            }
-          }
-          best = wave_max_u64(mine);
-          if (__all(all)) break;
-          const uint32_t cand = key_id(best);
-          if (next && best != kNoCandidate && cand != spec && cand < (uint32_t)V) {
-            spec = cand;
-            if (lane < KSEG) ev = *reinterpret_cast<const uint4*>(p.embed + (size_t)cand * R + lane * 8);
-          }
-          if (now_ticks() > deadline) {
-            if (lane == 0) {
-              s_abort = 1;
-              __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        uint32_t win = key_id(best);
-        if (win >= (uint32_t)V) win = 0;  // only after a timeout
-        if (next) {
-          if (win != spec && lane < KSEG) ev = *reinterpret_cast<const uint4*>(p.embed + (size_t)win * R + lane * 8);
-          if (lane < KSEG) s_e[b * ES + lane] = ev;
-        }
-        if (lane == 0) s_tok[b] = (int)win;
-      }
-    } else {
-      // H2: the leader workgroup of each row (b % G) finds the chunk that
-      // holds u * S and publishes it with the threshold in that chunk's
-      // own scale, or the token itself for an argmax row.
-      const int KPL = (NC + 63) / 64;  // chunks per lane, contiguous
-      for (int b = wg; b < rows; b += G) {
-        if (((b / G) % kWaves) != wave || !s_active[b]) continue;
-        const uint64_t* kslots = L.keys + ((size_t)i * rows + b) * NC;
-        const uint32_t* sslots = L.sums + ((size_t)i * rows + b) * NC;
-        for (;;) {
-          bool all = true;
-          for (int k = 0; k < KPL; ++k) {
-            const int c = lane * KPL + k;
-            if (c < NC) all = all && ld_agent(kslots + c) != 0 && ld_agent32(sslots + c) != 0;
-          }
-          if (__all(all)) break;
-          if (now_ticks() > deadline) {
-            if (lane == 0) {
-              s_abort = 1;
-              __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        uint64_t K = kNoCandidate;
-        for (int k = 0; k < KPL; ++k) {
-          const int c = lane * KPL + k;
-          if (c < NC) K = umax64(K, ld_agent(kslots + c));
-        }
-        K = wave_max_key(K);
-        const float M = ord_score((uint32_t)(K >> 32));
-        uint64_t dec;
-        if (!(s_T[b] > 0.0f) || !isfinite(M)) {
-          dec = (1ull << 63) | key_id(K);
-        } else {
-          // Weights of this lane's chunks and their running sum.
-          float lsum = 0.0f;
-          for (int k = 0; k < KPL; ++k) {
-            const int c = lane * KPL + k;
-            if (c < NC) {
-              const uint64_t kc = ld_agent(kslots + c);
-              const float mc = ord_score((uint32_t)(kc >> 32));
-              const float sc = __uint_as_float(ld_agent32(sslots + c) & 0x7FFFFFFFu);
-              if (kc != kNoCandidate && isfinite(mc)) lsum += sc * expf(mc - M);
-            }
-          }
-          // Inclusive scan of the lane totals in lane order.
-          float incl = lsum;
-#pragma unroll
-          for (int d = 1; d < 64; d <<= 1) {
-            const float o = __shfl_up(incl, d);
-            if (lane >= d) incl += o;
-          }
-          const float total = __shfl(incl, 63);
-          const float excl = incl - lsum;
-          const float t = hash_uniform(noise_prefix(p.seeds[b], b, i)) * total;
-          // First chunk whose inclusive prefix exceeds t.
-          int found = -1;
-          float before = 0.0f, wfound = 0.0f;
-          float run = excl;
-          int last_pos = -1;
-          float last_before = 0.0f, last_w = 0.0f;
-          for (int k = 0; k < KPL; ++k) {
-            const int c = lane * KPL + k;
-            if (c < NC) {
-              const uint64_t kc = ld_agent(kslots + c);
-              const float mc = ord_score((uint32_t)(kc >> 32));
-              const float sc = __uint_as_float(ld_agent32(sslots + c) & 0x7FFFFFFFu);
-              const float w = (kc != kNoCandidate && isfinite(mc)) ? sc * expf(mc - M) : 0.0f;
-              if (found < 0 && run + w > t) {
-                found = c;
-                before = run;
-                wfound = expf(mc - M);
-              }
-              if (w > 0.0f) {
-                last_pos = c;
-                last_before = run;
-                last_w = expf(mc - M);
-              }
-              run += w;
-            }
-          }
-          const uint64_t hit = __ballot(found >= 0);
-          int o;
-          float tl;
-          if (hit) {
-            const int src = __builtin_ctzll(hit);
-            o = __shfl(found, src);
-            const float bf = __shfl(before, src);
-            const float sf = __shfl(wfound, src);
-            tl = (t - bf) / sf;
-          } else {
-            // Rounding left no chunk above t: the last chunk with weight.
-            const uint64_t any = __ballot(last_pos >= 0);
-            const int src = 63 - __builtin_clzll(any);
-            o = __shfl(last_pos, src);
-            const float bf = __shfl(last_before, src);
-            const float sf = __shfl(last_w, src);
-            tl = (t - bf) / sf;
-          }
-          if (!(tl >= 0.0f)) tl = 0.0f;
-          dec = ((uint64_t)(uint32_t)(o + 1) << 32) | __float_as_uint(tl);
-        }
-        if (lane == 0) st_agent(L.dec + (size_t)i * rows + b, dec);
-      }
-      // H3: every workgroup reads every row's decision.
-      for (int b = wave; b < rows; b += kWaves) {
-        if (!s_active[b]) continue;
-        uint64_t d;
-        for (;;) {
-          d = ld_agent(L.dec + (size_t)i * rows + b);
-          if (d != 0) break;
-          if (now_ticks() > deadline) {
-            if (lane == 0) {
-              s_abort = 1;
-              __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            d = 1ull << 63;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        if (lane == 0) {
-          if (d >> 63) {
-            s_tok[b] = (int)(uint32_t)d;
-            s_need[b] = 0;
-          } else {
-            const int o = (int)(d >> 32) - 1;
-            s_dec[b] = d;
-            s_need[b] = (o % G == wg) ? 2 : 1;
-          }
-        }
-      }
-      __syncthreads();
-      // The chunk's owner scans it in vocabulary order (its cache values were
-      // stored by this workgroup in this step).
-      for (int b = wave; b < rows; b += kWaves) {
-        if (!s_active[b] || s_need[b] != 2) continue;
-        const uint64_t d = s_dec[b];
-        const int o = (int)(d >> 32) - 1;
-        const float tl = __uint_as_float((uint32_t)d);
-        const float T = s_T[b];
-        constexpr int PER = CHUNK / 64;  // ids per lane
-        const int v0 = o * CHUNK + lane * PER;
-        const uint16_t* crow = p.cache + (long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss;
-        float z[PER];
-        float m = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          const int v = v0 + k;
-          z[k] = v < V ? __fdiv_rn(bf16_to_f32(crow[v]), T) : -INFINITY;
-          m = fmaxf(m, z[k]);
-        }
-        // chunk maximum
-        {
-          float mm = m;
-          mm = fmaxf(mm, xshf<1>(mm));
-          mm = fmaxf(mm, xshf<2>(mm));
-          mm = fmaxf(mm, xshf<4>(mm));
-          mm = fmaxf(mm, xshf<8>(mm));
-          mm = fmaxf(mm, xshf<16>(mm));
-          mm = fmaxf(mm, xshf<32>(mm));
-          m = mm;
-        }
-        float w[PER];
-        float lsum = 0.0f;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          w[k] = (v0 + k < V && z[k] > -INFINITY) ? expf(z[k] - m) : 0.0f;
-          lsum += w[k];
-        }
-        float incl = lsum;
-#pragma unroll
-        for (int dd = 1; dd < 64; dd <<= 1) {
-          const float ov = __shfl_up(incl, dd);
-          if (lane >= dd) incl += ov;
-        }
-        float run = incl - lsum;
-        int found = -1, lastv = -1;
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-          if (found < 0 && w[k] > 0.0f && run + w[k] > tl) found = v0 + k;
-          if (w[k] > 0.0f) lastv = v0 + k;
-          run += w[k];
-        }
-        const uint64_t hit = __ballot(found >= 0);
-        int tok;
-        if (hit) {
-          tok = __shfl(found, __builtin_ctzll(hit));
-        } else {
-          const uint64_t any = __ballot(lastv >= 0);
-          tok = any ? __shfl(lastv, 63 - __builtin_clzll(any)) : o * CHUNK;
-        }
-        if (lane == 0) {
-          s_tok[b] = tok;
-          st_agent(L.tok + (size_t)i * rows + b, (1ull << 63) | (uint32_t)tok);
-        }
-      }
-      // H4: rows whose chunk another workgroup owns.
-      for (int b = wave; b < rows; b += kWaves) {
-        if (!s_active[b] || s_need[b] != 1) continue;
-        uint64_t d;
-        for (;;) {
-          d = ld_agent(L.tok + (size_t)i * rows + b);
-          if (d != 0) break;
-          if (now_ticks() > deadline) {
-            if (lane == 0) {
-              s_abort = 1;
-              __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            d = 1ull << 63;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        if (lane == 0) s_tok[b] = (int)(uint32_t)d;
-      }
-    }
-    __syncthreads();
-    if (s_abort) break;
-
-    // ---- the winners: tokens out, next embeddings in.
+  auto write_tokens = [&](int i) {
     if (wg == 0)
       for (int b = tid; b < rows; b += kThreads)
         if (s_active[b]) p.tokens[(long long)b * p.tok_rs + i] = s_tok[b];
-    if (MODE == 1 && i + 1 < N) {
-      for (int k = tid; k < rows * KSEG; k += kThreads) {
-        const int b = k / KSEG, seg = k - b * KSEG;
-        if (s_active[b]) {
-          // A winner is always a valid id; the clamp only keeps the gather in
-          // bounds should that ever fail.
-          const uint32_t t = (uint32_t)s_tok[b] < (uint32_t)V ? (uint32_t)s_tok[b] : 0u;
-          s_e[b * ES + seg] = *reinterpret_cast<const uint4*>(p.embed + (size_t)t * R + seg * 8);
+  };
+
+  if constexpr (speculate) {
+    for (int i = 0; i < N; ++i) {
+      local_work(i);
+      if (tid == 0) s_miss = 0;
+      __syncthreads();
+      publish(i);
+      if (i > 0) {
+        phase_b(i - 1, false);
+        __syncthreads();
+        if (s_abort) break;
+        write_tokens(i - 1);
+        if (s_miss) {  // redo step i on the confirmed embeddings
+          local_work(i);
+          __syncthreads();
+          publish_fix(i);
+        }
+      }
+      if (i + 1 < N) {
+        prefetch(i + 1);
+        phase_a(i);
+        __syncthreads();
+        if (s_abort) break;
+      } else {
+        phase_b(i, true);
+        __syncthreads();
+        if (s_abort) break;
+        write_tokens(i);
+      }
+    }
+  } else {
+    // The step loop without speculation: local work, publication, then the
+    // whole exchange of the step.
+    for (int i = 0; i < N; ++i) {
+      local_work(i);
+      if (MODE == 1 && ahead && i + 1 < N) prefetch(i + 1);
+      if (MODE == 0) {
+        __syncthreads();
+        publish(i);
+        if (ahead && i + 1 < N) prefetch(i + 1);
+      }
+
+      // ---- grid-wide exchange.
+      if (MODE == 0) {
+        // Every workgroup reads every workgroup's key; wave w serves rows w,
+        // w+8, ...  While it polls, the wave fetches the embedding row of the
+        // best key seen so far: that key is almost always the final winner
+        // (unless the workgroup holding the winner is the last to publish), so
+        // the next step's embedding is usually in flight before the exchange
+        // ends.  The row goes straight into the LDS embedding buffer, which no
+        // wave reads again in this step.
+        for (int b = wave; b < rows; b += kWaves) {
+          if (!s_active[b]) continue;
+          const uint64_t* slots = L.keys + ((size_t)i * rows + b) * NC;
+          const bool next = i + 1 < N;
+              uint64_t best = kNoCandidate;
+          uint32_t spec = 0xFFFFFFFFu;
+          uint4 ev = make_uint4(0, 0, 0, 0);
+          for (;;) {
+            bool all = true;
+            uint64_t mine = kNoCandidate;
+            for (int k0 = 0; k0 < G; k0 += 256) {  // 4 slots per lane per batch
+  #pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const int idx = k0 + lane + 64 * k;
+                if (idx < G) {
+                  const uint64_t x = ld_agent(slots + idx);
+                  all = all && (x != 0);
+                  mine = umax64(mine, x);
+                }
+              }
+            }
+            best = wave_max_u64(mine);
+            if (__all(all)) break;
+            const uint32_t cand = key_id(best);
+            if (next && best != kNoCandidate && cand != spec && cand < (uint32_t)V) {
+              spec = cand;
+              if (lane < KSEG) ev = *reinterpret_cast<const uint4*>(p.embed + (size_t)cand * R + lane * 8);
+            }
+            if (now_ticks() > deadline) {
+              if (lane == 0) {
+                s_abort = 1;
+                __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          uint32_t win = key_id(best);
+          if (win >= (uint32_t)V) win = 0;  // only after a timeout
+          if (next) {
+            if (win != spec && lane < KSEG) ev = *reinterpret_cast<const uint4*>(p.embed + (size_t)win * R + lane * 8);
+            if (lane < KSEG) s_e[b * ES + lane] = ev;
+          }
+          if (lane == 0) s_tok[b] = (int)win;
+        }
+      } else {
+        // H2: the leader workgroup of each row (b % G) finds the chunk that
+        // holds u * S and publishes it with the threshold in that chunk's
+        // own scale, or the token itself for an argmax row.
+        const int KPL = (NC + 63) / 64;  // chunks per lane, contiguous
+        for (int b = wg; b < rows; b += G) {
+          if (((b / G) % kWaves) != wave || !s_active[b]) continue;
+          const uint64_t* kslots = L.keys + ((size_t)i * rows + b) * NC;
+          const uint32_t* sslots = L.sums + ((size_t)i * rows + b) * NC;
+          for (;;) {
+            bool all = true;
+            for (int k = 0; k < KPL; ++k) {
+              const int c = lane * KPL + k;
+              if (c < NC) all = all && ld_agent(kslots + c) != 0 && ld_agent32(sslots + c) != 0;
+            }
+            if (__all(all)) break;
+            if (now_ticks() > deadline) {
+              if (lane == 0) {
+                s_abort = 1;
+                __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          uint64_t K = kNoCandidate;
+          for (int k = 0; k < KPL; ++k) {
+            const int c = lane * KPL + k;
+            if (c < NC) K = umax64(K, ld_agent(kslots + c));
+          }
+          K = wave_max_key(K);
+          const float M = ord_score((uint32_t)(K >> 32));
+          uint64_t dec;
+          if (!(s_T[b] > 0.0f) || !isfinite(M)) {
+            dec = (1ull << 63) | key_id(K);
+          } else {
+            // Weights of this lane's chunks and their running sum.
+            float lsum = 0.0f;
+            for (int k = 0; k < KPL; ++k) {
+              const int c = lane * KPL + k;
+              if (c < NC) {
+                const uint64_t kc = ld_agent(kslots + c);
+                const float mc = ord_score((uint32_t)(kc >> 32));
+                const float sc = __uint_as_float(ld_agent32(sslots + c) & 0x7FFFFFFFu);
+                if (kc != kNoCandidate && isfinite(mc)) lsum += sc * expf(mc - M);
+              }
+            }
+            // Inclusive scan of the lane totals in lane order.
+            float incl = lsum;
+  #pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+              const float o = __shfl_up(incl, d);
+              if (lane >= d) incl += o;
+            }
+            const float total = __shfl(incl, 63);
+            const float excl = incl - lsum;
+            const float t = hash_uniform(noise_prefix(p.seeds[b], b, i)) * total;
+            // First chunk whose inclusive prefix exceeds t.
+            int found = -1;
+            float before = 0.0f, wfound = 0.0f;
+            float run = excl;
+            int last_pos = -1;
+            float last_before = 0.0f, last_w = 0.0f;
+            for (int k = 0; k < KPL; ++k) {
+              const int c = lane * KPL + k;
+              if (c < NC) {
+                const uint64_t kc = ld_agent(kslots + c);
+                const float mc = ord_score((uint32_t)(kc >> 32));
+                const float sc = __uint_as_float(ld_agent32(sslots + c) & 0x7FFFFFFFu);
+                const float w = (kc != kNoCandidate && isfinite(mc)) ? sc * expf(mc - M) : 0.0f;
+                if (found < 0 && run + w > t) {
+                  found = c;
+                  before = run;
+                  wfound = expf(mc - M);
+                }
+                if (w > 0.0f) {
+                  last_pos = c;
+                  last_before = run;
+                  last_w = expf(mc - M);
+                }
+                run += w;
+              }
+            }
+            const uint64_t hit = __ballot(found >= 0);
+            int o;
+            float tl;
+            if (hit) {
+              const int src = __builtin_ctzll(hit);
+              o = __shfl(found, src);
+              const float bf = __shfl(before, src);
+              const float sf = __shfl(wfound, src);
+              tl = (t - bf) / sf;
+            } else {
+              // Rounding left no chunk above t: the last chunk with weight.
+              const uint64_t any = __ballot(last_pos >= 0);
+              const int src = 63 - __builtin_clzll(any);
+              o = __shfl(last_pos, src);
+              const float bf = __shfl(last_before, src);
+              const float sf = __shfl(last_w, src);
+              tl = (t - bf) / sf;
+            }
+            if (!(tl >= 0.0f)) tl = 0.0f;
+            dec = ((uint64_t)(uint32_t)(o + 1) << 32) | __float_as_uint(tl);
+          }
+          if (lane == 0) st_agent(L.dec + (size_t)i * rows + b, dec);
+        }
+        // H3: every workgroup reads every row's decision.
+        for (int b = wave; b < rows; b += kWaves) {
+          if (!s_active[b]) continue;
+          uint64_t d;
+          for (;;) {
+            d = ld_agent(L.dec + (size_t)i * rows + b);
+            if (d != 0) break;
+            if (now_ticks() > deadline) {
+              if (lane == 0) {
+                s_abort = 1;
+                __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+              d = 1ull << 63;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          if (lane == 0) {
+            if (d >> 63) {
+              s_tok[b] = (int)(uint32_t)d;
+              s_need[b] = 0;
+            } else {
+              const int o = (int)(d >> 32) - 1;
+              s_dec[b] = d;
+              s_need[b] = (o % G == wg) ? 2 : 1;
+            }
+          }
+        }
+        __syncthreads();
+        // The chunk's owner scans it in vocabulary order (its cache values were
+        // stored by this workgroup in this step).
+        for (int b = wave; b < rows; b += kWaves) {
+          if (!s_active[b] || s_need[b] != 2) continue;
+          const uint64_t d = s_dec[b];
+          const int o = (int)(d >> 32) - 1;
+          const float tl = __uint_as_float((uint32_t)d);
+          const float T = s_T[b];
+          constexpr int PER = CHUNK / 64;  // ids per lane
+          const int v0 = o * CHUNK + lane * PER;
+          const uint16_t* crow = p.cache + (long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss;
+          float z[PER];
+          float m = -INFINITY;
+  #pragma unroll
+          for (int k = 0; k < PER; ++k) {
+            const int v = v0 + k;
+            z[k] = v < V ? __fdiv_rn(bf16_to_f32(crow[v]), T) : -INFINITY;
+            m = fmaxf(m, z[k]);
+          }
+          // chunk maximum
+          {
+            float mm = m;
+            mm = fmaxf(mm, xshf<1>(mm));
+            mm = fmaxf(mm, xshf<2>(mm));
+            mm = fmaxf(mm, xshf<4>(mm));
+            mm = fmaxf(mm, xshf<8>(mm));
+            mm = fmaxf(mm, xshf<16>(mm));
+            mm = fmaxf(mm, xshf<32>(mm));
+            m = mm;
+          }
+          float w[PER];
+          float lsum = 0.0f;
+  #pragma unroll
+          for (int k = 0; k < PER; ++k) {
+            w[k] = (v0 + k < V && z[k] > -INFINITY) ? expf(z[k] - m) : 0.0f;
+            lsum += w[k];
+          }
+          float incl = lsum;
+  #pragma unroll
+          for (int dd = 1; dd < 64; dd <<= 1) {
+            const float ov = __shfl_up(incl, dd);
+            if (lane >= dd) incl += ov;
+          }
+          float run = incl - lsum;
+          int found = -1, lastv = -1;
+  #pragma unroll
+          for (int k = 0; k < PER; ++k) {
+            if (found < 0 && w[k] > 0.0f && run + w[k] > tl) found = v0 + k;
+            if (w[k] > 0.0f) lastv = v0 + k;
+            run += w[k];
+          }
+          const uint64_t hit = __ballot(found >= 0);
+          int tok;
+          if (hit) {
+            tok = __shfl(found, __builtin_ctzll(hit));
+          } else {
+            const uint64_t any = __ballot(lastv >= 0);
+            tok = any ? __shfl(lastv, 63 - __builtin_clzll(any)) : o * CHUNK;
+          }
+          if (lane == 0) {
+            s_tok[b] = tok;
+            st_agent(L.tok + (size_t)i * rows + b, (1ull << 63) | (uint32_t)tok);
+          }
+        }
+        // H4: rows whose chunk another workgroup owns.
+        for (int b = wave; b < rows; b += kWaves) {
+          if (!s_active[b] || s_need[b] != 1) continue;
+          uint64_t d;
+          for (;;) {
+            d = ld_agent(L.tok + (size_t)i * rows + b);
+            if (d != 0) break;
+            if (now_ticks() > deadline) {
+              if (lane == 0) {
+                s_abort = 1;
+                __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+              d = 1ull << 63;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          if (lane == 0) s_tok[b] = (int)(uint32_t)d;
         }
       }
       __syncthreads();
+      if (s_abort) break;
+
+      // ---- the winners: tokens out, next embeddings in.
+      write_tokens(i);
+      if (MODE == 1 && i + 1 < N) {
+        for (int k = tid; k < rows * KSEG; k += kThreads) {
+          const int b = k / KSEG, seg = k - b * KSEG;
+          if (s_active[b]) {
+            // A winner is always a valid id; the clamp only keeps the gather in
+            // bounds should that ever fail.
+            const uint32_t t = (uint32_t)s_tok[b] < (uint32_t)V ? (uint32_t)s_tok[b] : 0u;
+            s_e[b * ES + seg] = *reinterpret_cast<const uint4*>(p.embed + (size_t)t * R + seg * 8);
+          }
+        }
+        __syncthreads();
+      }
     }
-    if (++i >= N) break;
   }
   // Every workgroup has read the parity by now (all published the last step).
   if (wg == 0 && tid == 0 && !s_abort) st_agent32(header, parity ^ 1u);
@@ -1134,15 +1291,27 @@ int check_shape(int rows, int steps, int vocab, int rank, int mode, Shape* sh) {
   return MARKOV_OK;
 }
 
+// Kernel kinds: 0 streamed head, 1 resident head, 2 resident with at most
+// kAhead rows, 3 resident with one row (mode 0).
 template <int R, int MODE>
-const void* kernel_variant(bool res, bool small) {
-  if (!res) return (const void*)chain_kernel<R, MODE, false, false>;
-  return small ? (const void*)chain_kernel<R, MODE, true, true> : (const void*)chain_kernel<R, MODE, true, false>;
+const void* kernel_variant(int kind) {
+  switch (kind) {
+    case 0: return (const void*)chain_kernel<R, MODE, false, false, false>;
+    case 1: return (const void*)chain_kernel<R, MODE, true, false, false>;
+    case 2: return (const void*)chain_kernel<R, MODE, true, true, false>;
+    default: return (const void*)chain_kernel<R, MODE, true, true, MODE == 0>;
+  }
 }
 
-const void* kernel_for(int rank, int mode, bool res, bool small) {
-  if (rank == 256) return mode == 0 ? kernel_variant<256, 0>(res, small) : kernel_variant<256, 1>(res, small);
-  return mode == 0 ? kernel_variant<512, 0>(res, small) : kernel_variant<512, 1>(res, small);
+int kernel_kind(int rows, int mode, bool res) {
+  if (!res) return 0;
+  if (rows == 1 && mode == 0) return 3;
+  return rows <= kAhead ? 2 : 1;
+}
+
+const void* kernel_for(int rank, int mode, int kind) {
+  if (rank == 256) return mode == 0 ? kernel_variant<256, 0>(kind) : kernel_variant<256, 1>(kind);
+  return mode == 0 ? kernel_variant<512, 0>(kind) : kernel_variant<512, 1>(kind);
 }
 
 // Dynamic LDS above the default per-launch limit is opted into once per
@@ -1153,8 +1322,8 @@ int prepare_kernels() {
   std::call_once(once, [] {
     for (int rank : {256, 512})
       for (int mode : {0, 1})
-        for (int v = 0; v < 3; ++v) {
-          hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, v > 0, v == 2),
+        for (int kind = 0; kind < 4; ++kind) {
+          hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, kind),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              MARKOV_MAX_ROWS * (512 / 8 + 1) * 16);
           if (e != hipSuccess && err == hipSuccess) err = e;
@@ -1181,7 +1350,7 @@ int pick_grid(int rows, int rank, int mode, const Shape& sh, int* grid, bool* re
   if (g > 64 * kMaxPollPerLane) g = 64 * kMaxPollPerLane;
   const bool resident = (g == sh.NC);
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel_for(rank, mode, resident, rows <= kAhead),
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel_for(rank, mode, kernel_kind(rows, mode, resident)),
                                                     kThreads, shmem);
   if (e != hipSuccess) return fail(MARKOV_E_HIP, "occupancy query: %s", hipGetErrorString(e));
   if (per_cu < 1) return fail(MARKOV_E_HIP, "the chain kernel does not fit on a compute unit");
@@ -1291,7 +1460,7 @@ int markov_chain_sample(const uint16_t* base_logits, int64_t base_row_stride, in
 
   void* args[] = {&p};
   const size_t shmem = (size_t)rows * (rank / 8 + 1) * 16;
-  const void* kern = kernel_for(rank, mode, res, rows <= kAhead);
+  const void* kern = kernel_for(rank, mode, kernel_kind(rows, mode, res));
   rc = prepare_kernels();
   if (rc != MARKOV_OK) return rc;
   // A regular launch: the grid is at most one workgroup per CU and the

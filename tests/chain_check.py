@@ -4,13 +4,14 @@ The walk follows each row position by position with the oracle's own
 tokens.  At every position it checks:
   * cache: the same NaN-ness, and every value within the bound the bias
     tolerance implies.  The device bias is an fp32 sum rounded to bf16, the
-    oracle's the exact sum rounded once, so the two biases may differ by one
-    bf16 ulp of the bias; x = base + bias then moves by at most that times
-    |multiplier| (the soft cap's slope is at most 1), and each side rounds
-    x to bf16 once: |c_dev - c_orc| <= ulp(bias) |mult| + ulp(c).  Where base
-    and bias nearly cancel this exceeds one ulp of the tiny c, so "one bf16
-    ulp" alone would be the wrong test.  Exact and within-one-ulp counts are
-    reported;
+    oracle's the exact sum rounded once; `bias_tolerance` bounds their
+    difference (one bf16 spacing, plus the fp32 accumulation error, which
+    only matters where the sum nearly cancels).  x = base + bias then moves
+    by at most that times |multiplier| (the soft cap's slope is at most 1),
+    and each side rounds x to bf16 once:
+    |c_dev - c_orc| <= tol(bias) |mult| + ulp(c).  Where base and bias nearly
+    cancel this exceeds one ulp of the tiny c, so "one bf16 ulp" alone would
+    be the wrong test.  Exact and within-one-ulp counts are reported;
   * token: equal to the oracle's.  A different token is accepted only when
     the device's own cache explains it (the device token is what the
     sampling rule gives on the device cache, evaluated here in the same fp32
@@ -52,6 +53,35 @@ def bf16_spacing(x: np.ndarray) -> np.ndarray:
     e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
     e = np.where(a > 0, np.maximum(e, -126.0), -126.0)
     return np.exp2(e - 7)
+
+
+def bias_tolerance(bias_o_bits: np.ndarray, abs_dot: np.ndarray, r: int) -> np.ndarray:
+    """Largest |bias_dev - bias_orc| allowed per element.
+
+    bias_orc = bf16(S) for the exact sum S; bias_dev = bf16(S_dev) for an fp32
+    accumulation of the r exact products, |S_dev - S| <= E = r 2^-24 sum|h e|
+    (the recursive-summation bound; abs_dot = sum_k |h_vk e_k|).  The two
+    roundings add at most half a bf16 spacing each at magnitude
+    max(|S|, |S_dev|) <= |bias_orc| + spacing/2 + E, so the difference is at
+    most spacing(|bias_orc| + spacing(bias_orc)/2 + E) + E: one bf16 ulp
+    unless the sum nearly cancels."""
+    b = np.abs(f32(bias_o_bits).astype(np.float64))
+    E = r * 2.0**-24 * np.asarray(abs_dot, dtype=np.float64)
+    return bf16_spacing(b + 0.5 * bf16_spacing(b) + E) + E
+
+
+class AbsDot:
+    """sum_k |head[v, k] * embed[p, k]| for every v (the scale of the fp32
+    accumulation error), with |head| converted once."""
+
+    def __init__(self, w):
+        self.abs_head = np.abs(f32(w.head[:w.V]))
+        self.abs_embed = np.abs(f32(w.embed))
+
+    def __call__(self, p: int) -> np.ndarray:
+        # an fp32 sum of r <= 512 positive terms is within r 2^-24 < 2^-10 of
+        # its exact value, so the inflated result is an upper bound
+        return (self.abs_head @ self.abs_embed[p]).astype(np.float64) * (1.0 + 2.0**-10)
 
 
 def is_nan_bits(bits: np.ndarray) -> np.ndarray:
@@ -108,6 +138,7 @@ def walk(w, tok_gpu, cache_gpu, gumbel, rows=None, exact=False) -> Stats:
     sidx = np.arange(w.rows) if w.state_idx is None else w.state_idx
     rows = range(w.rows) if rows is None else rows
     V = w.V
+    absdot = None if exact else AbsDot(w)
     for b in rows:
         s = int(sidx[b])
         if s < 0:
@@ -137,7 +168,8 @@ def walk(w, tok_gpu, cache_gpu, gumbel, rows=None, exact=False) -> Stats:
                 fg = f32(c_g).astype(np.float64)
                 fin = ~nan_o & np.isfinite(fo) & np.isfinite(fg)
                 assert np.array_equal(fo[~nan_o & ~fin], fg[~nan_o & ~fin]), f"row {b} step {i}: infinities differ"
-                bound = (bf16_spacing(f32(bias_o)) * abs(w.mult)
+                tol_bias = bias_tolerance(bias_o, absdot(p), w.r)
+                bound = (tol_bias * abs(w.mult)
                          + bf16_spacing(np.maximum(np.abs(fo), np.abs(fg))))
                 bad = fin & (np.abs(fo - fg) > bound)
                 assert not bad.any(), (f"row {b} step {i}: {int(bad.sum())} cache values beyond the "

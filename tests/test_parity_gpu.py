@@ -81,6 +81,18 @@ def test_noise_fill_matches_oracle(rows, N, V):
     assert np.all(err <= 2.0**-22 * (1.0 + np.abs(ref)))
 
 
+def bias_check(w, absdot, p, bias_o, bias_dev, where):
+    """With base = 0 and no transform the cache holds the device bias: it
+    must lie within chain_check.bias_tolerance of the oracle's.  Returns the
+    per-element ulp distances and how many exceed one ulp."""
+    d = np.abs(chain_check.ordinal(bias_o) - chain_check.ordinal(bias_dev))
+    diff = np.abs(chain_check.f32(bias_o).astype(np.float64) - chain_check.f32(bias_dev).astype(np.float64))
+    tol = chain_check.bias_tolerance(bias_o, absdot(p), w.r)
+    bad = diff > tol
+    assert not bad.any(), f"{where}: bias beyond tolerance at v={int(np.flatnonzero(bad)[0])}"
+    return d, int((d > 1).sum())
+
+
 # ------------------------------------------------------------ exact chain --
 
 def test_tiny_exact_bit_exact():
@@ -125,29 +137,115 @@ def test_exact_rank512_small():
     chain_check.walk(w, t, c, g, exact=True)
 
 
-def test_bias_within_one_bf16_ulp_random_weights():
+def test_bias_tolerance_random_weights():
     """With base = 0 and no transform the cache holds the bias itself: the
     device's fp32-accumulated bias is within one bf16 ulp of the oracle's
-    exactly summed bias on random N(0, 0.02) weights at full vocabulary."""
+    exactly summed bias on random N(0, 0.02) weights at full vocabulary,
+    except where the sum nearly cancels (then within the fp32 accumulation
+    bound; at most 1e-4 of the elements)."""
     w = synth.make("bias", 129280, 256, 2, 2, seed=31, temperature=[0.0, 0.0])
     w.base[:] = 0
     g = oracle_noise(w)
     t, c, _ = run(w, gumbel=g)
-    exact = total = 0
+    absdot = chain_check.AbsDot(w)
+    exact = total = over = 0
     for b in range(w.rows):
         p = int(w.prev[b])
         for i in range(w.N):
             tok_o, _, bias_o = oracle.step(w.base[b, i], w.head, w.embed, p, 0.0, g[b, i],
                                            with_bias=True)
-            d = np.abs(chain_check.ordinal(bias_o) - chain_check.ordinal(c[b, i]))
-            assert d.max() <= 1, f"row {b} step {i}: bias differs by {int(d.max())} ulp"
+            d, beyond = bias_check(w, absdot, p, bias_o, c[b, i], f"row {b} step {i}")
             exact += int((d == 0).sum())
+            over += beyond
             total += d.size
             if int(t[b, i]) != tok_o:
                 break
             p = tok_o
-    say(f"  bias bit-exact {exact}/{total}")
+    say(f"  bias bit-exact {exact}/{total}, beyond one ulp (near-cancelling sums) {over}")
     assert exact > 0.99 * total
+    assert over <= 1e-4 * total
+
+
+# --------------------------------------------------------- one request row --
+# A single request row runs its own kernel variant (vector-ALU bias that stays
+# in registers); these cases cover both ranks, ragged vocabularies, greedy
+# rows, the output transform, the bias tolerance and the NaN / tie rules.
+
+@pytest.mark.parametrize("V,r,N,T", [
+    (16, 256, 3, 1.0),
+    (1040, 512, 4, 0.7),
+    (8192 + 48, 256, 5, 0.0),
+    (4096 + 16, 512, 3, 1.5),
+    (20000, 256, 6, 0.6),
+])
+def test_one_row_exact(V, r, N, T):
+    w = synth.make(f"one_V{V}_r{r}", V, r, 1, N, seed=V + r, weights="int", base_std=2.0,
+                   temperature=T)
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    st = chain_check.walk(w, t, c, g, exact=True)
+    assert st.token_match == st.pairs == N
+
+
+@pytest.mark.parametrize("V,r", [(129280, 256), (65536 + 16, 512)])
+def test_one_row_bias_tolerance(V, r):
+    """The one-row bias (dot2 accumulation) on random N(0, 0.02) weights:
+    within one bf16 ulp of the oracle's exactly summed bias except where the
+    sum nearly cancels (then within the fp32 accumulation bound)."""
+    w = synth.make(f"one_bias_r{r}", V, r, 1, 3, seed=41 + r, temperature=0.0)
+    w.base[:] = 0
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    p = int(w.prev[0])
+    absdot = chain_check.AbsDot(w)
+    exact = total = over = 0
+    for i in range(w.N):
+        tok_o, _, bias_o = oracle.step(w.base[0, i], w.head, w.embed, p, 0.0, g[0, i], with_bias=True)
+        d, beyond = bias_check(w, absdot, p, bias_o, c[0, i], f"step {i}")
+        exact += int((d == 0).sum())
+        over += beyond
+        total += d.size
+        if int(t[0, i]) != tok_o:
+            break
+        p = tok_o
+    say(f"  bias bit-exact {exact}/{total}, beyond one ulp (near-cancelling sums) {over}")
+    assert exact > 0.99 * total
+    assert over <= 1e-4 * total
+
+
+def test_one_row_transform_random_weights():
+    w = synth.make("one_cap", 129280, 256, 1, 8, seed=43, peaks=32, temperature=1.0,
+                   mult=0.5, cap=30.0)
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    st = chain_check.walk(w, t, c, g)
+    say("  " + st.summary())
+    assert len(st.mismatches) <= 1
+
+
+@pytest.mark.parametrize("r", [256, 512])
+def test_one_row_nan_and_ties(r):
+    """Greedy single row: NaN logits at two ids on even steps (the lower id
+    wins), three exact 40.0 ties on odd steps (the lowest id wins)."""
+    V, N = 50000, 6
+    w = synth.make(f"one_nan_r{r}", V, r, 1, N, seed=47 + r, temperature=0.0)
+    rng = np.random.default_rng(48 + r)
+    nan_bits = np.uint16(0x7FC0)
+    forty = synth.to_bf16_bits(np.array([40.0], dtype=np.float32))[0]
+    expect = []
+    for i in range(N):
+        ids = np.sort(rng.choice(V, size=3, replace=False))
+        if i % 2 == 0:
+            w.base[0, i, ids[1:]] = nan_bits
+            expect.append(int(ids[1]))
+        else:
+            w.base[0, i, ids] = forty
+            expect.append(int(ids[0]))
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    assert list(t[0]) == expect
+    st = chain_check.walk(w, t, c, g)
+    assert len(st.mismatches) == 0
 
 
 # ------------------------------------------------------- named workloads --
