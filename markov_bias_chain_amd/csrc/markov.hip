@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <limits.h>
 #include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -56,7 +57,9 @@ constexpr int kWaves = 8;                  // waves per workgroup
 constexpr int kThreads = kWaves * 64;      // 512 threads, one workgroup per CU
 constexpr int kSlots = 32;                 // 16-byte head vectors per lane per group
 constexpr int kAhead = 8;                  // request rows whose next-step inputs are prefetched
-constexpr int kOrdStride = 68;             // LDS row stride (words) of a wave's per-row lane tile
+constexpr int kBatch = 8;                  // request rows per epilogue batch
+constexpr int kLanesPerRow = 8;            // lanes per request row in a batch
+static_assert(kAhead == kBatch, "prefetched rows form one epilogue batch");
 constexpr int kHeader = 256;               // workspace header bytes
 constexpr int kMaxPollPerLane = 16;        // slots one lane polls (<= 1024 per row)
 constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz
@@ -74,6 +77,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_hw(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to_bf16_hw(f)); }
+// Two fp32 values to two bf16 (a in the low half) with one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
 
 // fp32 -> bf16, round to nearest even; NaN -> quiet NaN 0x7FC0.
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
@@ -176,6 +185,52 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   const uint32_t hi = row_fold_umax((uint32_t)(k >> 32));
   const uint32_t lo = row_fold_umax((uint32_t)(k >> 32) == hi ? (uint32_t)k : 0u);
   return ((uint64_t)hi << 32) | lo;
+}
+
+// A signed 32-bit key that orders non-NaN fp32 values as their values do
+// (-0 just below +0), and its inverse.
+__device__ __forceinline__ int order_key(float z) {
+  const int b = __float_as_int(z);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float order_key_inv(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
+// Signed maximum over the wave on the DPP path only: folds within each
+// 16-lane row, then row broadcasts (lane 15 into rows 1 and 3, lane 31 into
+// rows 2 and 3) leave the wave maximum in lane 63.
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ int dpp_i(int old, int x) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, ROW_MASK, 0xF, BOUND);
+}
+__device__ __forceinline__ int wave_imax(int x) {
+  x = max(x, dpp_i<0xB1, 0xF, true>(0, x));    // quad_perm [1,0,3,2]
+  x = max(x, dpp_i<0x4E, 0xF, true>(0, x));    // quad_perm [2,3,0,1]
+  x = max(x, dpp_i<0x141, 0xF, true>(0, x));   // row_half_mirror
+  x = max(x, dpp_i<0x140, 0xF, true>(0, x));   // row_mirror
+  x = max(x, dpp_i<0x142, 0xA, false>(x, x));  // row_bcast:15
+  x = max(x, dpp_i<0x143, 0xC, false>(x, x));  // row_bcast:31
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+// Reductions over each group of 8 consecutive lanes (xor 1, xor 2, then the
+// mirror within 8); every lane of a group ends with the group's result.
+__device__ __forceinline__ int group8_imax(int x) {
+  x = max(x, dpp_i<0xB1, 0xF, true>(0, x));
+  x = max(x, dpp_i<0x4E, 0xF, true>(0, x));
+  x = max(x, dpp_i<0x141, 0xF, true>(0, x));
+  return x;
+}
+__device__ __forceinline__ uint32_t group8_umin(uint32_t x) {
+  x = min(x, (uint32_t)dpp_i<0xB1, 0xF, true>(0, (int)x));
+  x = min(x, (uint32_t)dpp_i<0x4E, 0xF, true>(0, (int)x));
+  x = min(x, (uint32_t)dpp_i<0x141, 0xF, true>(0, (int)x));
+  return x;
+}
+__device__ __forceinline__ float group8_sum(float x) {
+  x += __int_as_float(dpp_i<0xB1, 0xF, true>(0, __float_as_int(x)));
+  x += __int_as_float(dpp_i<0x4E, 0xF, true>(0, __float_as_int(x)));
+  x += __int_as_float(dpp_i<0x141, 0xF, true>(0, __float_as_int(x)));
+  return x;
 }
 
 // ------------------------------------------------------ packed (score, id) --
@@ -418,7 +473,6 @@ __device__ __forceinline__ void group_bias(const uint4 (&h)[kSlots], const uint4
 template <int R>
 __device__ __forceinline__ float one_row_bias(const uint4 (&h)[kSlots], const uint4* __restrict__ e_row,
                                               int lane) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   constexpr int KT = R / 32, MT = kSlots / KT;
   const int q = lane >> 4;
   float acc[MT][2];
@@ -486,8 +540,6 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   __shared__ uint64_t s_key[kWaves][MARKOV_MAX_ROWS];
   __shared__ float s_wsum[kWaves][MARKOV_MAX_ROWS];
   __shared__ float s_bias[kWaves][kRowPass * BS];  // each wave's [16][RPG] bias tile
-  __shared__ uint16_t s_inb[kWaves][kRowPass][64];  // a pass's base logits (bf16 bits) per lane
-  __shared__ __align__(16) uint32_t s_ing[kWaves][kRowPass][kOrdStride];  // a pass's noise bits per lane, then score ordinals
   __shared__ int s_abort;
   __shared__ int s_miss;
   __shared__ int s_spec[kAhead];   // phase A's guess of the row's winner
@@ -561,51 +613,171 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   }
   __syncthreads();
 
-  // Base logit (bf16 bits) and noise of row b at step i, vocab id v: a
-  // uniform row pointer plus a 32-bit lane offset.
-  auto load_in = [&](int i, int b, int v, uint32_t& bl, float& gl) {
-    const uint16_t* brow = p.base + ((long long)b * p.base_rs + (long long)i * p.base_ss);
-    bl = brow[(unsigned)v];
-    gl = 0.0f;
-    if (MODE == 0 && s_T[b] > 0.0f) {
-      const float* grow = p.gumbel + ((size_t)b * N + i) * (size_t)V;
-      gl = grow[(unsigned)v];
-    }
-  };
-  // With a resident head and at most kAhead rows, the next step's base logits
-  // and noise (which do not depend on the winner) are loaded while the
-  // current step's exchange is in flight.
+  // ---- per-step inputs.
+  // Single row (lane = vocab id): the base logit and noise of lane lr's id,
+  // prefetched for the next step while the current step's exchange is in
+  // flight (they do not depend on the winner).
   constexpr bool ahead = RES && SMALL;
   const int v_res = (wg * kWaves + wave) * RPG + lr;
   const bool own_res = (wg * kWaves + wave) < NG && v_res < V && lane_owns;
-  uint32_t nbl[kAhead / 2];  // two bf16 base logits per register
-  float ngl[kAhead];
-  auto prefetch = [&](int i) {
-#pragma unroll
-    for (int bi = 0; bi < kAhead; ++bi) {
-      uint32_t bv = 0;
-      ngl[bi] = 0.0f;
-      if (bi < rows && s_active[bi] && own_res) load_in(i, bi, v_res, bv, ngl[bi]);
-      if (bi & 1) nbl[bi / 2] |= bv << 16;
-      else nbl[bi / 2] = bv;
+  uint32_t one_base = 0;
+  float one_noise = 0.0f;
+  auto prefetch_one = [&](int i) {
+    one_base = 0;
+    one_noise = 0.0f;
+    if (s_active[0] && own_res) {
+      one_base = p.base[(long long)i * p.base_ss + v_res];
+      if (MODE == 0 && s_T[0] > 0.0f) one_noise = p.gumbel[(size_t)i * V + v_res];
     }
   };
+  // Several rows: a batch of kBatch request rows is spread over the wave,
+  // kLanesPerRow lanes per row; lane l serves row b0 + (l >> 3) and the IPL
+  // consecutive vocab ids g * RPG + (l & 7) * IPL + 0 .. IPL - 1 of group g,
+  // so its base logits, noise and cache values move in 16-byte vectors.
+  // V is a multiple of 16, so a lane's ids are all valid or all not.
+  constexpr int IPL = RPG / kLanesPerRow;  // vocab ids per lane: 8 (r = 256) or 4 (r = 512)
+  static_assert(kBatch * kLanesPerRow == 64 && (IPL == 8 || IPL == 4), "batch layout");
+  const int rr = lane >> 3;  // row of the batch
+  const int q = lane & 7;    // vocab segment of the group
+  struct LaneIn {
+    uint32_t bw[IPL / 2];  // base logits, two bf16 per word
+    float nz[IPL];         // noise
+  };
+  auto load_rows = [&](int i, int b0, int g, LaneIn& in) {
+#pragma unroll
+    for (int e = 0; e < IPL / 2; ++e) in.bw[e] = 0;
+#pragma unroll
+    for (int e = 0; e < IPL; ++e) in.nz[e] = 0.0f;
+    const int b = b0 + rr;
+    const int v0 = g * RPG + q * IPL;
+    if (b < rows && g < NG && v0 < V && s_active[b]) {
+      const uint16_t* brow = p.base + ((long long)b * p.base_rs + (long long)i * p.base_ss) + v0;
+      if constexpr (IPL == 8) {
+        const uint4 t = *reinterpret_cast<const uint4*>(brow);
+        in.bw[0] = t.x, in.bw[1] = t.y, in.bw[2] = t.z, in.bw[3] = t.w;
+      } else {
+        const uint2 t = *reinterpret_cast<const uint2*>(brow);
+        in.bw[0] = t.x, in.bw[1] = t.y;
+      }
+      if (MODE == 0 && s_T[b] > 0.0f) {
+        const float4* grow = reinterpret_cast<const float4*>(p.gumbel + ((size_t)b * N + i) * (size_t)V + v0);
+#pragma unroll
+        for (int e4 = 0; e4 < IPL / 4; ++e4) {
+          const float4 t = grow[e4];
+          in.nz[4 * e4] = t.x, in.nz[4 * e4 + 1] = t.y, in.nz[4 * e4 + 2] = t.z, in.nz[4 * e4 + 3] = t.w;
+        }
+      }
+    }
+  };
+  LaneIn pre;  // the resident SMALL kernel's prefetched batch
+  auto prefetch = [&](int i) {
+    if constexpr (ONE) prefetch_one(i);
+    else load_rows(i, 0, wg * kWaves + wave, pre);
+  };
   if (ahead) prefetch(0);
+
+  // Epilogue of the batch of rows b0 .. b0 + nb - 1 in the layout above:
+  // per vocab id, bias -> bf16, + base logit, output transform, bf16 cache
+  // store (one vector per lane), score; then per row the best (score, id)
+  // key of the wave's group and, in mode 1, the group's sum of exp(z - max).
+  // sbt is the wave's bias tile row block of the batch (row rr at rr * BS).
+  auto epilogue_rows = [&](int i, int b0, int nb, int g, const float* sbt, const LaneIn& in) {
+    const int b = b0 + rr;
+    const int v0 = g * RPG + q * IPL;
+    const bool ok = rr < nb && g < NG && v0 < V && s_active[b];
+    const float T = s_T[b];
+    float bsum[IPL];
+#pragma unroll
+    for (int e4 = 0; e4 < IPL / 4; ++e4) {
+      const float4 t = *reinterpret_cast<const float4*>(sbt + rr * BS + q * IPL + 4 * e4);
+      bsum[4 * e4] = t.x, bsum[4 * e4 + 1] = t.y, bsum[4 * e4 + 2] = t.z, bsum[4 * e4 + 3] = t.w;
+    }
+    float x[IPL];
+#pragma unroll
+    for (int e = 0; e < IPL; ++e) {
+      const uint32_t w = in.bw[e / 2];
+      const float base = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      x[e] = __fmul_rn(__fadd_rn(base, bf16_round(bsum[e])), p.mult);
+    }
+    if (p.has_cap) {
+#pragma unroll
+      for (int e = 0; e < IPL; ++e) x[e] = __fmul_rn(tanhf(__fmul_rn(x[e], p.inv_cap)), p.cap);
+    }
+    uint32_t cw[IPL / 2];
+    float z[IPL];
+#pragma unroll
+    for (int e = 0; e < IPL / 2; ++e) {
+      cw[e] = f32x2_to_bf16x2(x[2 * e], x[2 * e + 1]);
+      z[2 * e] = __uint_as_float(cw[e] << 16);
+      z[2 * e + 1] = __uint_as_float(cw[e] & 0xFFFF0000u);
+    }
+    if (ok) {
+      uint16_t* crow = p.cache + ((long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss) + v0;
+      if constexpr (IPL == 8) *reinterpret_cast<uint4*>(crow) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+      else *reinterpret_cast<uint2*>(crow) = make_uint2(cw[0], cw[1]);
+    }
+    // Scores: T <= 0 is argmax; c / 1 is exact.
+    if (T > 0.0f && T != 1.0f) {
+#pragma unroll
+      for (int e = 0; e < IPL; ++e) z[e] = __fdiv_rn(z[e], T);
+    }
+    if (MODE == 0 && T > 0.0f) {
+#pragma unroll
+      for (int e = 0; e < IPL; ++e) z[e] = __fadd_rn(z[e], in.nz[e]);
+    }
+    // This lane's best: the first NaN, else the first maximum (order keys
+    // of z + 0, which makes -0 equal to +0).
+    int kbest = INT_MIN;
+    uint32_t ebest = 0, enan = IPL;
+#pragma unroll
+    for (int e = 0; e < IPL; ++e) {
+      const bool isn = isnan(z[e]);
+      enan = (isn && enan == IPL) ? e : enan;
+      const int k = isn ? INT_MIN : order_key(__fadd_rn(z[e], 0.0f));
+      ebest = k > kbest ? e : ebest;
+      kbest = k > kbest ? k : kbest;
+    }
+    if (!ok) kbest = INT_MIN, enan = IPL;
+    // The row's best over its kLanesPerRow lanes.
+    const int gmax = group8_imax(kbest);
+    const uint32_t gid = group8_umin(kbest != INT_MIN && kbest == gmax ? (uint32_t)v0 + ebest : 0xFFFFFFFFu);
+    const uint32_t gnan = group8_umin(enan < IPL ? (uint32_t)v0 + enan : 0xFFFFFFFFu);
+    float wsum = 0.0f;
+    if (MODE == 1) {
+      const float m = order_key_inv(gmax);
+      float s = 0.0f;
+      if (ok && gmax != INT_MIN && isfinite(m)) {
+#pragma unroll
+        for (int e = 0; e < IPL; ++e) s += isnan(z[e]) ? 0.0f : __expf(z[e] - m);
+      }
+      wsum = group8_sum(s);
+    }
+    if (q == 0 && rr < nb && s_active[b]) {
+      const uint64_t key = gnan != 0xFFFFFFFFu ? ((0xFFFFFFFFull << 32) | (0xFFFFFFFFu - gnan))
+                           : gmax != INT_MIN ? (((uint64_t)score_ord(order_key_inv(gmax)) << 32) | (0xFFFFFFFFu - gid))
+                                             : kNoCandidate;
+      if (MODE == 0) {
+        if (key > s_key[wave][b]) s_key[wave][b] = key;
+      } else {
+        s_key[wave][b] = key;
+        s_wsum[wave][b] = wsum;
+      }
+    }
+  };
 
   float* sb = s_bias[wave];
   // Local work of step i: bias, epilogue, keys for every chunk of this
   // workgroup (mode 1 also publishes each chunk's partials).
   auto local_work = [&](int i) {
-    // ---- local work: bias, epilogue, keys for every chunk of this workgroup.
     if (lane == 0)
       for (int b = 0; b < rows; ++b) s_key[wave][b] = kNoCandidate;
     for (int j = 0; wg + j * G < NC; ++j) {
       const int c = wg + j * G;
       const int g = c * kWaves + wave;
-      const int v = g * RPG + lr;
-      const bool own = g < NG && v < V && lane_owns;
+      LaneIn cur, nxt;
       if constexpr (!RES) {
-        // Stream this group's head (all 32 tiles in flight at once).
+        // Stream this group's head (all 32 tiles in flight at once), with
+        // the first batch's inputs.
 #pragma unroll
         for (int s2 = 0; s2 < kSlots; ++s2)
           h[s2] = g < NG ? load_head_tile<R>(p.head, g, s2, lane, V) : make_uint4(0, 0, 0, 0);
@@ -614,11 +786,13 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // Lane lr's vocab id v: bias, cache value and score ordinal in
         // registers; one wave maximum and a ballot give the lowest id of the
         // maximum (or of the NaNs, which order first).
+        const int v = g * RPG + lr;
+        const bool own = g < NG && v < V && lane_owns;
         const float bsum = one_row_bias<R>(h, s_e, lane);
         uint32_t ord = 0;
         if (s_active[0] && own) {
           const float T = s_T[0];
-          float x = __fadd_rn(bf16_to_f32(nbl[0] & 0xFFFFu), bf16_round(bsum));
+          float x = __fadd_rn(bf16_to_f32(one_base), bf16_round(bsum));
           x = __fmul_rn(x, p.mult);
           if (p.has_cap) x = __fmul_rn(tanhf(__fmul_rn(x, p.inv_cap)), p.cap);
           const uint32_t cb = f32_to_bf16_hw(x);
@@ -627,7 +801,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           float z = bf16_to_f32(cb);
           if (T > 0.0f) {
             if (T != 1.0f) z = __fdiv_rn(z, T);  // c / 1 is exact
-            z = __fadd_rn(z, ngl[0]);
+            z = __fadd_rn(z, one_noise);
           }
           ord = score_ord(z);
         }
@@ -638,105 +812,25 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
                                : kNoCandidate;
         continue;
       }
-      for (int b0 = 0; b0 < rows; b0 += kRowPass) {
-        const int nb = rows - b0 < kRowPass ? rows - b0 : kRowPass;
-        // This pass's base and noise, staged in LDS for the epilogue loop:
-        // prefetched during the last exchange, or issued now so that the
-        // MFMAs cover their latency.
+      // Batches of kBatch rows; a pass of kRowPass rows shares one MFMA
+      // bias tile.  Without a prefetch, the next batch's inputs are loaded
+      // before the current batch's epilogue.
+      static_assert(kRowPass == 2 * kBatch, "a pass is two batches");
+      const int nbat = (rows + kBatch - 1) / kBatch;
+      if constexpr (!ahead) load_rows(i, 0, g, cur);
+      for (int t = 0; t < nbat; ++t) {
+        const int b0 = t * kBatch;
+        if ((t & 1) == 0) {
+          const int np = rows - b0 < kRowPass ? rows - b0 : kRowPass;
+          group_bias<R>(h, s_e, b0, np, lane, sb);
+        }
+        const int nb = rows - b0 < kBatch ? rows - b0 : kBatch;
         if constexpr (ahead) {
-#pragma unroll
-          for (int bi = 0; bi < kAhead; ++bi) {
-            if (bi < nb) {
-              s_inb[wave][bi][lane] = (uint16_t)(nbl[bi / 2] >> (16 * (bi & 1)));
-              s_ing[wave][bi][lane] = __float_as_uint(ngl[bi]);
-            }
-          }
-          group_bias<R>(h, s_e, b0, nb, lane, sb);
+          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, pre);
         } else {
-          uint32_t bl[kRowPass];
-          float gl[kRowPass];
-#pragma unroll
-          for (int bi = 0; bi < kRowPass; ++bi) {
-            bl[bi] = 0;
-            gl[bi] = 0.0f;
-            if (bi < nb && s_active[b0 + bi] && own) load_in(i, b0 + bi, v, bl[bi], gl[bi]);
-          }
-          group_bias<R>(h, s_e, b0, nb, lane, sb);
-#pragma unroll
-          for (int bi = 0; bi < kRowPass; ++bi) {
-            if (bi < nb) {
-              s_inb[wave][bi][lane] = (uint16_t)bl[bi];
-              s_ing[wave][bi][lane] = __float_as_uint(gl[bi]);
-            }
-          }
-        }
-        // Epilogue.  (1) Per request row, every lane turns its bias into the
-        // cache value and the score, stored as an order-preserving ordinal
-        // in the wave's LDS tile (0 = no candidate; the noise slot of the
-        // same lane is reused).  (2) All rows are reduced at once: lane
-        // (r = l & 15, quarter l >> 4) folds 16 ordinals of row r, then the
-        // four quarters combine.  (3) Per row one compare and ballot find the
-        // lowest lane holding the maximum; lane order is vocab order, so that
-        // is the lowest id of the maximum (or of the NaNs, which order first).
-        uint32_t* so = &s_ing[wave][0][0];  // all accesses are 32-bit words
-        for (int bi = 0; bi < nb; ++bi) {
-          const int b = b0 + bi;
-          uint32_t ord = 0;
-          if (s_active[b] && own) {
-            const float T = s_T[b];
-            const float bias = bf16_round(sb[bi * BS + lr]);
-            float x = __fadd_rn(bf16_to_f32(s_inb[wave][bi][lane]), bias);
-            x = __fmul_rn(x, p.mult);
-            if (p.has_cap) x = __fmul_rn(tanhf(__fmul_rn(x, p.inv_cap)), p.cap);
-            const uint32_t cb = f32_to_bf16_hw(x);
-            uint16_t* crow = p.cache + ((long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss);
-            crow[(unsigned)v] = (uint16_t)cb;
-            const float cf = bf16_to_f32(cb);
-            float z = cf;
-            if (T > 0.0f) {
-              if (T != 1.0f) z = __fdiv_rn(cf, T);  // c / 1 is exact
-              if (MODE == 0) z = __fadd_rn(z, __uint_as_float(so[bi * kOrdStride + lane]));
-            }
-            ord = score_ord(z);
-          }
-          so[bi * kOrdStride + lane] = ord;
-        }
-        uint32_t rmax;
-        {
-          const uint4* q4 = reinterpret_cast<const uint4*>(so + (lane & 15) * kOrdStride + 16 * (lane >> 4));
-          rmax = 0;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint4 t4 = q4[k];
-            rmax = max(rmax, max(max(t4.x, t4.y), max(t4.z, t4.w)));
-          }
-          rmax = max(rmax, (uint32_t)xsh16((int)rmax));
-          rmax = max(rmax, (uint32_t)xsh32((int)rmax));
-        }
-        for (int bi = 0; bi < nb; ++bi) {
-          const int b = b0 + bi;
-          if (!s_active[b]) continue;
-          const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)rmax, bi);
-          const uint32_t mine = so[bi * kOrdStride + lane];
-          const uint64_t hit = __ballot(m != 0 && mine == m);
-          const uint64_t wk = hit ? (((uint64_t)m << 32) | (0xFFFFFFFFu - (uint32_t)(g * RPG + __builtin_ctzll(hit))))
-                                  : kNoCandidate;
-          if (MODE == 0) {
-            if (lane == 0 && wk > s_key[wave][b]) s_key[wave][b] = wk;
-          } else {
-            // Per-wave softmax partial relative to the wave's own maximum.
-            const float mw = ord_score(m);
-            float e = 0.0f;
-            if (mine != 0 && m != 0 && isfinite(mw)) {
-              const float z = ord_score(mine);
-              if (!isnan(z)) e = expf(z - mw);
-            }
-            const float ws = wave_sum_fast(e);
-            if (lane == 0) {
-              s_key[wave][b] = wk;
-              s_wsum[wave][b] = ws;
-            }
-          }
+          if (t + 1 < nbat) load_rows(i, b0 + kBatch, g, nxt);
+          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur);
+          cur = nxt;
         }
       }
       if (MODE == 1) {
