@@ -34,18 +34,28 @@ KERNEL_SRC = os.path.join(ROOT, "markov_bias_chain_amd", "csrc", "markov.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "chain_kernel_dsv41_single_row_pmc.md")
 
 
+def kernel_source_digest() -> str:
+    """sha256 prefix of the kernel source with comments and blank lines
+    removed, so that a comment edit does not invalidate counter readings."""
+    import hashlib
+    import re
+
+    text = open(KERNEL_SRC).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
+
+
 def measured_traffic():
     """HBM-side bytes per chain launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source (else None)."""
-    import hashlib
-
+    summary, if it was taken on the current kernel code (else None)."""
     try:
         text = open(TRAFFIC_PROFILE).read()
     except OSError:
         return None
     fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and " " not in line.split(": ")[0])
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
-    if fields.get("kernel_source_sha256_prefix", "").strip() != sha:
+    if fields.get("kernel_code_sha256_prefix", "").strip() != kernel_source_digest():
         return None
     return int(fields["traffic_bytes_per_launch"])
 

@@ -13,25 +13,32 @@
 // Design (one GPU):
 //  * markov_noise_fill: one thread per 4 consecutive vocab ids, one 16-byte
 //    store; the (seed, row, step) part of the hash is computed per thread.
-//  * markov_chain_sample: ONE persistent cooperative launch runs all N
-//    positions.  The vocabulary is cut into groups of 16384 / r head rows
-//    (32 KiB of bf16 head each); a wavefront owns one group per chunk, and a
-//    chunk is 8 consecutive groups (one per wave of a 512-thread workgroup).
-//    The first chunk of every workgroup stays in VGPRs for the whole launch
-//    (128 VGPRs per lane), so the head is read from HBM once per call when
-//    the grid covers the vocabulary; further chunks are streamed every step.
-//  * The bias GEMV is 64-wide wavefront work: each lane holds 16-byte head
-//    vectors (8 bf16 of one row) and dots them with the matching 8 bf16 of
-//    the embedding row with v_dot2_f32_bf16; a transposing butterfly then
-//    leaves one finished row sum per lane, so the epilogue (logit, cache
-//    store, score, key) is one vocab id per lane.
+//  * markov_chain_sample: ONE persistent launch (at most one workgroup per
+//    CU) runs all N positions.  The vocabulary is cut into groups of
+//    16384 / r head rows (32 KiB of bf16 head each); a wavefront owns one
+//    group per chunk, and a chunk is 8 consecutive groups (one per wave of a
+//    512-thread workgroup).  When the grid covers every chunk, each wave's
+//    group stays in VGPRs for the whole launch (128 VGPRs per lane), so the
+//    head is read from HBM once per call; otherwise groups are streamed every
+//    step.
+//  * The bias GEMV: up to 16 request rows per v_mfma_f32_16x16x32_bf16 pass
+//    (head tiles as A, the rows' embeddings from LDS as B), results through
+//    a per-wave LDS tile; a single request row uses v_dot2c_f32_bf16 and a
+//    permlane reduce-scatter so that each lane ends with its vocab id's sum.
+//  * The epilogue (bias -> bf16, + base logit, output transform, bf16 cache
+//    store, score, per-row best key) handles batches of 8 request rows with
+//    8 lanes per row and 8 (r = 256) or 4 (r = 512) consecutive ids per
+//    lane, so logits, noise and cache move in 16-byte vectors; per-row
+//    maxima are DPP reductions over 8 lanes.
 //  * Each step ends in a grid-wide exchange through the workspace: every
 //    workgroup stores its candidate (a packed 64-bit (score, index) key) in
 //    its own slot with a single agent-scope store, and every workgroup polls
 //    all slots, so there is no contended atomic and no second flag.  A zero
 //    slot means "not arrived"; real keys are never zero.  Alternate calls use
 //    alternate halves of the workspace and each call clears the half the
-//    next call will use, so no reset launch is needed.
+//    next call will use, so no reset launch is needed.  A single row
+//    overlaps the next step with the tail of the exchange (speculation on
+//    the best key seen once 7/8 of the slots have arrived).
 //  * Mode 1 (inverse CDF) publishes per-chunk (max key, sum of exp) partials;
 //    a leader workgroup per row locates the chunk holding u * S, the chunk's
 //    owner scans it in vocabulary order and publishes the token.
@@ -62,6 +69,7 @@ constexpr int kLanesPerRow = 8;            // lanes per request row in a batch
 static_assert(kAhead == kBatch, "prefetched rows form one epilogue batch");
 constexpr int kHeader = 256;               // workspace header bytes
 constexpr int kMaxPollPerLane = 16;        // slots one lane polls (<= 1024 per row)
+constexpr int kLeaderRegs = 4;             // inverse-CDF chunks per lane kept in registers by a leader
 constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz
 
 // ----------------------------------------------------------- bf16 helpers --
@@ -80,6 +88,8 @@ __device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to
 // Two fp32 values to two bf16 (a in the low half) with one v_cvt_pk_bf16_f32.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
@@ -224,6 +234,18 @@ __device__ __forceinline__ uint32_t group8_umin(uint32_t x) {
   x = min(x, (uint32_t)dpp_i<0xB1, 0xF, true>(0, (int)x));
   x = min(x, (uint32_t)dpp_i<0x4E, 0xF, true>(0, (int)x));
   x = min(x, (uint32_t)dpp_i<0x141, 0xF, true>(0, (int)x));
+  return x;
+}
+// Inclusive prefix sum over the wave in lane order on the DPP path: shifts
+// by 1, 2, 4, 8 within each 16-lane row (lanes shifted in from outside the
+// row add 0), then the row broadcasts carry rows 0..2 into the rows above.
+__device__ __forceinline__ float wave_incl_scan(float x) {
+  x += __int_as_float(dpp_i<0x111, 0xF, true>(0, __float_as_int(x)));  // row_shr:1
+  x += __int_as_float(dpp_i<0x112, 0xF, true>(0, __float_as_int(x)));  // row_shr:2
+  x += __int_as_float(dpp_i<0x114, 0xF, true>(0, __float_as_int(x)));  // row_shr:4
+  x += __int_as_float(dpp_i<0x118, 0xF, true>(0, __float_as_int(x)));  // row_shr:8
+  x += __int_as_float(dpp_i<0x142, 0xA, false>(0, __float_as_int(x)));  // row_bcast:15
+  x += __int_as_float(dpp_i<0x143, 0xC, false>(0, __float_as_int(x)));  // row_bcast:31
   return x;
 }
 __device__ __forceinline__ float group8_sum(float x) {
@@ -534,12 +556,15 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   __shared__ int s_state[MARKOV_MAX_ROWS];
   __shared__ int s_active[MARKOV_MAX_ROWS];
   __shared__ float s_T[MARKOV_MAX_ROWS];
+  __shared__ int64_t s_seed[MARKOV_MAX_ROWS];  // mode 1: the rows' seeds
   __shared__ int s_tok[MARKOV_MAX_ROWS];
   __shared__ int s_need[MARKOV_MAX_ROWS];
   __shared__ uint64_t s_dec[MARKOV_MAX_ROWS];
   __shared__ uint64_t s_key[kWaves][MARKOV_MAX_ROWS];
   __shared__ float s_wsum[kWaves][MARKOV_MAX_ROWS];
   __shared__ float s_bias[kWaves][kRowPass * BS];  // each wave's [16][RPG] bias tile
+  // the next step's base logits of every batch (inverse CDF, resident head, > kAhead rows)
+  __shared__ uint32_t s_pre[(MODE == 1 && RES && !SMALL) ? kWaves * (MARKOV_MAX_ROWS / kBatch) * (RPG / 16) * 64 : 1];
   __shared__ int s_abort;
   __shared__ int s_miss;
   __shared__ int s_spec[kAhead];   // phase A's guess of the row's winner
@@ -591,6 +616,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     s_state[b] = (int)st;
     s_active[b] = active;
     s_T[b] = p.temp[b];
+    if (MODE == 1) s_seed[b] = p.seeds[b];
     s_tok[b] = active ? (int)tok : 0;
     if (b < kAhead) s_use[b] = s_conf[b] = s_tok[b];
   }
@@ -648,7 +674,10 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     for (int e = 0; e < IPL / 2; ++e) in.bw[e] = 0;
 #pragma unroll
     for (int e = 0; e < IPL; ++e) in.nz[e] = 0.0f;
-    const int b = b0 + rr;
+    int b = b0 + rr;
+    // Opaque to the optimiser: otherwise it hoists every batch's 64-bit row
+    // address out of the step loop and spills them.
+    asm volatile("" : "+v"(b));
     const int v0 = g * RPG + q * IPL;
     if (b < rows && g < NG && v0 < V && s_active[b]) {
       const uint16_t* brow = p.base + ((long long)b * p.base_rs + (long long)i * p.base_ss) + v0;
@@ -675,6 +704,38 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     else load_rows(i, 0, wg * kWaves + wave, pre);
   };
   if (ahead) prefetch(0);
+  // Inverse CDF with a resident head and more than kAhead rows: every
+  // batch's base logits of the next step are loaded before the step's
+  // exchange and parked in LDS (s_pre, each wave's own lanes), so the local
+  // work reads no global memory.
+  constexpr bool stage = MODE == 1 && RES && !SMALL;
+  constexpr int kStageBatches = MARKOV_MAX_ROWS / kBatch;
+  LaneIn pst[stage ? kStageBatches : 1];
+  auto stage_load = [&](int i) {
+    const int nbat = (rows + kBatch - 1) / kBatch;
+#pragma unroll
+    for (int t = 0; t < (stage ? kStageBatches : 1); ++t)
+      if (t < nbat) load_rows(i, t * kBatch, wg * kWaves + wave, pst[t]);
+  };
+  auto stage_park = [&]() {
+    const int nbat = (rows + kBatch - 1) / kBatch;
+#pragma unroll
+    for (int t = 0; t < (stage ? kStageBatches : 1); ++t)
+      if (t < nbat) {
+#pragma unroll
+        for (int e = 0; e < IPL / 2; ++e) s_pre[((wave * kStageBatches + t) * (IPL / 2) + e) * 64 + lane] = pst[t].bw[e];
+      }
+  };
+  auto stage_fetch = [&](int t, LaneIn& in) {
+#pragma unroll
+    for (int e = 0; e < IPL / 2; ++e) in.bw[e] = s_pre[((wave * kStageBatches + t) * (IPL / 2) + e) * 64 + lane];
+#pragma unroll
+    for (int e = 0; e < IPL; ++e) in.nz[e] = 0.0f;
+  };
+  if (stage) {
+    stage_load(0);
+    stage_park();
+  }
 
   // Epilogue of the batch of rows b0 .. b0 + nb - 1 in the layout above:
   // per vocab id, bias -> bf16, + base logit, output transform, bf16 cache
@@ -713,8 +774,10 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     }
     if (ok) {
       uint16_t* crow = p.cache + ((long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss) + v0;
-      if constexpr (IPL == 8) *reinterpret_cast<uint4*>(crow) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-      else *reinterpret_cast<uint2*>(crow) = make_uint2(cw[0], cw[1]);
+      // Streaming stores: the cache is not read again by this launch (but
+      // for an inverse-CDF owner's one chunk).
+      if constexpr (IPL == 8) __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]}, reinterpret_cast<u32x4_t*>(crow));
+      else __builtin_nontemporal_store((u32x2_t){cw[0], cw[1]}, reinterpret_cast<u32x2_t*>(crow));
     }
     // Scores: T <= 0 is argmax; c / 1 is exact.
     if (T > 0.0f && T != 1.0f) {
@@ -817,7 +880,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       // before the current batch's epilogue.
       static_assert(kRowPass == 2 * kBatch, "a pass is two batches");
       const int nbat = (rows + kBatch - 1) / kBatch;
-      if constexpr (!ahead) load_rows(i, 0, g, cur);
+      if constexpr (!ahead && !stage) load_rows(i, 0, g, cur);
       for (int t = 0; t < nbat; ++t) {
         const int b0 = t * kBatch;
         if ((t & 1) == 0) {
@@ -827,6 +890,9 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         const int nb = rows - b0 < kBatch ? rows - b0 : kBatch;
         if constexpr (ahead) {
           epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, pre);
+        } else if constexpr (stage) {
+          stage_fetch(t, cur);
+          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur);
         } else {
           if (t + 1 < nbat) load_rows(i, b0 + kBatch, g, nxt);
           epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur);
@@ -869,7 +935,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // and its fix slot (written once it found out) holds the recomputed key.
   // On a wrong guess a workgroup reloads the embedding, redoes step i+1's
   // local work (overwriting its cache stores) and writes the fix slots.
-  constexpr bool speculate = MODE == 0 && ahead;
+  constexpr bool speculate = MODE == 0 && ahead && ONE;
 
   // Publication of the workgroup's best key per row (mode 0): row b by
   // thread b, or with speculation by lane 0 of wave b (the wave that also
@@ -1038,6 +1104,12 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     for (int i = 0; i < N; ++i) {
       local_work(i);
       if (MODE == 1 && ahead && i + 1 < N) prefetch(i + 1);
+      if (stage && i + 1 < N) {
+        // Parked at once: the wait for the loads overlaps the wait for the
+        // other workgroups' partials.
+        stage_load(i + 1);
+        stage_park();
+      }
       if (MODE == 0) {
         __syncthreads();
         publish(i);
@@ -1101,85 +1173,114 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       } else {
         // H2: the leader workgroup of each row (b % G) finds the chunk that
         // holds u * S and publishes it with the threshold in that chunk's
-        // own scale, or the token itself for an argmax row.
-        const int KPL = (NC + 63) / 64;  // chunks per lane, contiguous
+        // own scale, or the token itself for an argmax row.  Each lane owns
+        // KPL contiguous chunks.  With at most kLeaderRegs chunks per lane the
+        // polled slots stay in registers (a slot once written is final, so
+        // only missing ones are reloaded); otherwise they are read again.
+        const int KPL = (NC + 63) / 64;
         for (int b = wg; b < rows; b += G) {
           if (((b / G) % kWaves) != wave || !s_active[b]) continue;
           const uint64_t* kslots = L.keys + ((size_t)i * rows + b) * NC;
           const uint32_t* sslots = L.sums + ((size_t)i * rows + b) * NC;
+          const bool regs = KPL <= kLeaderRegs;
+          uint64_t kc[kLeaderRegs];
+          uint32_t sc[kLeaderRegs];
+#pragma unroll
+          for (int k = 0; k < kLeaderRegs; ++k) kc[k] = 0, sc[k] = 0;
+          // Slot k of this lane: (key, sum bits), 0 where the chunk does not exist.
+          auto slot = [&](int k, uint64_t& key, uint32_t& sum) {
+            const int c = lane * KPL + k;
+            key = 0, sum = 0;
+            if (c < NC) {
+              if (regs) {
+#pragma unroll
+                for (int r2 = 0; r2 < kLeaderRegs; ++r2)
+                  if (r2 == k) key = kc[r2], sum = sc[r2];
+              } else {
+                key = ld_agent(kslots + c);
+                sum = ld_agent32(sslots + c);
+              }
+            }
+          };
           for (;;) {
             bool all = true;
-            for (int k = 0; k < KPL; ++k) {
-              const int c = lane * KPL + k;
-              if (c < NC) all = all && ld_agent(kslots + c) != 0 && ld_agent32(sslots + c) != 0;
+            if (regs) {
+#pragma unroll
+              for (int k = 0; k < kLeaderRegs; ++k) {
+                const int c = lane * KPL + k;
+                if (k < KPL && c < NC) {
+                  if (kc[k] == 0) kc[k] = ld_agent(kslots + c);
+                  if (sc[k] == 0) sc[k] = ld_agent32(sslots + c);
+                  all = all && kc[k] != 0 && sc[k] != 0;
+                }
+              }
+            } else {
+              for (int k = 0; k < KPL; ++k) {
+                const int c = lane * KPL + k;
+                if (c < NC) all = all && ld_agent(kslots + c) != 0 && ld_agent32(sslots + c) != 0;
+              }
             }
             if (__all(all)) break;
             if (now_ticks() > deadline) {
-              if (lane == 0) {
-                s_abort = 1;
-                __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              }
+              slot_wait_abort();
               break;
             }
             __builtin_amdgcn_s_sleep(1);
           }
           uint64_t K = kNoCandidate;
           for (int k = 0; k < KPL; ++k) {
-            const int c = lane * KPL + k;
-            if (c < NC) K = umax64(K, ld_agent(kslots + c));
+            uint64_t key;
+            uint32_t sum;
+            slot(k, key, sum);
+            if (lane * KPL + k < NC) K = umax64(K, key);
           }
-          K = wave_max_key(K);
+          K = wave_max_u64(K);
           const float M = ord_score((uint32_t)(K >> 32));
           uint64_t dec;
           if (!(s_T[b] > 0.0f) || !isfinite(M)) {
             dec = (1ull << 63) | key_id(K);
           } else {
-            // Weights of this lane's chunks and their running sum.
+            // Weight of chunk c: its sum of exp(z - m_c) rescaled by
+            // exp(m_c - M); the lanes' totals are scanned in chunk order.
+            auto weight = [&](int k, float& e) -> float {
+              uint64_t key;
+              uint32_t sum;
+              slot(k, key, sum);
+              e = 0.0f;
+              if (lane * KPL + k >= NC) return 0.0f;
+              const float mc = ord_score((uint32_t)(key >> 32));
+              if (key == kNoCandidate || !isfinite(mc)) return 0.0f;
+              e = expf(mc - M);
+              return __uint_as_float(sum & 0x7FFFFFFFu) * e;
+            };
             float lsum = 0.0f;
             for (int k = 0; k < KPL; ++k) {
-              const int c = lane * KPL + k;
-              if (c < NC) {
-                const uint64_t kc = ld_agent(kslots + c);
-                const float mc = ord_score((uint32_t)(kc >> 32));
-                const float sc = __uint_as_float(ld_agent32(sslots + c) & 0x7FFFFFFFu);
-                if (kc != kNoCandidate && isfinite(mc)) lsum += sc * expf(mc - M);
-              }
+              float e;
+              lsum += weight(k, e);
             }
-            // Inclusive scan of the lane totals in lane order.
-            float incl = lsum;
-  #pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-              const float o = __shfl_up(incl, d);
-              if (lane >= d) incl += o;
-            }
-            const float total = __shfl(incl, 63);
-            const float excl = incl - lsum;
-            const float t = hash_uniform(noise_prefix(p.seeds[b], b, i)) * total;
-            // First chunk whose inclusive prefix exceeds t.
-            int found = -1;
-            float before = 0.0f, wfound = 0.0f;
-            float run = excl;
-            int last_pos = -1;
-            float last_before = 0.0f, last_w = 0.0f;
+            const float incl = wave_incl_scan(lsum);
+            const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+            const float t = hash_uniform(noise_prefix(s_seed[b], b, i)) * total;
+            // First chunk whose inclusive prefix exceeds t (else the last
+            // chunk with weight, when rounding left none above t).
+            int found = -1, last_pos = -1;
+            float before = 0.0f, wfound = 0.0f, last_before = 0.0f, last_w = 0.0f;
+            float run = incl - lsum;
             for (int k = 0; k < KPL; ++k) {
+              float e;
+              const float w = weight(k, e);
               const int c = lane * KPL + k;
-              if (c < NC) {
-                const uint64_t kc = ld_agent(kslots + c);
-                const float mc = ord_score((uint32_t)(kc >> 32));
-                const float sc = __uint_as_float(ld_agent32(sslots + c) & 0x7FFFFFFFu);
-                const float w = (kc != kNoCandidate && isfinite(mc)) ? sc * expf(mc - M) : 0.0f;
-                if (found < 0 && run + w > t) {
-                  found = c;
-                  before = run;
-                  wfound = expf(mc - M);
-                }
-                if (w > 0.0f) {
-                  last_pos = c;
-                  last_before = run;
-                  last_w = expf(mc - M);
-                }
-                run += w;
+              if (found < 0 && run + w > t) {
+                found = c;
+                before = run;
+                wfound = e;
               }
+              if (w > 0.0f) {
+                last_pos = c;
+                last_before = run;
+                last_w = e;
+              }
+              run += w;
             }
             const uint64_t hit = __ballot(found >= 0);
             int o;
@@ -1187,41 +1288,35 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             if (hit) {
               const int src = __builtin_ctzll(hit);
               o = __shfl(found, src);
-              const float bf = __shfl(before, src);
-              const float sf = __shfl(wfound, src);
-              tl = (t - bf) / sf;
+              tl = (t - __shfl(before, src)) / __shfl(wfound, src);
             } else {
-              // Rounding left no chunk above t: the last chunk with weight.
               const uint64_t any = __ballot(last_pos >= 0);
               const int src = 63 - __builtin_clzll(any);
               o = __shfl(last_pos, src);
-              const float bf = __shfl(last_before, src);
-              const float sf = __shfl(last_w, src);
-              tl = (t - bf) / sf;
+              tl = (t - __shfl(last_before, src)) / __shfl(last_w, src);
             }
             if (!(tl >= 0.0f)) tl = 0.0f;
             dec = ((uint64_t)(uint32_t)(o + 1) << 32) | __float_as_uint(tl);
           }
           if (lane == 0) st_agent(L.dec + (size_t)i * rows + b, dec);
         }
-        // H3: every workgroup reads every row's decision.
-        for (int b = wave; b < rows; b += kWaves) {
-          if (!s_active[b]) continue;
-          uint64_t d;
+        // H3: every workgroup reads every row's decision; wave w serves rows
+        // w + 8 j, lane j polls row w + 8 j, all at once.
+        {
+          const int b = wave + kWaves * lane;
+          const bool mine = lane < MARKOV_MAX_ROWS / kWaves && b < rows && s_active[b];
+          uint64_t d = 0;
           for (;;) {
-            d = ld_agent(L.dec + (size_t)i * rows + b);
-            if (d != 0) break;
+            if (mine && d == 0) d = ld_agent(L.dec + (size_t)i * rows + b);
+            if (__all(!mine || d != 0)) break;
             if (now_ticks() > deadline) {
-              if (lane == 0) {
-                s_abort = 1;
-                __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              }
-              d = 1ull << 63;
+              slot_wait_abort();
+              if (d == 0) d = 1ull << 63;
               break;
             }
             __builtin_amdgcn_s_sleep(1);
           }
-          if (lane == 0) {
+          if (mine) {
             if (d >> 63) {
               s_tok[b] = (int)(uint32_t)d;
               s_need[b] = 0;
@@ -1244,41 +1339,39 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           constexpr int PER = CHUNK / 64;  // ids per lane
           const int v0 = o * CHUNK + lane * PER;
           const uint16_t* crow = p.cache + (long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss;
+          // PER (8 or 4) cache values per lane in one vector load; V is a
+          // multiple of 16, so a lane's ids are all valid or all not.
+          static_assert(PER == 8 || PER == 4, "owner slice");
+          uint32_t cw[PER / 2];
+          if (v0 < V) {
+            if constexpr (PER == 8) {
+              const uint4 t4 = *reinterpret_cast<const uint4*>(crow + v0);
+              cw[0] = t4.x, cw[1] = t4.y, cw[2] = t4.z, cw[3] = t4.w;
+            } else {
+              const uint2 t2 = *reinterpret_cast<const uint2*>(crow + v0);
+              cw[0] = t2.x, cw[1] = t2.y;
+            }
+          }
           float z[PER];
           float m = -INFINITY;
-  #pragma unroll
+#pragma unroll
           for (int k = 0; k < PER; ++k) {
-            const int v = v0 + k;
-            z[k] = v < V ? __fdiv_rn(bf16_to_f32(crow[v]), T) : -INFINITY;
+            const uint32_t w = cw[k / 2];
+            const float c = __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            z[k] = v0 < V ? (T != 1.0f ? __fdiv_rn(c, T) : c) : -INFINITY;
             m = fmaxf(m, z[k]);
           }
-          // chunk maximum
-          {
-            float mm = m;
-            mm = fmaxf(mm, xshf<1>(mm));
-            mm = fmaxf(mm, xshf<2>(mm));
-            mm = fmaxf(mm, xshf<4>(mm));
-            mm = fmaxf(mm, xshf<8>(mm));
-            mm = fmaxf(mm, xshf<16>(mm));
-            mm = fmaxf(mm, xshf<32>(mm));
-            m = mm;
-          }
+          m = order_key_inv(wave_imax(order_key(m)));  // chunk maximum (no NaN: the decision excludes it)
           float w[PER];
           float lsum = 0.0f;
-  #pragma unroll
+#pragma unroll
           for (int k = 0; k < PER; ++k) {
             w[k] = (v0 + k < V && z[k] > -INFINITY) ? expf(z[k] - m) : 0.0f;
             lsum += w[k];
           }
-          float incl = lsum;
-  #pragma unroll
-          for (int dd = 1; dd < 64; dd <<= 1) {
-            const float ov = __shfl_up(incl, dd);
-            if (lane >= dd) incl += ov;
-          }
-          float run = incl - lsum;
+          float run = wave_incl_scan(lsum) - lsum;
           int found = -1, lastv = -1;
-  #pragma unroll
+#pragma unroll
           for (int k = 0; k < PER; ++k) {
             if (found < 0 && w[k] > 0.0f && run + w[k] > tl) found = v0 + k;
             if (w[k] > 0.0f) lastv = v0 + k;
@@ -1297,24 +1390,22 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             st_agent(L.tok + (size_t)i * rows + b, (1ull << 63) | (uint32_t)tok);
           }
         }
-        // H4: rows whose chunk another workgroup owns.
-        for (int b = wave; b < rows; b += kWaves) {
-          if (!s_active[b] || s_need[b] != 1) continue;
-          uint64_t d;
+        // H4: rows whose chunk another workgroup owns, polled all at once.
+        {
+          const int b = wave + kWaves * lane;
+          const bool mine = lane < MARKOV_MAX_ROWS / kWaves && b < rows && s_active[b] && s_need[b] == 1;
+          uint64_t d = 0;
           for (;;) {
-            d = ld_agent(L.tok + (size_t)i * rows + b);
-            if (d != 0) break;
+            if (mine && d == 0) d = ld_agent(L.tok + (size_t)i * rows + b);
+            if (__all(!mine || d != 0)) break;
             if (now_ticks() > deadline) {
-              if (lane == 0) {
-                s_abort = 1;
-                __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              }
-              d = 1ull << 63;
+              slot_wait_abort();
+              if (d == 0) d = 1ull << 63;
               break;
             }
             __builtin_amdgcn_s_sleep(1);
           }
-          if (lane == 0) s_tok[b] = (int)(uint32_t)d;
+          if (mine) s_tok[b] = (int)(uint32_t)d;
         }
       }
       __syncthreads();
@@ -1409,7 +1500,8 @@ const void* kernel_for(int rank, int mode, int kind) {
 }
 
 // Dynamic LDS above the default per-launch limit is opted into once per
-// process for every chain kernel (the embeddings take up to 64 KiB).
+// process for every chain kernel (the embeddings of MARKOV_MAX_ROWS rows:
+// 33 KiB at r = 256, 65 KiB at r = 512).
 int prepare_kernels() {
   static std::once_flag once;
   static hipError_t err = hipSuccess;
@@ -1419,7 +1511,7 @@ int prepare_kernels() {
         for (int kind = 0; kind < 4; ++kind) {
           hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, kind),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             MARKOV_MAX_ROWS * (512 / 8 + 1) * 16);
+                                             MARKOV_MAX_ROWS * (rank / 8 + 1) * 16);
           if (e != hipSuccess && err == hipSuccess) err = e;
         }
   });
