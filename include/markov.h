@@ -68,8 +68,7 @@ typedef enum {
  * workspace serves one call at a time: calls that overlap in time (e.g. on
  * two streams) must use different workspaces.  A workspace may serve
  * several call shapes: size it as the largest markov_workspace_bytes of
- * those shapes (with at most 8 rows in mode 0 a slot takes 20 bytes, else 8,
- * so fewer rows can need more bytes).
+ * those shapes.
  */
 size_t markov_workspace_bytes(int rows, int steps, int vocab, int rank, int mode);
 

@@ -36,9 +36,10 @@
 //    all slots, so there is no contended atomic and no second flag.  A zero
 //    slot means "not arrived"; real keys are never zero.  Alternate calls use
 //    alternate halves of the workspace and each call clears the half the
-//    next call will use, so no reset launch is needed.  A single row
-//    overlaps the next step with the tail of the exchange (speculation on
-//    the best key seen once 7/8 of the slots have arrived).
+//    next call will use, so no reset launch is needed.  A single row on more
+//    than 64 workgroups exchanges in two levels (4 reducer workgroups, whose
+//    partials everyone polls).  While polling, each wave fetches the
+//    embedding of the best key seen so far.
 //  * Mode 1 (inverse CDF) publishes per-chunk (max key, sum of exp) partials;
 //    a leader workgroup per row locates the chunk holding u * S, the chunk's
 //    owner scans it in vocabulary order and publishes the token.
@@ -374,9 +375,8 @@ struct ChainParams {
 // most once per call, and 0 means "not written yet"):
 //   keys [N][rows][NC] u64     candidate keys (mode 0: one per workgroup,
 //                               mode 1: one per chunk)
-//   mode 0 with at most kAhead rows (speculative publication):
-//   fix  [N][rows][NC] u64     a key recomputed after a wrong guess
-//   tags [N][rows][NC] u32     1 + the previous token the key was computed for
+//   mode 0:
+//   part [N][rows][NR] u64     reducer r's maximum over slots 64 r .. 64 r + 63
 //   mode 1:
 //   dec  [N][rows]     u64     the leader's decision for the row
 //   tok  [N][rows]     u64     the owner's token for the row
@@ -384,34 +384,39 @@ struct ChainParams {
 // (64-bit arrays first, so that every array is aligned to its element size.)
 struct HalfLayout {
   uint64_t* keys;
-  uint64_t* fix;
-  uint32_t* tags;
+  uint64_t* part;
   uint64_t* dec;
   uint64_t* tok;
   uint32_t* sums;
 };
 
-__host__ __device__ inline bool speculative_rows(int rows, int mode) { return mode == 0 && rows <= kAhead; }
+// Reducer workgroups of the two-level mode-0 exchange (slots per reducer: 64).
+__host__ __device__ inline int reducers_for(int NC) { return (NC + 63) / 64; }
 
 __host__ __device__ inline size_t half_bytes_needed(int rows, int N, int NC, int mode) {
   const size_t slots = (size_t)N * rows * NC;
   size_t b = slots * 8;
-  if (mode == 1) b += (size_t)N * rows * 16 + slots * 4;
-  else if (speculative_rows(rows, mode)) b += slots * 12;
+  if (mode == 1) {
+    b += (size_t)N * rows * 16 + slots * 4;
+  } else {
+    b += (size_t)N * rows * reducers_for(NC) * 8;
+  }
   return (b + 255) & ~(size_t)255;
 }
 
 __device__ inline HalfLayout half_layout(unsigned char* half, int rows, int N, int NC, int mode) {
-  HalfLayout L;
+  HalfLayout L = {};
   const size_t slots = (size_t)N * rows * NC;
-  L.keys = reinterpret_cast<uint64_t*>(half);
-  L.fix = L.keys + slots;
-  L.tags = reinterpret_cast<uint32_t*>(L.fix + slots);
-  L.dec = L.keys + slots;
-  L.tok = L.dec + (size_t)N * rows;
-  L.sums = reinterpret_cast<uint32_t*>(L.tok + (size_t)N * rows);
-  if (!speculative_rows(rows, mode)) L.fix = nullptr, L.tags = nullptr;
-  if (mode != 1) L.dec = L.tok = nullptr, L.sums = nullptr;
+  uint64_t* cur = reinterpret_cast<uint64_t*>(half);
+  L.keys = cur;
+  cur += slots;
+  if (mode == 1) {
+    L.dec = cur;
+    L.tok = cur + (size_t)N * rows;
+    L.sums = reinterpret_cast<uint32_t*>(L.tok + (size_t)N * rows);
+  } else {
+    L.part = cur;
+  }
   return L;
 }
 
@@ -542,9 +547,8 @@ __device__ __forceinline__ float one_row_bias(const uint4 (&h)[kSlots], const ui
 // VGPRs for the whole launch.  !RES: workgroups stride over the chunks and
 // stream the head from memory at every step.  SMALL (with RES): at most
 // kAhead request rows, whose next-step inputs are prefetched in registers
-// (and, in mode 0, whose exchange is overlapped with the next step).  ONE
-// (with SMALL, mode 0): a single request row, whose bias and epilogue stay in
-// registers.
+// during the exchange.  ONE (with SMALL, mode 0): a single request row,
+// whose bias and epilogue stay in registers.
 template <int R, int MODE, bool RES, bool SMALL, bool ONE>
 __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   constexpr int RPG = 16384 / R;       // head rows per group
@@ -566,12 +570,6 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // the next step's base logits of every batch (inverse CDF, resident head, > kAhead rows)
   __shared__ uint32_t s_pre[(MODE == 1 && RES && !SMALL) ? kWaves * (MARKOV_MAX_ROWS / kBatch) * (RPG / 16) * 64 : 1];
   __shared__ int s_abort;
-  __shared__ int s_miss;
-  __shared__ int s_spec[kAhead];   // phase A's guess of the row's winner
-  __shared__ int s_done[kAhead];   // phase A already saw every slot valid
-  __shared__ int s_use[kAhead];    // the token whose embedding s_e holds
-  __shared__ int s_conf[kAhead];   // the last confirmed token of the row
-  __shared__ int s_rmiss[kAhead];  // the row's guess was wrong this step
   __shared__ uint32_t s_parity;
   extern __shared__ uint4 s_e[];  // [rows][ES] 16-byte vectors of the current embeddings
 
@@ -618,7 +616,6 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     s_T[b] = p.temp[b];
     if (MODE == 1) s_seed[b] = p.seeds[b];
     s_tok[b] = active ? (int)tok : 0;
-    if (b < kAhead) s_use[b] = s_conf[b] = s_tok[b];
   }
   __syncthreads();
   const uint32_t parity = s_parity & 1u;
@@ -924,143 +921,21 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     }
   };
 
-  // Speculation (mode 0, resident head, at most kAhead rows, so wave b
-  // serves row b).  Phase A of step i polls step i's slots until at least
-  // 7/8 are valid, takes the best key so far as the winner and puts its
-  // embedding in LDS; the local work of step i+1 runs on it at once and is
-  // published with a tag: 1 + the token whose embedding it used.  Phase B of
-  // step i then waits, while step i+1's keys travel, until every slot of
-  // step i is valid and confirms the winner.  A slot is valid when its tag
-  // names the confirmed previous token; otherwise the publisher guessed wrong
-  // and its fix slot (written once it found out) holds the recomputed key.
-  // On a wrong guess a workgroup reloads the embedding, redoes step i+1's
-  // local work (overwriting its cache stores) and writes the fix slots.
-  constexpr bool speculate = MODE == 0 && ahead && ONE;
-
   // Publication of the workgroup's best key per row (mode 0): row b by
-  // thread b, or with speculation by lane 0 of wave b (the wave that also
-  // runs the row's phases A and B, so its tag is read in program order).
+  // thread b.
   auto row_key = [&](int b) {
     uint64_t K = kNoCandidate;
     for (int w = 0; w < kWaves; ++w) K = umax64(K, s_key[w][b]);
     return K;
   };
   auto publish = [&](int i) {
-    if constexpr (speculate) {
-      const int b = wave;
-      if (lane == 0 && b < rows && s_active[b]) {
-        const size_t slot = ((size_t)i * rows + b) * NC + wg;
-        st_agent(L.keys + slot, row_key(b));
-        st_agent32(L.tags + slot, (uint32_t)s_use[b] + 1u);
-      }
-    } else {
-      for (int b = tid; b < rows; b += kThreads)
-        if (s_active[b]) st_agent(L.keys + ((size_t)i * rows + b) * NC + wg, row_key(b));
-    }
-  };
-  auto publish_fix = [&](int i) {
-    const int b = wave;
-    if (lane == 0 && b < rows && s_active[b] && s_rmiss[b])
-      st_agent(L.fix + ((size_t)i * rows + b) * NC + wg, row_key(b));
+    for (int b = tid; b < rows; b += kThreads)
+      if (s_active[b]) st_agent(L.keys + ((size_t)i * rows + b) * NC + wg, row_key(b));
   };
   auto slot_wait_abort = [&]() {
     if (lane == 0) {
       s_abort = 1;
       __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  };
-  // A slot judged against the row's confirmed previous token (want = 1 +
-  // that token): the key if its tag matches, else the fix slot; 0 while the
-  // slot is not valid yet.  Each word is written once per call, so a key
-  // and tag that are both nonzero are final.
-  auto valid_key = [&](size_t slot, uint32_t want) -> uint64_t {
-    const uint64_t k = ld_agent(L.keys + slot);
-    const uint32_t t = ld_agent32(L.tags + slot);
-    if (k == 0 || t == 0) return 0;
-    return t == want ? k : ld_agent(L.fix + slot);
-  };
-  auto load_embedding = [&](int b, uint32_t tok) {
-    if (lane < KSEG) s_e[b * ES + lane] = *reinterpret_cast<const uint4*>(p.embed + (size_t)tok * R + lane * 8);
-  };
-  auto phase_a = [&](int i) {
-    const int b = wave;
-    if (b >= rows || !s_active[b]) return;
-    const size_t slot0 = ((size_t)i * rows + b) * NC;
-    const uint32_t want = (uint32_t)s_conf[b] + 1u;
-    uint64_t best = kNoCandidate;
-    bool all = false;
-    for (;;) {
-      uint64_t mine = kNoCandidate;
-      int arrived = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int idx = lane + 64 * k;
-        const uint64_t x = idx < G ? valid_key(slot0 + idx, want) : 0;
-        mine = umax64(mine, x);
-        arrived += __popcll(__ballot(x != 0));
-      }
-      best = wave_max_u64(mine);
-      all = arrived == G;
-      if (all || 8 * arrived >= 7 * G) break;
-      if (now_ticks() > deadline) {
-        slot_wait_abort();
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    uint32_t spec = key_id(best);
-    if (spec >= (uint32_t)V) spec = 0;  // only if nothing arrived (timeout)
-    load_embedding(b, spec);
-    if (lane == 0) {
-      s_spec[b] = (int)spec;
-      s_use[b] = (int)spec;
-      s_done[b] = all;
-    }
-  };
-  // Phase B of step i; last: the final step (no phase A before it, no next
-  // embedding to correct).
-  auto phase_b = [&](int i, bool last) {
-    const int b = wave;
-    if (b >= rows || !s_active[b]) return;
-    const uint32_t spec = (uint32_t)s_spec[b];
-    uint32_t fin = spec;
-    if (last || !s_done[b]) {
-      const size_t slot0 = ((size_t)i * rows + b) * NC;
-      const uint32_t want = (uint32_t)s_conf[b] + 1u;
-      uint64_t best = kNoCandidate;
-      for (;;) {
-        bool all = true;
-        uint64_t mine = kNoCandidate;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int idx = lane + 64 * k;
-          if (idx < G) {
-            const uint64_t x = valid_key(slot0 + idx, want);
-            all = all && x != 0;
-            mine = umax64(mine, x);
-          }
-        }
-        best = wave_max_u64(mine);
-        if (__all(all)) break;
-        if (now_ticks() > deadline) {
-          slot_wait_abort();
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      fin = key_id(best);
-      if (fin >= (uint32_t)V) fin = 0;  // only after a timeout
-    }
-    const bool miss = !last && fin != spec;
-    if (miss) load_embedding(b, fin);
-    if (lane == 0) {
-      s_tok[b] = (int)fin;
-      s_conf[b] = (int)fin;
-      s_rmiss[b] = miss;
-      if (miss) {
-        s_use[b] = (int)fin;
-        s_miss = 1;
-      }
     }
   };
   auto write_tokens = [&](int i) {
@@ -1069,38 +944,9 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         if (s_active[b]) p.tokens[(long long)b * p.tok_rs + i] = s_tok[b];
   };
 
-  if constexpr (speculate) {
-    for (int i = 0; i < N; ++i) {
-      local_work(i);
-      if (tid == 0) s_miss = 0;
-      __syncthreads();
-      publish(i);
-      if (i > 0) {
-        phase_b(i - 1, false);
-        __syncthreads();
-        if (s_abort) break;
-        write_tokens(i - 1);
-        if (s_miss) {  // redo step i on the confirmed embeddings
-          local_work(i);
-          __syncthreads();
-          publish_fix(i);
-        }
-      }
-      if (i + 1 < N) {
-        prefetch(i + 1);
-        phase_a(i);
-        __syncthreads();
-        if (s_abort) break;
-      } else {
-        phase_b(i, true);
-        __syncthreads();
-        if (s_abort) break;
-        write_tokens(i);
-      }
-    }
-  } else {
-    // The step loop without speculation: local work, publication, then the
-    // whole exchange of the step.
+  {
+    // The step loop: local work, publication, then the exchange of the
+    // step (its tail overlaps the fetch of the next embedding).
     for (int i = 0; i < N; ++i) {
       local_work(i);
       if (MODE == 1 && ahead && i + 1 < N) prefetch(i + 1);
@@ -1125,21 +971,49 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // the next step's embedding is usually in flight before the exchange
         // ends.  The row goes straight into the LDS embedding buffer, which no
         // wave reads again in this step.
+        // A single row with more than 64 workgroups exchanges in two levels:
+        // reducer r (workgroup r < NR) waits for slots 64 r .. 64 r + 63 and
+        // publishes their maximum; every workgroup then polls the NR
+        // partials instead of all G slots, which keeps the polled lines few.
+        // (Measured: one row 43.7 -> 41.0 us per call; several rows, whose
+        // reducers each serve every row, were slower than all-to-all.)
+        const int NR = rows == 1 ? reducers_for(G) : 1;
+        const int NRS = reducers_for(NC);  // the part arrays' row stride
+        if (NR > 1 && wg < NR) {
+          for (int b = wave; b < rows; b += kWaves) {
+            if (!s_active[b]) continue;
+            const uint64_t* slots = L.keys + ((size_t)i * rows + b) * NC;
+            const int idx = wg * 64 + lane;
+            uint64_t x = idx < G ? 0 : kNoCandidate;
+            for (;;) {
+              if (x == 0) x = ld_agent(slots + idx);
+              if (__all(x != 0)) break;
+              if (now_ticks() > deadline) {
+                slot_wait_abort();
+                break;
+              }
+              __builtin_amdgcn_s_sleep(1);
+            }
+            const uint64_t K = wave_max_u64(x == 0 ? kNoCandidate : x);
+            if (lane == 0) st_agent(L.part + ((size_t)i * rows + b) * NRS + wg, K);
+          }
+        }
         for (int b = wave; b < rows; b += kWaves) {
           if (!s_active[b]) continue;
-          const uint64_t* slots = L.keys + ((size_t)i * rows + b) * NC;
+          const uint64_t* slots = NR > 1 ? L.part + ((size_t)i * rows + b) * NRS : L.keys + ((size_t)i * rows + b) * NC;
+          const int n = NR > 1 ? NR : G;  // words polled: partials or slots
           const bool next = i + 1 < N;
-              uint64_t best = kNoCandidate;
+          uint64_t best = kNoCandidate;
           uint32_t spec = 0xFFFFFFFFu;
           uint4 ev = make_uint4(0, 0, 0, 0);
           for (;;) {
             bool all = true;
             uint64_t mine = kNoCandidate;
-            for (int k0 = 0; k0 < G; k0 += 256) {  // 4 slots per lane per batch
-  #pragma unroll
+            for (int k0 = 0; k0 < n; k0 += 256) {  // 4 words per lane per batch
+#pragma unroll
               for (int k = 0; k < 4; ++k) {
                 const int idx = k0 + lane + 64 * k;
-                if (idx < G) {
+                if (idx < n) {
                   const uint64_t x = ld_agent(slots + idx);
                   all = all && (x != 0);
                   mine = umax64(mine, x);
@@ -1154,10 +1028,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
               if (lane < KSEG) ev = *reinterpret_cast<const uint4*>(p.embed + (size_t)cand * R + lane * 8);
             }
             if (now_ticks() > deadline) {
-              if (lane == 0) {
-                s_abort = 1;
-                __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              }
+              slot_wait_abort();
               break;
             }
             __builtin_amdgcn_s_sleep(1);

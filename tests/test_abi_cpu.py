@@ -30,20 +30,21 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_workspace_bytes():
-    # header + two halves; mode 0 with at most 8 rows: an 8-byte key, an
-    # 8-byte fix slot and a 4-byte tag per (step, row, chunk) (512-id chunks
-    # at r=256)
+    # header + two halves; mode 0: an 8-byte key per (step, row, chunk) and an
+    # 8-byte reducer partial per (step, row, 64 chunks) (512-id chunks at
+    # r=256)
     chunks = -(-129280 // 512)
-    half = -(-(8 * 1 * chunks * 20) // 256) * 256
+    red = -(-chunks // 64)
+    half = -(-(8 * 1 * chunks * 8 + 8 * 1 * red * 8) // 256) * 256
     assert lm.markov_workspace_bytes(1, 8, 129280, 256, 0) == 256 + 2 * half
-    # more rows: keys only
-    half9 = -(-(8 * 9 * chunks * 8) // 256) * 256
+    half9 = -(-(8 * 9 * chunks * 8 + 8 * 9 * red * 8) // 256) * 256
     assert lm.markov_workspace_bytes(9, 8, 129280, 256, 0) == 256 + 2 * half9
-    # mode 1 adds 4-byte sums and two 8-byte words per (step, row)
+    # mode 1 adds 4-byte sums and two 8-byte words per (step, row), no partials
     half1 = -(-(8 * 64 * chunks * 12 + 8 * 64 * 16) // 256) * 256
     assert lm.markov_workspace_bytes(64, 8, 129280, 256, 1) == 256 + 2 * half1
     # r=512 chunks hold 256 ids
-    half5 = -(-(16 * 8 * (262144 // 256) * 20) // 256) * 256
+    c5 = 262144 // 256
+    half5 = -(-(16 * 8 * c5 * 8 + 16 * 8 * (c5 // 64) * 8) // 256) * 256
     assert lm.markov_workspace_bytes(8, 16, 262144, 512, 0) == 256 + 2 * half5
 
 
