@@ -97,6 +97,80 @@ def cpu_baseline(w, budget_s: float) -> dict:
                       f"{el:.1f} s, single thread on {os.cpu_count()} online cores)"}
 
 
+def draft_step_figures(w, hidden: int, dev, reps: int = 50) -> dict:
+    """The pages' deployment shape around the chain, as context: a stand-in
+    draft LM head (base logits = hidden states @ W with random bf16 weights
+    [hidden, V]) runs on the current stream while the noise runs on a side
+    stream, then the chain; eager and captured as one HIP graph.  The LM
+    head is not part of the hot path and not part of `value`."""
+    import torch
+
+    from markov_bias_chain_amd import binding
+    from markov_bias_chain_amd.device import DeviceChain
+
+    d = DeviceChain(w, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0x4D41524B)
+    weight = torch.empty(hidden, w.V, dtype=torch.bfloat16, device=dev)
+    for k in range(0, hidden, 512):  # fp32 draws in slices, cast to bf16
+        weight[k:k + 512] = (torch.randn(min(512, hidden - k), w.V, device=dev, generator=gen) * 0.02)
+    hs = torch.randn(w.rows * w.N, hidden, device=dev, generator=gen).to(torch.bfloat16)
+    base2d = d.base.view(w.rows * w.N, w.V)
+
+    def lm_head():
+        torch.matmul(hs, weight, out=base2d)
+
+    def step():
+        cur = torch.cuda.current_stream(dev)
+        if w.mode == 0:
+            d.side.wait_stream(cur)
+            d.noise(stream=d.side)
+        lm_head()
+        if w.mode == 0:
+            cur.wait_stream(d.side)
+        d.chain(stream=cur)
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize(dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) / reps * 1e3
+
+    lm_us = timed(lm_head)
+    chain_us = timed(lambda: d.chain())
+    noise_us = timed(lambda: d.noise()) if w.mode == 0 else 0.0
+    eager_us = timed(step)
+    binding.markov_status(d.workspace)
+    step()
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    # one replay against an eager step on the same inputs
+    g.replay()
+    binding.markov_status(d.workspace)
+    t_g, c_g = d.results()
+    step()
+    binding.markov_status(d.workspace)
+    t_e, c_e = d.results()
+    same = bool((t_g == t_e).all() and (c_g == c_e).all())
+    graph_us = timed(g.replay)
+    binding.markov_status(d.workspace)
+    del g, d, weight, hs
+    torch.cuda.empty_cache()
+    return {"lm_head_stand_in": f"[{w.rows * w.N}, {hidden}] @ [{hidden}, {w.V}] bf16 (torch.matmul)",
+            "lm_head_us": lm_us, "noise_us": noise_us, "chain_us": chain_us,
+            "eager_step_us": eager_us, "graph_step_us": graph_us,
+            "noise_hidden_us": lm_us + noise_us + chain_us - eager_us,
+            "graph_replay_matches_eager": same}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,7 +180,9 @@ def main() -> int:
     ap.add_argument("--cold", type=int, default=50, help="cold calls timed after the main loop")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the 8-row figures")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 8-row and draft-step figures")
+    ap.add_argument("--lm-hidden", type=int, default=7168,
+                    help="hidden size of the stand-in draft LM head of the draft-step figures (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 256 MiB device-to-device copy (a known-size kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -236,6 +312,8 @@ def main() -> int:
                            "chain_us_cold_median": statistics.median(k8) * 1e3,
                            "draft_tokens_per_s": w8.real_rows * w8.N / (us8 * 1e-6),
                            "head_GBps_warm": algorithmic_bytes(w8)["head"] / (us8 * 1e-6) / 1e9}
+    if not args.no_extra and args.lm_hidden > 0:
+        result["draft_step"] = draft_step_figures(w, args.lm_hidden, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

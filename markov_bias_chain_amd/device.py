@@ -68,6 +68,21 @@ class DeviceChain:
             cur.wait_stream(self.side)
         self.chain(stream=cur)
 
+    def capture_step(self) -> torch.cuda.CUDAGraph:
+        """A HIP graph of one step(): the noise fork on the side stream, the
+        join and the chain, replayable with g.replay() on fixed buffers (the
+        workspace needs no reset between calls, and no memset is recorded).
+        One eager step runs first so that every one-time set-up (kernel
+        attributes, library loading) happens outside the capture."""
+        self.step()
+        torch.cuda.synchronize(self.device)
+        lm.markov_status(self.workspace)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize(self.device)
+        return g
+
     def results(self):
         """(tokens int64 [rows, N], cache uint16 [states, N, V]) on the host."""
         torch.cuda.synchronize(self.device)
