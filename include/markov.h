@@ -44,6 +44,12 @@ typedef enum {
 #define MARKOV_MODE_GUMBEL 0 /* max of logit / T + gumbel (sharded_markov page) */
 #define MARKOV_MODE_INVCDF 1 /* inverse CDF of softmax(logit / T) (fused_markov page) */
 
+/* Element types, OR-ed into `mode` (sharded_markov page, _kernel and
+ * unsupported_reason: base logits and the draft-logits cache are each bf16 or
+ * fp32).  Without a flag the tensor is bf16. */
+#define MARKOV_BASE_F32 0x10  /* base_logits are fp32 */
+#define MARKOV_CACHE_F32 0x20 /* the cache is fp32: cache_round keeps x unrounded */
+
 /* Limits of this build. */
 #define MARKOV_MAX_ROWS 64
 #define MARKOV_MAX_STEPS 256
@@ -105,7 +111,8 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
  *   x[v]     = f32(base[b][i][v]) + f32(bias[v])
  *   x[v]     = x[v] * output_multiplier;
  *              if soft_cap > 0: x[v] = tanhf(x[v] * (1 / soft_cap)) * soft_cap
- *   cache[s][i][v] = c[v] = bf16(x[v])                      (round to nearest even)
+ *   cache[s][i][v] = c[v] = bf16(x[v])  (round to nearest even; c = x with
+ *            MARKOV_CACHE_F32)
  *   MARKOV_MODE_GUMBEL: score[v] = f32(c[v]) / T[b] + gumbel[b][i][v] if
  *            T[b] > 0, else f32(c[v]); the token is the lowest v whose score
  *            is NaN if any, else the lowest v of the maximum score.
@@ -118,7 +125,8 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
  * Rows with state_idx[b] < 0 are padding: nothing of theirs is read or
  * written (muse_spark/sharded_markov pages: padding rows are inert).
  *
- *   base_logits     device, bf16 [rows][steps][>= vocab] with row stride
+ *   base_logits     device, bf16 (fp32 with MARKOV_BASE_F32)
+ *                   [rows][steps][>= vocab] with row stride
  *                   base_row_stride and step stride base_step_stride
  *                   (elements, multiples of 8), 16-byte aligned, read.
  *   head, embed     device, bf16 [>= vocab][rank], contiguous, 16-byte
@@ -139,10 +147,12 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
  *   soft_cap        fp32 soft cap (0: none); finite, >= 0.
  *   rows in [1, MARKOV_MAX_ROWS]; steps in [1, MARKOV_MAX_STEPS]; vocab a
  *   positive multiple of 16 up to MARKOV_MAX_VOCAB; rank 256 or 512;
- *   mode MARKOV_MODE_GUMBEL or MARKOV_MODE_INVCDF.
+ *   mode MARKOV_MODE_GUMBEL or MARKOV_MODE_INVCDF, with the element-type
+ *   flags above (markov_workspace_bytes and markov_grid ignore them).
  *   draft_tokens    device, int64 [rows][>= steps], row stride
  *                   tokens_row_stride, written for non-padding rows.
- *   cache           device, bf16 [cache_states][steps][>= vocab] with state
+ *   cache           device, bf16 (fp32 with MARKOV_CACHE_F32)
+ *                   [cache_states][steps][>= vocab] with state
  *                   stride cache_state_stride and step stride
  *                   cache_step_stride (multiples of 8), 16-byte aligned,
  *                   written at cache[state_idx[b]][i][0 .. vocab).  A state
@@ -157,7 +167,7 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
  * (e.g. the grid cannot be co-resident).  Device-side conditions (bad anchor
  * token, a wait that timed out) are reported by markov_status.
  */
-int markov_chain_sample(const uint16_t* base_logits, int64_t base_row_stride,
+int markov_chain_sample(const void* base_logits, int64_t base_row_stride,
                         int64_t base_step_stride, const uint16_t* head,
                         const uint16_t* embed, const int64_t* prev_tokens,
                         const float* temperature, const int64_t* seeds,
@@ -165,7 +175,7 @@ int markov_chain_sample(const uint16_t* base_logits, int64_t base_row_stride,
                         float output_multiplier, float soft_cap, int rows,
                         int steps, int vocab, int rank, int mode,
                         int64_t* draft_tokens, int64_t tokens_row_stride,
-                        uint16_t* cache, int64_t cache_states,
+                        void* cache, int64_t cache_states,
                         int64_t cache_state_stride, int64_t cache_step_stride,
                         void* workspace,
                         size_t workspace_bytes, void* stream);

@@ -25,6 +25,8 @@ MARKOV_E_HIP = -3
 MARKOV_E_DEVICE = -4
 MARKOV_MODE_GUMBEL = 0
 MARKOV_MODE_INVCDF = 1
+MARKOV_BASE_F32 = 0x10
+MARKOV_CACHE_F32 = 0x20
 MARKOV_MAX_ROWS = 64
 MARKOV_MAX_STEPS = 256
 
@@ -101,8 +103,9 @@ def _stream(stream) -> ctypes.c_void_p:
 def _need(t, dtype, name, device=None, contiguous=False):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in allowed:
+        raise TypeError(f"{name} must be {' or '.join(map(str, allowed))}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU")
     if device is not None and t.device != device:
@@ -146,15 +149,17 @@ def markov_chain_sample(base_logits: torch.Tensor, head: torch.Tensor, embed: to
                         output_multiplier: float = 1.0, soft_cap: float = 0.0,
                         mode: int = MARKOV_MODE_GUMBEL, stream=None) -> None:
     """Run the whole chain: draft_tokens[rows, >=N] (int64) and
-    cache[states, N, >=V] (bf16) are written in place."""
+    cache[states, N, >=V] (bf16 or fp32) are written in place.  base_logits
+    are bf16 or fp32; the element types are passed to the library as flags
+    of `mode`."""
     dev = base_logits.device
-    _need(base_logits, torch.bfloat16, "base_logits", dev)
+    _need(base_logits, (torch.bfloat16, torch.float32), "base_logits", dev)
     _need(head, torch.bfloat16, "head", dev, contiguous=True)
     _need(embed, torch.bfloat16, "embed", dev, contiguous=True)
     _need(prev_tokens, torch.int64, "prev_tokens", dev, contiguous=True)
     _need(temperature, torch.float32, "temperature", dev, contiguous=True)
     _need(draft_tokens, torch.int64, "draft_tokens", dev)
-    _need(cache, torch.bfloat16, "cache", dev)
+    _need(cache, (torch.bfloat16, torch.float32), "cache", dev)
     _need(workspace, torch.uint8, "workspace", dev, contiguous=True)
     if base_logits.dim() != 3 or base_logits.stride(2) != 1:
         raise ValueError("base_logits must be [rows, N, V] with unit last stride")
@@ -187,7 +192,9 @@ def markov_chain_sample(base_logits: torch.Tensor, head: torch.Tensor, embed: to
         _ptr(base_logits), base_logits.stride(0), base_logits.stride(1),
         _ptr(head), _ptr(embed), _ptr(prev_tokens), _ptr(temperature), _ptr(seeds),
         _ptr(gumbel), _ptr(state_idx), float(output_multiplier), float(soft_cap),
-        rows, steps, vocab, rank, int(mode),
+        rows, steps, vocab, rank,
+        int(mode) | (MARKOV_BASE_F32 if base_logits.dtype == torch.float32 else 0)
+        | (MARKOV_CACHE_F32 if cache.dtype == torch.float32 else 0),
         _ptr(draft_tokens), draft_tokens.stride(0),
         _ptr(cache), cache.shape[0], cache.stride(0), cache.stride(1),
         _ptr(workspace), workspace.numel(), _stream(stream)))

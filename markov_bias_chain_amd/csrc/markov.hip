@@ -69,6 +69,7 @@ constexpr int kBatch = 8;                  // request rows per epilogue batch
 constexpr int kLanesPerRow = 8;            // lanes per request row in a batch
 static_assert(kAhead == kBatch, "prefetched rows form one epilogue batch");
 constexpr int kHeader = 256;               // workspace header bytes
+constexpr int kDtypeFlags = MARKOV_BASE_F32 | MARKOV_CACHE_F32;  // dtype bits of `mode`
 constexpr int kMaxPollPerLane = 16;        // slots one lane polls (<= 1024 per row)
 constexpr int kLeaderRegs = 4;             // inverse-CDF chunks per lane kept in registers by a leader
 constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(256) void noise_fill_kernel(float* __restrict__ gum
 // ============================================================ chain kernel ==
 
 struct ChainParams {
-  const uint16_t* base;
+  const void* base;  // bf16 bits, or fp32 when base_f32
   long long base_rs, base_ss;
   const uint16_t* head;
   const uint16_t* embed;
@@ -364,8 +365,9 @@ struct ChainParams {
   int rows, N, V, NG, NC, G;
   int64_t* tokens;
   long long tok_rs;
-  uint16_t* cache;
+  void* cache;  // bf16 bits, or fp32 when cache_f32
   long long cache_rs, cache_ss;
+  int base_f32, cache_f32;
   long long cache_states;
   unsigned char* ws;
   unsigned long long ws_half;  // bytes per parity half
@@ -543,14 +545,19 @@ __device__ __forceinline__ float one_row_bias(const uint4 (&h)[kSlots], const ui
   }
 }
 
-// RES: every workgroup owns exactly one chunk (G == NC) and keeps its head in
+// DT: base logits or cache may be fp32 (the element-type flags are read);
+// without it both are bf16.  RES: every workgroup owns exactly one chunk
+// (G == NC) and keeps its head in
 // VGPRs for the whole launch.  !RES: workgroups stride over the chunks and
 // stream the head from memory at every step.  SMALL (with RES): at most
 // kAhead request rows, whose next-step inputs are prefetched in registers
 // during the exchange.  ONE (with SMALL, mode 0): a single request row,
 // whose bias and epilogue stay in registers.
-template <int R, int MODE, bool RES, bool SMALL, bool ONE>
+template <int R, int MODE, bool RES, bool SMALL, bool ONE, bool DT>
 __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
+  // Element types: only the DT variants read the flags (bf16 otherwise).
+  const bool base_f32 = DT && p.base_f32;
+  const bool cache_f32 = DT && p.cache_f32;
   constexpr int RPG = 16384 / R;       // head rows per group
   constexpr int CHUNK = kWaves * RPG;  // vocab ids per chunk
   constexpr int KSEG = R / 8;          // 16-byte segments per head row
@@ -649,7 +656,10 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     one_base = 0;
     one_noise = 0.0f;
     if (s_active[0] && own_res) {
-      one_base = p.base[(long long)i * p.base_ss + v_res];
+      // the base logit as fp32 bits (a bf16 value widened)
+      const long long at = (long long)i * p.base_ss + v_res;
+      one_base = base_f32 ? reinterpret_cast<const uint32_t*>(p.base)[at]
+                            : (uint32_t)reinterpret_cast<const uint16_t*>(p.base)[at] << 16;
       if (MODE == 0 && s_T[0] > 0.0f) one_noise = p.gumbel[(size_t)i * V + v_res];
     }
   };
@@ -663,12 +673,12 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   const int rr = lane >> 3;  // row of the batch
   const int q = lane & 7;    // vocab segment of the group
   struct LaneIn {
-    uint32_t bw[IPL / 2];  // base logits, two bf16 per word
-    float nz[IPL];         // noise
+    uint32_t bw[IPL];  // base logits: two bf16 per word (words 0 .. IPL/2 - 1), or IPL fp32
+    float nz[IPL];     // noise
   };
   auto load_rows = [&](int i, int b0, int g, LaneIn& in) {
 #pragma unroll
-    for (int e = 0; e < IPL / 2; ++e) in.bw[e] = 0;
+    for (int e = 0; e < IPL; ++e) in.bw[e] = 0;
 #pragma unroll
     for (int e = 0; e < IPL; ++e) in.nz[e] = 0.0f;
     int b = b0 + rr;
@@ -677,13 +687,23 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     asm volatile("" : "+v"(b));
     const int v0 = g * RPG + q * IPL;
     if (b < rows && g < NG && v0 < V && s_active[b]) {
-      const uint16_t* brow = p.base + ((long long)b * p.base_rs + (long long)i * p.base_ss) + v0;
-      if constexpr (IPL == 8) {
-        const uint4 t = *reinterpret_cast<const uint4*>(brow);
-        in.bw[0] = t.x, in.bw[1] = t.y, in.bw[2] = t.z, in.bw[3] = t.w;
+      const long long at = (long long)b * p.base_rs + (long long)i * p.base_ss + v0;
+      if (base_f32) {
+        const uint4* brow = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.base) + at);
+#pragma unroll
+        for (int e4 = 0; e4 < IPL / 4; ++e4) {
+          const uint4 t = brow[e4];
+          in.bw[4 * e4] = t.x, in.bw[4 * e4 + 1] = t.y, in.bw[4 * e4 + 2] = t.z, in.bw[4 * e4 + 3] = t.w;
+        }
       } else {
-        const uint2 t = *reinterpret_cast<const uint2*>(brow);
-        in.bw[0] = t.x, in.bw[1] = t.y;
+        const uint16_t* brow = reinterpret_cast<const uint16_t*>(p.base) + at;
+        if constexpr (IPL == 8) {
+          const uint4 t = *reinterpret_cast<const uint4*>(brow);
+          in.bw[0] = t.x, in.bw[1] = t.y, in.bw[2] = t.z, in.bw[3] = t.w;
+        } else {
+          const uint2 t = *reinterpret_cast<const uint2*>(brow);
+          in.bw[0] = t.x, in.bw[1] = t.y;
+        }
       }
       if (MODE == 0 && s_T[b] > 0.0f) {
         const float4* grow = reinterpret_cast<const float4*>(p.gumbel + ((size_t)b * N + i) * (size_t)V + v0);
@@ -707,12 +727,29 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // work reads no global memory.
   constexpr bool stage = MODE == 1 && RES && !SMALL;
   constexpr int kStageBatches = MARKOV_MAX_ROWS / kBatch;
-  LaneIn pst[stage ? kStageBatches : 1];
+  uint32_t pst[stage ? kStageBatches : 1][IPL / 2];  // bf16 pairs of every batch
   auto stage_load = [&](int i) {
     const int nbat = (rows + kBatch - 1) / kBatch;
+    const int g = wg * kWaves + wave;
+    const int v0 = g * RPG + q * IPL;
 #pragma unroll
-    for (int t = 0; t < (stage ? kStageBatches : 1); ++t)
-      if (t < nbat) load_rows(i, t * kBatch, wg * kWaves + wave, pst[t]);
+    for (int t = 0; t < (stage ? kStageBatches : 1); ++t) {
+#pragma unroll
+      for (int e = 0; e < IPL / 2; ++e) pst[t][e] = 0;
+      int b = t * kBatch + rr;
+      asm volatile("" : "+v"(b));  // keeps the row addresses inside the step loop
+      if (t < nbat && b < rows && g < NG && v0 < V && s_active[b]) {
+        const uint16_t* brow = reinterpret_cast<const uint16_t*>(p.base) +
+                               ((long long)b * p.base_rs + (long long)i * p.base_ss + v0);
+        if constexpr (IPL == 8) {
+          const uint4 w4 = *reinterpret_cast<const uint4*>(brow);
+          pst[t][0] = w4.x, pst[t][1] = w4.y, pst[t][2] = w4.z, pst[t][3] = w4.w;
+        } else {
+          const uint2 w2 = *reinterpret_cast<const uint2*>(brow);
+          pst[t][0] = w2.x, pst[t][1] = w2.y;
+        }
+      }
+    }
   };
   auto stage_park = [&]() {
     const int nbat = (rows + kBatch - 1) / kBatch;
@@ -720,7 +757,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     for (int t = 0; t < (stage ? kStageBatches : 1); ++t)
       if (t < nbat) {
 #pragma unroll
-        for (int e = 0; e < IPL / 2; ++e) s_pre[((wave * kStageBatches + t) * (IPL / 2) + e) * 64 + lane] = pst[t].bw[e];
+        for (int e = 0; e < IPL / 2; ++e) s_pre[((wave * kStageBatches + t) * (IPL / 2) + e) * 64 + lane] = pst[t][e];
       }
   };
   auto stage_fetch = [&](int t, LaneIn& in) {
@@ -729,7 +766,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
 #pragma unroll
     for (int e = 0; e < IPL; ++e) in.nz[e] = 0.0f;
   };
-  if (stage) {
+  if (stage && !base_f32) {
     stage_load(0);
     stage_park();
   }
@@ -754,27 +791,39 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
 #pragma unroll
     for (int e = 0; e < IPL; ++e) {
       const uint32_t w = in.bw[e / 2];
-      const float base = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      const float base = base_f32 ? __uint_as_float(in.bw[e])
+                                    : __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
       x[e] = __fmul_rn(__fadd_rn(base, bf16_round(bsum[e])), p.mult);
     }
     if (p.has_cap) {
 #pragma unroll
       for (int e = 0; e < IPL; ++e) x[e] = __fmul_rn(tanhf(__fmul_rn(x[e], p.inv_cap)), p.cap);
     }
+    // The cache value: x rounded to bf16, or x itself in an fp32 cache.
     uint32_t cw[IPL / 2];
     float z[IPL];
 #pragma unroll
     for (int e = 0; e < IPL / 2; ++e) {
       cw[e] = f32x2_to_bf16x2(x[2 * e], x[2 * e + 1]);
-      z[2 * e] = __uint_as_float(cw[e] << 16);
-      z[2 * e + 1] = __uint_as_float(cw[e] & 0xFFFF0000u);
+      z[2 * e] = cache_f32 ? x[2 * e] : __uint_as_float(cw[e] << 16);
+      z[2 * e + 1] = cache_f32 ? x[2 * e + 1] : __uint_as_float(cw[e] & 0xFFFF0000u);
     }
     if (ok) {
-      uint16_t* crow = p.cache + ((long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss) + v0;
       // Streaming stores: the cache is not read again by this launch (but
       // for an inverse-CDF owner's one chunk).
-      if constexpr (IPL == 8) __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]}, reinterpret_cast<u32x4_t*>(crow));
-      else __builtin_nontemporal_store((u32x2_t){cw[0], cw[1]}, reinterpret_cast<u32x2_t*>(crow));
+      const long long at = (long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss + v0;
+      if (cache_f32) {
+        u32x4_t* crow = reinterpret_cast<u32x4_t*>(reinterpret_cast<float*>(p.cache) + at);
+#pragma unroll
+        for (int e4 = 0; e4 < IPL / 4; ++e4)
+          __builtin_nontemporal_store((u32x4_t){__float_as_uint(z[4 * e4]), __float_as_uint(z[4 * e4 + 1]),
+                                                __float_as_uint(z[4 * e4 + 2]), __float_as_uint(z[4 * e4 + 3])},
+                                      crow + e4);
+      } else {
+        uint16_t* crow = reinterpret_cast<uint16_t*>(p.cache) + at;
+        if constexpr (IPL == 8) __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]}, reinterpret_cast<u32x4_t*>(crow));
+        else __builtin_nontemporal_store((u32x2_t){cw[0], cw[1]}, reinterpret_cast<u32x2_t*>(crow));
+      }
     }
     // Scores: T <= 0 is argmax; c / 1 is exact.
     if (T > 0.0f && T != 1.0f) {
@@ -852,13 +901,19 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         uint32_t ord = 0;
         if (s_active[0] && own) {
           const float T = s_T[0];
-          float x = __fadd_rn(bf16_to_f32(one_base), bf16_round(bsum));
+          float x = __fadd_rn(__uint_as_float(one_base), bf16_round(bsum));
           x = __fmul_rn(x, p.mult);
           if (p.has_cap) x = __fmul_rn(tanhf(__fmul_rn(x, p.inv_cap)), p.cap);
-          const uint32_t cb = f32_to_bf16_hw(x);
-          uint16_t* crow = p.cache + ((long long)s_state[0] * p.cache_rs + (long long)i * p.cache_ss);
-          crow[(unsigned)v] = (uint16_t)cb;
-          float z = bf16_to_f32(cb);
+          const long long at = (long long)s_state[0] * p.cache_rs + (long long)i * p.cache_ss + v;
+          float z;
+          if (cache_f32) {
+            reinterpret_cast<float*>(p.cache)[at] = x;
+            z = x;
+          } else {
+            const uint32_t cb = f32_to_bf16_hw(x);
+            reinterpret_cast<uint16_t*>(p.cache)[at] = (uint16_t)cb;
+            z = bf16_to_f32(cb);
+          }
           if (T > 0.0f) {
             if (T != 1.0f) z = __fdiv_rn(z, T);  // c / 1 is exact
             z = __fadd_rn(z, one_noise);
@@ -877,7 +932,9 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       // before the current batch's epilogue.
       static_assert(kRowPass == 2 * kBatch, "a pass is two batches");
       const int nbat = (rows + kBatch - 1) / kBatch;
-      if constexpr (!ahead && !stage) load_rows(i, 0, g, cur);
+      // (staged base logits hold bf16 only; fp32 ones are loaded per batch)
+      const bool staged = stage && !base_f32;
+      if (!ahead && !staged) load_rows(i, 0, g, cur);
       for (int t = 0; t < nbat; ++t) {
         const int b0 = t * kBatch;
         if ((t & 1) == 0) {
@@ -887,7 +944,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         const int nb = rows - b0 < kBatch ? rows - b0 : kBatch;
         if constexpr (ahead) {
           epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, pre);
-        } else if constexpr (stage) {
+        } else if (staged) {
           stage_fetch(t, cur);
           epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur);
         } else {
@@ -950,7 +1007,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     for (int i = 0; i < N; ++i) {
       local_work(i);
       if (MODE == 1 && ahead && i + 1 < N) prefetch(i + 1);
-      if (stage && i + 1 < N) {
+      if (stage && !base_f32 && i + 1 < N) {
         // Parked at once: the wait for the loads overlaps the wait for the
         // other workgroups' partials.
         stage_load(i + 1);
@@ -1209,26 +1266,38 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           const float T = s_T[b];
           constexpr int PER = CHUNK / 64;  // ids per lane
           const int v0 = o * CHUNK + lane * PER;
-          const uint16_t* crow = p.cache + (long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss;
-          // PER (8 or 4) cache values per lane in one vector load; V is a
+          const long long at = (long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss + v0;
+          // PER (8 or 4) cache values per lane in vector loads; V is a
           // multiple of 16, so a lane's ids are all valid or all not.
           static_assert(PER == 8 || PER == 4, "owner slice");
-          uint32_t cw[PER / 2];
+          uint32_t cw[PER];  // fp32 bits of the cache values
           if (v0 < V) {
-            if constexpr (PER == 8) {
-              const uint4 t4 = *reinterpret_cast<const uint4*>(crow + v0);
-              cw[0] = t4.x, cw[1] = t4.y, cw[2] = t4.z, cw[3] = t4.w;
+            if (cache_f32) {
+              const uint4* crow = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.cache) + at);
+#pragma unroll
+              for (int k4 = 0; k4 < PER / 4; ++k4) {
+                const uint4 t4 = crow[k4];
+                cw[4 * k4] = t4.x, cw[4 * k4 + 1] = t4.y, cw[4 * k4 + 2] = t4.z, cw[4 * k4 + 3] = t4.w;
+              }
             } else {
-              const uint2 t2 = *reinterpret_cast<const uint2*>(crow + v0);
-              cw[0] = t2.x, cw[1] = t2.y;
+              const uint16_t* crow = reinterpret_cast<const uint16_t*>(p.cache) + at;
+              uint32_t pk[PER / 2];
+              if constexpr (PER == 8) {
+                const uint4 t4 = *reinterpret_cast<const uint4*>(crow);
+                pk[0] = t4.x, pk[1] = t4.y, pk[2] = t4.z, pk[3] = t4.w;
+              } else {
+                const uint2 t2 = *reinterpret_cast<const uint2*>(crow);
+                pk[0] = t2.x, pk[1] = t2.y;
+              }
+#pragma unroll
+              for (int k = 0; k < PER; ++k) cw[k] = (k & 1) ? (pk[k / 2] & 0xFFFF0000u) : (pk[k / 2] << 16);
             }
           }
           float z[PER];
           float m = -INFINITY;
 #pragma unroll
           for (int k = 0; k < PER; ++k) {
-            const uint32_t w = cw[k / 2];
-            const float c = __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            const float c = __uint_as_float(cw[k]);
             z[k] = v0 < V ? (T != 1.0f ? __fdiv_rn(c, T) : c) : -INFINITY;
             m = fmaxf(m, z[k]);
           }
@@ -1349,13 +1418,13 @@ int check_shape(int rows, int steps, int vocab, int rank, int mode, Shape* sh) {
 
 // Kernel kinds: 0 streamed head, 1 resident head, 2 resident with at most
 // kAhead rows, 3 resident with one row (mode 0).
-template <int R, int MODE>
+template <int R, int MODE, bool DT>
 const void* kernel_variant(int kind) {
   switch (kind) {
-    case 0: return (const void*)chain_kernel<R, MODE, false, false, false>;
-    case 1: return (const void*)chain_kernel<R, MODE, true, false, false>;
-    case 2: return (const void*)chain_kernel<R, MODE, true, true, false>;
-    default: return (const void*)chain_kernel<R, MODE, true, true, MODE == 0>;
+    case 0: return (const void*)chain_kernel<R, MODE, false, false, false, DT>;
+    case 1: return (const void*)chain_kernel<R, MODE, true, false, false, DT>;
+    case 2: return (const void*)chain_kernel<R, MODE, true, true, false, DT>;
+    default: return (const void*)chain_kernel<R, MODE, true, true, MODE == 0, DT>;
   }
 }
 
@@ -1365,9 +1434,15 @@ int kernel_kind(int rows, int mode, bool res) {
   return rows <= kAhead ? 2 : 1;
 }
 
-const void* kernel_for(int rank, int mode, int kind) {
-  if (rank == 256) return mode == 0 ? kernel_variant<256, 0>(kind) : kernel_variant<256, 1>(kind);
-  return mode == 0 ? kernel_variant<512, 0>(kind) : kernel_variant<512, 1>(kind);
+template <bool DT>
+const void* kernel_for_dt(int rank, int mode, int kind) {
+  if (rank == 256) return mode == 0 ? kernel_variant<256, 0, DT>(kind) : kernel_variant<256, 1, DT>(kind);
+  return mode == 0 ? kernel_variant<512, 0, DT>(kind) : kernel_variant<512, 1, DT>(kind);
+}
+
+// dt: base logits or cache fp32 (the kernels that read the element-type flags).
+const void* kernel_for(int rank, int mode, int kind, bool dt) {
+  return dt ? kernel_for_dt<true>(rank, mode, kind) : kernel_for_dt<false>(rank, mode, kind);
 }
 
 // Dynamic LDS above the default per-launch limit is opted into once per
@@ -1379,8 +1454,9 @@ int prepare_kernels() {
   std::call_once(once, [] {
     for (int rank : {256, 512})
       for (int mode : {0, 1})
-        for (int kind = 0; kind < 4; ++kind) {
-          hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, kind),
+        for (int kind = 0; kind < 4; ++kind)
+          for (bool dt : {false, true}) {
+          hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, kind, dt),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              MARKOV_MAX_ROWS * (rank / 8 + 1) * 16);
           if (e != hipSuccess && err == hipSuccess) err = e;
@@ -1407,7 +1483,7 @@ int pick_grid(int rows, int rank, int mode, const Shape& sh, int* grid, bool* re
   if (g > 64 * kMaxPollPerLane) g = 64 * kMaxPollPerLane;
   const bool resident = (g == sh.NC);
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel_for(rank, mode, kernel_kind(rows, mode, resident)),
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel_for(rank, mode, kernel_kind(rows, mode, resident), false),
                                                     kThreads, shmem);
   if (e != hipSuccess) return fail(MARKOV_E_HIP, "occupancy query: %s", hipGetErrorString(e));
   if (per_cu < 1) return fail(MARKOV_E_HIP, "the chain kernel does not fit on a compute unit");
@@ -1421,6 +1497,7 @@ int pick_grid(int rows, int rank, int mode, const Shape& sh, int* grid, bool* re
 extern "C" {
 
 size_t markov_workspace_bytes(int rows, int steps, int vocab, int rank, int mode) {
+  mode &= ~kDtypeFlags;
   Shape sh;
   if (check_shape(rows, steps, vocab, rank, mode, &sh) != MARKOV_OK) return 0;
   return kHeader + 2 * half_bytes_needed(rows, steps, sh.NC, mode);
@@ -1444,15 +1521,17 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps, 
   return MARKOV_OK;
 }
 
-int markov_chain_sample(const uint16_t* base_logits, int64_t base_row_stride, int64_t base_step_stride,
+int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_step_stride,
                         const uint16_t* head, const uint16_t* embed, const int64_t* prev_tokens,
                         const float* temperature, const int64_t* seeds, const float* gumbel,
                         const int64_t* state_idx, float output_multiplier, float soft_cap, int rows,
                         int steps, int vocab, int rank, int mode, int64_t* draft_tokens,
-                        int64_t tokens_row_stride, uint16_t* cache, int64_t cache_states,
+                        int64_t tokens_row_stride, void* cache, int64_t cache_states,
                         int64_t cache_state_stride, int64_t cache_step_stride, void* workspace,
                         size_t workspace_bytes, void* stream) {
   g_last_error.clear();
+  const int base_f32 = (mode & MARKOV_BASE_F32) != 0, cache_f32 = (mode & MARKOV_CACHE_F32) != 0;
+  mode &= ~kDtypeFlags;
   Shape sh;
   int rc = check_shape(rows, steps, vocab, rank, mode, &sh);
   if (rc != MARKOV_OK) return rc;
@@ -1487,6 +1566,7 @@ int markov_chain_sample(const uint16_t* base_logits, int64_t base_row_stride, in
 
   ChainParams p;
   p.base = base_logits;
+  p.base_f32 = base_f32;
   p.base_rs = base_row_stride;
   p.base_ss = base_step_stride;
   p.head = head;
@@ -1509,6 +1589,7 @@ int markov_chain_sample(const uint16_t* base_logits, int64_t base_row_stride, in
   p.tokens = draft_tokens;
   p.tok_rs = tokens_row_stride;
   p.cache = cache;
+  p.cache_f32 = cache_f32;
   p.cache_rs = cache_state_stride;
   p.cache_ss = cache_step_stride;
   p.cache_states = cache_states;
@@ -1517,7 +1598,7 @@ int markov_chain_sample(const uint16_t* base_logits, int64_t base_row_stride, in
 
   void* args[] = {&p};
   const size_t shmem = (size_t)rows * (rank / 8 + 1) * 16;
-  const void* kern = kernel_for(rank, mode, kernel_kind(rows, mode, res));
+  const void* kern = kernel_for(rank, mode, kernel_kind(rows, mode, res), base_f32 || cache_f32);
   rc = prepare_kernels();
   if (rc != MARKOV_OK) return rc;
   // A regular launch: the grid is at most one workgroup per CU and the
@@ -1555,6 +1636,7 @@ int markov_set_grid(int g) { return g_grid_override.exchange(g < 0 ? 0 : g); }
 
 int markov_grid(int rows, int steps, int vocab, int rank, int mode) {
   g_last_error.clear();
+  mode &= ~kDtypeFlags;
   Shape sh;
   int rc = check_shape(rows, steps, vocab, rank, mode, &sh);
   if (rc != MARKOV_OK) return rc;

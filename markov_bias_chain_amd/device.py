@@ -29,7 +29,8 @@ class DeviceChain:
         self.device = dev
         self.head = to_device_bf16(w.head, dev)
         self.embed = to_device_bf16(w.embed, dev)
-        self.base = to_device_bf16(w.base, dev)
+        self.base = (torch.from_numpy(np.ascontiguousarray(w.base)).to(dev) if w.base.dtype == np.float32
+                     else to_device_bf16(w.base, dev))
         self.prev = torch.from_numpy(w.prev).to(dev)
         self.seeds = torch.from_numpy(w.seeds).to(dev)
         self.temperature = torch.from_numpy(w.temperature).to(dev)
@@ -37,9 +38,12 @@ class DeviceChain:
         self.gumbel = torch.empty((w.rows, w.N, w.V), dtype=torch.float32, device=dev) \
             if w.mode == 0 else None
         self.tokens = torch.full((w.rows, w.N), token_fill, dtype=torch.int64, device=dev)
-        fill = cache_fill - 0x10000 if cache_fill >= 0x8000 else cache_fill  # as int16 bits
-        self.cache = torch.full((w.states, w.N, w.V), fill, dtype=torch.int16,
-                                device=dev).view(torch.bfloat16)
+        if w.cache_f32:
+            self.cache = torch.full((w.states, w.N, w.V), float("nan"), dtype=torch.float32, device=dev)
+        else:
+            fill = cache_fill - 0x10000 if cache_fill >= 0x8000 else cache_fill  # as int16 bits
+            self.cache = torch.full((w.states, w.N, w.V), fill, dtype=torch.int16,
+                                    device=dev).view(torch.bfloat16)
         self.workspace = lm.markov_workspace(w.rows, w.N, w.V, w.r, w.mode, device=dev)
         self.side = torch.cuda.Stream(dev)
 
@@ -84,6 +88,8 @@ class DeviceChain:
         return g
 
     def results(self):
-        """(tokens int64 [rows, N], cache uint16 [states, N, V]) on the host."""
+        """(tokens int64 [rows, N], cache [states, N, V]: uint16 bf16 bits, or
+        float32 values for an fp32 cache) on the host."""
         torch.cuda.synchronize(self.device)
-        return self.tokens.cpu().numpy(), bf16_bits(self.cache)
+        c = self.cache.cpu().numpy() if self.cache.dtype == torch.float32 else bf16_bits(self.cache)
+        return self.tokens.cpu().numpy(), c

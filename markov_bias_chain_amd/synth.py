@@ -42,7 +42,7 @@ class Workload:
     mode: int
     head: np.ndarray          # uint16 [V, r] bf16 bits
     embed: np.ndarray         # uint16 [V, r] bf16 bits
-    base: np.ndarray          # uint16 [rows, N, V] bf16 bits
+    base: np.ndarray          # uint16 [rows, N, V] bf16 bits, or float32 values
     prev: np.ndarray          # int64 [rows] anchor tokens
     seeds: np.ndarray         # int64 [rows]
     temperature: np.ndarray   # float32 [rows]
@@ -50,6 +50,7 @@ class Workload:
     mult: float = 1.0         # fp32 output multiplier (1 = none)
     cap: float = 0.0          # fp32 soft cap (0 = none)
     exact: bool = False       # integer-valued weights: fp32 sums are order-exact
+    cache_f32: bool = False   # an fp32 draft-logits cache (else bf16)
 
     @property
     def states(self) -> int:
@@ -90,9 +91,11 @@ def make(name: str, V: int, r: int, rows: int, N: int, *, seed: int,
          weights: str = "normal", weight_std: float = 0.02,
          base_std: float = 3.0, peaks: int = 0, peak_value: float = 12.0,
          temperature=1.0, state_idx=None, mult: float = 1.0, cap: float = 0.0,
-         mode: int = 0) -> Workload:
+         mode: int = 0, base_f32: bool = False, cache_f32: bool = False) -> Workload:
     """A generic workload.  weights: "normal" (N(0, weight_std)), "int"
-    (k * 2^-6 with k uniform in [-4, 4]) or "zero" (head = 0)."""
+    (k * 2^-6 with k uniform in [-4, 4]) or "zero" (head = 0).  base_f32
+    keeps the base logits as fp32 draws (else their bf16 rounding);
+    cache_f32 asks for an fp32 draft-logits cache."""
     r_head, r_embed, r_base, r_peak, r_prev, r_seed = _rngs(seed, 6)
     if weights == "int":
         head = to_bf16_bits(r_head.integers(-4, 5, size=(V, r)).astype(np.float32) * 2.0**-6)
@@ -103,17 +106,18 @@ def make(name: str, V: int, r: int, rows: int, N: int, *, seed: int,
     else:
         head = to_bf16_bits(_normal(r_head, (V, r), weight_std))
         embed = to_bf16_bits(_normal(r_embed, (V, r), weight_std))
+    base_f32_out = base_f32
     base_f32 = _normal(r_base, (rows, N, V), base_std)
     if peaks:
         _peaks(r_peak, base_f32, peaks, peak_value)
-    base = to_bf16_bits(base_f32)
+    base = base_f32 if base_f32_out else to_bf16_bits(base_f32)
     prev = r_prev.integers(0, V, size=rows, dtype=np.int64)
     seeds = _seeds(r_seed, rows)
     temp = np.broadcast_to(np.asarray(temperature, dtype=np.float32), (rows,)).copy()
     sidx = None if state_idx is None else np.asarray(state_idx, dtype=np.int64)
     return Workload(name, V, r, rows, N, mode, head, embed, base, prev, seeds,
                     temp, sidx, float(np.float32(mult)), float(np.float32(cap)),
-                    exact=(weights == "int"))
+                    exact=(weights == "int"), cache_f32=bool(cache_f32))
 
 
 # The five named workloads.  Each has its own master seed.

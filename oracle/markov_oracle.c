@@ -190,11 +190,17 @@ static int64_t orc_pick_max(const float* s, int V, double* diag) {
  *
  * gumbel may be NULL in mode 1 (unused).  bias_out (optional, [V]) receives
  * the bf16 bias for diagnostics.  Returns the token.
+ *
+ * Element types ([SM] DSparkShardedMarkovSampler and _kernel: base logits
+ * and the draft-logits cache are each bf16 or fp32; cache_round rounds to
+ * the cache's type): base is bf16 bits, or fp32 values when base_f32;
+ * cache is bf16 bits, or fp32 values when cache_f32, in which case the
+ * cache value is x itself.
  */
-int64_t orc_step(const uint16_t* base, const uint16_t* head,
-                 const uint16_t* embed, int V, int r, int64_t prev, float T,
-                 const float* gumbel, float u, float mult, float cap, int mode,
-                 uint16_t* cache, double* diag, uint16_t* bias_out) {
+int64_t orc_step_t(const void* base, int base_f32, const uint16_t* head,
+                   const uint16_t* embed, int V, int r, int64_t prev, float T,
+                   const float* gumbel, float u, float mult, float cap, int mode,
+                   void* cache, int cache_f32, double* diag, uint16_t* bias_out) {
   double* e = (double*)malloc(sizeof(double) * (size_t)r);
   float* s = (float*)malloc(sizeof(float) * (size_t)V);
   for (int k = 0; k < r; ++k)
@@ -208,12 +214,19 @@ int64_t orc_step(const uint16_t* base, const uint16_t* head,
     uint16_t bias_bits = orc_bf16_round(dot);
     if (bias_out) bias_out[v] = bias_bits; /* diagnostic copy of the bias */
     float bias = orc_bf16_to_f32(bias_bits);
-    float x = orc_bf16_to_f32(base[v]) + bias;
+    float b = base_f32 ? ((const float*)base)[v] : orc_bf16_to_f32(((const uint16_t*)base)[v]);
+    float x = b + bias;
     x = x * mult;
     if (cap > 0.0f) x = tanhf(x * inv_cap) * cap;
-    uint16_t c = orc_bf16_round((double)x);
-    cache[v] = c;
-    float cf = orc_bf16_to_f32(c);
+    float cf;
+    if (cache_f32) {
+      ((float*)cache)[v] = x;
+      cf = x;
+    } else {
+      uint16_t c = orc_bf16_round((double)x);
+      ((uint16_t*)cache)[v] = c;
+      cf = orc_bf16_to_f32(c);
+    }
     if (T > 0.0f) {
       s[v] = (mode == 0) ? cf / T + gumbel[v] : cf / T;
     } else {
@@ -281,6 +294,15 @@ int64_t orc_step(const uint16_t* base, const uint16_t* head,
   return win;
 }
 
+/* orc_step with bf16 base logits and a bf16 cache. */
+int64_t orc_step(const uint16_t* base, const uint16_t* head,
+                 const uint16_t* embed, int V, int r, int64_t prev, float T,
+                 const float* gumbel, float u, float mult, float cap, int mode,
+                 uint16_t* cache, double* diag, uint16_t* bias_out) {
+  return orc_step_t(base, 0, head, embed, V, r, prev, T, gumbel, u, mult, cap,
+                    mode, cache, 0, diag, bias_out);
+}
+
 /* ------------------------------------------------------------------------ */
 /* The chain: N positions in order, each draw the next position's previous   */
 /* token ([SM] module docstring, "winner p = draft_tokens[i]").              */
@@ -294,16 +316,18 @@ int64_t orc_step(const uint16_t* base, const uint16_t* head,
  * inert (no reads, no writes).  mult = 1 and cap = 0 mean no transform.
  * row_mask[rows] or NULL selects the rows to compute (the others are left
  * untouched), which lets a test sample rows of a large call.
- * tokens[row*N + i]; cache[state*cache_rs + i*cache_ss + v] (bf16).
+ * tokens[row*N + i]; cache[state*cache_rs + i*cache_ss + v].  base and
+ * cache are bf16 bits, or fp32 with base_f32 / cache_f32 (see orc_step_t).
  * Returns 0, or -1 if a computed row has a previous token outside [0, V).
  */
-int orc_chain(const uint16_t* base, int64_t base_rs, int64_t base_ss,
-              const uint16_t* head, const uint16_t* embed, int V, int r,
-              const int64_t* prev_tokens, const float* temperature,
-              const int64_t* seeds, const float* gumbel,
-              const int64_t* state_idx, float mult, float cap, int rows,
-              int N, int mode, const uint8_t* row_mask, int64_t* tokens,
-              uint16_t* cache, int64_t cache_rs, int64_t cache_ss) {
+int orc_chain_t(const void* base, int base_f32, int64_t base_rs, int64_t base_ss,
+                const uint16_t* head, const uint16_t* embed, int V, int r,
+                const int64_t* prev_tokens, const float* temperature,
+                const int64_t* seeds, const float* gumbel,
+                const int64_t* state_idx, float mult, float cap, int rows,
+                int N, int mode, const uint8_t* row_mask, int64_t* tokens,
+                void* cache, int cache_f32, int64_t cache_rs, int64_t cache_ss) {
+  const size_t bsz = base_f32 ? 4 : 2, csz = cache_f32 ? 4 : 2;
   float* g = (float*)malloc(sizeof(float) * (size_t)V);
   int status = 0;
   for (int row = 0; row < rows; ++row) {
@@ -327,12 +351,26 @@ int orc_chain(const uint16_t* base, int64_t base_rs, int64_t base_ss,
       } else {
         u = orc_uniform(orc_hash_step(seeds[row], row, i));
       }
-      p = orc_step(base + row * base_rs + i * base_ss, head, embed, V, r, p,
-                   temperature[row], gi, u, mult, cap, mode,
-                   cache + state * cache_rs + i * cache_ss, NULL, NULL);
+      p = orc_step_t((const char*)base + (size_t)(row * base_rs + i * base_ss) * bsz, base_f32,
+                     head, embed, V, r, p, temperature[row], gi, u, mult, cap, mode,
+                     (char*)cache + (size_t)(state * cache_rs + i * cache_ss) * csz, cache_f32,
+                     NULL, NULL);
       tokens[(size_t)row * N + i] = p;
     }
   }
   free(g);
   return status;
+}
+
+/* orc_chain with bf16 base logits and a bf16 cache. */
+int orc_chain(const uint16_t* base, int64_t base_rs, int64_t base_ss,
+              const uint16_t* head, const uint16_t* embed, int V, int r,
+              const int64_t* prev_tokens, const float* temperature,
+              const int64_t* seeds, const float* gumbel,
+              const int64_t* state_idx, float mult, float cap, int rows,
+              int N, int mode, const uint8_t* row_mask, int64_t* tokens,
+              uint16_t* cache, int64_t cache_rs, int64_t cache_ss) {
+  return orc_chain_t(base, 0, base_rs, base_ss, head, embed, V, r, prev_tokens,
+                     temperature, seeds, gumbel, state_idx, mult, cap, rows, N,
+                     mode, row_mask, tokens, cache, 0, cache_rs, cache_ss);
 }

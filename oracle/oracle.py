@@ -65,6 +65,19 @@ def _load():
                  ctypes.c_float, _f32p, ctypes.c_float, ctypes.c_float,
                  ctypes.c_float, ctypes.c_int, _u16p, _f64p, _u16p],
             ),
+            "orc_step_t": (
+                ctypes.c_int64,
+                [ctypes.c_void_p, ctypes.c_int, _u16p, _u16p, ctypes.c_int, ctypes.c_int,
+                 ctypes.c_int64, ctypes.c_float, _f32p, ctypes.c_float, ctypes.c_float,
+                 ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, _f64p, _u16p],
+            ),
+            "orc_chain_t": (
+                ctypes.c_int,
+                [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, _u16p, _u16p,
+                 ctypes.c_int, ctypes.c_int, _i64p, _f32p, _i64p, _f32p, _i64p, ctypes.c_float,
+                 ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, _u8p,
+                 _i64p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64],
+            ),
             "orc_chain": (
                 ctypes.c_int,
                 [_u16p, ctypes.c_int64, ctypes.c_int64, _u16p, _u16p, ctypes.c_int,
@@ -151,22 +164,34 @@ def noise_fill(seeds: np.ndarray, steps: int, vocab: int) -> np.ndarray:
     return out
 
 
+def _base_array(a):
+    """bf16 bits (uint16) stay as they are; float32 values select fp32 base
+    logits."""
+    a = np.asarray(a)
+    if a.dtype == np.float32:
+        return np.ascontiguousarray(a), 1
+    return _c(a, np.uint16), 0
+
+
 def step(base_row, head, embed, prev, temperature, gumbel_row=None, u=0.0,
-         mult=1.0, cap=0.0, mode=0, with_diag=False, with_bias=False):
-    """One position of one row: returns (token, cache_row[, diag][, bias])."""
-    base_row = _c(base_row, np.uint16)
+         mult=1.0, cap=0.0, mode=0, with_diag=False, with_bias=False, cache_f32=False):
+    """One position of one row: returns (token, cache_row[, diag][, bias]).
+    base_row is bf16 bits (uint16) or fp32 values; the cache row is bf16 bits,
+    or fp32 values with cache_f32."""
+    base_row, base_f32 = _base_array(base_row)
     head = _c(head, np.uint16)
     embed = _c(embed, np.uint16)
     V, r = head.shape
     assert base_row.shape == (V,) and embed.shape[1] == r
     g = None if gumbel_row is None else _c(gumbel_row, np.float32)
-    cache = np.empty(V, dtype=np.uint16)
+    cache = np.empty(V, dtype=np.float32 if cache_f32 else np.uint16)
     diag = np.zeros(DIAG, dtype=np.float64)
     bias = np.empty(V, dtype=np.uint16) if with_bias else None
-    tok = _load().orc_step(
-        _ptr(base_row, _u16p), _ptr(head, _u16p), _ptr(embed, _u16p), V, r,
+    tok = _load().orc_step_t(
+        base_row.ctypes.data, base_f32, _ptr(head, _u16p), _ptr(embed, _u16p), V, r,
         int(prev), float(temperature), _ptr(g, _f32p), float(u), float(mult),
-        float(cap), int(mode), _ptr(cache, _u16p), _ptr(diag, _f64p), _ptr(bias, _u16p))
+        float(cap), int(mode), cache.ctypes.data, int(bool(cache_f32)), _ptr(diag, _f64p),
+        _ptr(bias, _u16p))
     out = (int(tok), cache)
     if with_diag:
         out += (diag,)
@@ -177,11 +202,12 @@ def step(base_row, head, embed, prev, temperature, gumbel_row=None, u=0.0,
 
 def chain(base, head, embed, prev_tokens, temperature, seeds, gumbel=None,
           state_idx=None, mult=1.0, cap=0.0, mode=0, row_mask=None,
-          tokens=None, cache=None):
-    """The whole chain.  base [rows, N, V] bf16 bits; head/embed [V, r];
-    returns (tokens [rows, N] int64, cache [states, N, V] uint16).  Rows that
-    are masked out or inert keep what ``tokens``/``cache`` held."""
-    base = _c(base, np.uint16)
+          tokens=None, cache=None, cache_f32=False):
+    """The whole chain.  base [rows, N, V] bf16 bits (uint16) or fp32 values;
+    head/embed [V, r]; returns (tokens [rows, N] int64, cache [states, N, V]
+    uint16 bf16 bits, or float32 with cache_f32).  Rows that are masked out or
+    inert keep what ``tokens``/``cache`` held."""
+    base, base_f32 = _base_array(base)
     head = _c(head, np.uint16)
     embed = _c(embed, np.uint16)
     rows, N, V = base.shape
@@ -197,16 +223,17 @@ def chain(base, head, embed, prev_tokens, temperature, seeds, gumbel=None,
     states = rows if sidx is None else max(int(sidx.max()) + 1, 1)
     if tokens is None:
         tokens = np.full((rows, N), -7, dtype=np.int64)
+    cdt = np.float32 if cache_f32 else np.uint16
     if cache is None:
-        cache = np.zeros((states, N, V), dtype=np.uint16)
+        cache = np.zeros((states, N, V), dtype=cdt)
     assert tokens.flags.c_contiguous and tokens.dtype == np.int64
-    assert cache.flags.c_contiguous and cache.dtype == np.uint16
+    assert cache.flags.c_contiguous and cache.dtype == cdt
     mask = None if row_mask is None else _c(row_mask, np.uint8)
-    rc = _load().orc_chain(
-        _ptr(base, _u16p), N * V, V, _ptr(head, _u16p), _ptr(embed, _u16p), V, r,
+    rc = _load().orc_chain_t(
+        base.ctypes.data, base_f32, N * V, V, _ptr(head, _u16p), _ptr(embed, _u16p), V, r,
         _ptr(prev, _i64p), _ptr(temp, _f32p), _ptr(seeds, _i64p), _ptr(g, _f32p),
         _ptr(sidx, _i64p), float(mult), float(cap), rows, N, int(mode),
-        _ptr(mask, _u8p), _ptr(tokens, _i64p), _ptr(cache, _u16p),
+        _ptr(mask, _u8p), _ptr(tokens, _i64p), cache.ctypes.data, int(bool(cache_f32)),
         cache.shape[1] * cache.shape[2], cache.shape[2])
     if rc != 0:
         raise ValueError("oracle: a previous token outside [0, V)")

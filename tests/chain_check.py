@@ -88,6 +88,31 @@ def is_nan_bits(bits: np.ndarray) -> np.ndarray:
     return ((bits & 0x7F80) == 0x7F80) & ((bits & 0x7F) != 0)
 
 
+def cache_values(c: np.ndarray) -> np.ndarray:
+    """Cache values as float32: bf16 bit patterns (uint16) widened, fp32
+    caches as they are."""
+    return f32(c) if c.dtype == np.uint16 else np.asarray(c, dtype=np.float32)
+
+
+def cache_ordinal(c: np.ndarray) -> np.ndarray:
+    """Cache values on a monotone integer line in units of the cache type's
+    ulp (+0 and -0 both 0)."""
+    if c.dtype == np.uint16:
+        return ordinal(c)
+    b = np.asarray(c, dtype=np.float32).view(np.int32).astype(np.int64)
+    mag = b & 0x7FFFFFFF
+    return np.where(b < 0, -mag, mag)
+
+
+def cache_spacing(c: np.ndarray, mag: np.ndarray) -> np.ndarray:
+    """One ulp of the cache type at magnitude mag: a bf16 spacing, or for an
+    fp32 cache four fp32 spacings (its roundings of x, x * mult and the soft
+    cap, and the two libraries' tanhf, each within an ulp or two)."""
+    if c.dtype == np.uint16:
+        return bf16_spacing(mag)
+    return 4.0 * np.spacing(np.asarray(mag, dtype=np.float32)).astype(np.float64)
+
+
 def pick_max(s: np.ndarray) -> int:
     """Lowest NaN index, else lowest index of the maximum (numpy argmax
     returns the first NaN or the first maximum)."""
@@ -95,7 +120,7 @@ def pick_max(s: np.ndarray) -> int:
 
 
 def scores(c_bits, T, g):
-    cf = f32(c_bits)
+    cf = cache_values(c_bits)
     if T > 0:
         s = cf / np.float32(T)
         if g is not None:
@@ -106,7 +131,7 @@ def scores(c_bits, T, g):
 
 def inv_cdf_bin(c_bits, T, u):
     """(bin, cdf, t) of the fp64 inverse CDF of softmax(f32(c) / T)."""
-    z = (f32(c_bits) / np.float32(T)).astype(np.float64)
+    z = (cache_values(c_bits) / np.float32(T)).astype(np.float64)
     e = np.exp(z - z.max())
     cdf = np.cumsum(e)
     t = float(u) * cdf[-1]
@@ -151,11 +176,12 @@ def walk(w, tok_gpu, cache_gpu, gumbel, rows=None, exact=False) -> Stats:
             u = oracle.uniform(oracle.hash_step(int(w.seeds[b]), b, i)) if w.mode == 1 else 0.0
             tok_o, c_o, diag, bias_o = oracle.step(w.base[b, i], w.head, w.embed, p, T, g, u=u,
                                                    mult=w.mult, cap=w.cap, mode=w.mode,
-                                                   with_diag=True, with_bias=True)
+                                                   with_diag=True, with_bias=True,
+                                                   cache_f32=w.cache_f32)
             c_g = cache_gpu[s, i, :V]
-            nan_o, nan_g = is_nan_bits(c_o), is_nan_bits(c_g)
+            nan_o, nan_g = np.isnan(cache_values(c_o)), np.isnan(cache_values(c_g))
             assert np.array_equal(nan_o, nan_g), f"row {b} step {i}: NaN positions differ"
-            d = np.abs(ordinal(c_o) - ordinal(c_g))
+            d = np.abs(cache_ordinal(c_o) - cache_ordinal(c_g))
             d[nan_o] = 0
             st.cache_elems += V
             same = (d == 0)
@@ -164,13 +190,13 @@ def walk(w, tok_gpu, cache_gpu, gumbel, rows=None, exact=False) -> Stats:
             if exact:
                 assert same.all(), f"row {b} step {i}: {int((~same).sum())} cache elements differ"
             else:
-                fo = f32(c_o).astype(np.float64)
-                fg = f32(c_g).astype(np.float64)
+                fo = cache_values(c_o).astype(np.float64)
+                fg = cache_values(c_g).astype(np.float64)
                 fin = ~nan_o & np.isfinite(fo) & np.isfinite(fg)
                 assert np.array_equal(fo[~nan_o & ~fin], fg[~nan_o & ~fin]), f"row {b} step {i}: infinities differ"
                 tol_bias = bias_tolerance(bias_o, absdot(p), w.r)
                 bound = (tol_bias * abs(w.mult)
-                         + bf16_spacing(np.maximum(np.abs(fo), np.abs(fg))))
+                         + cache_spacing(c_o, np.maximum(np.abs(fo), np.abs(fg))))
                 bad = fin & (np.abs(fo - fg) > bound)
                 assert not bad.any(), (f"row {b} step {i}: {int(bad.sum())} cache values beyond the "
                                        f"bias-implied bound, e.g. v={int(np.flatnonzero(bad)[0])}")

@@ -99,6 +99,9 @@ def _sample(**kw):
     (dict(rows=2, states=1, trs=8), lm.MARKOV_E_INVAL),          # no state_idx: states >= rows
     (dict(rank=384), lm.MARKOV_E_UNSUPPORTED),
     (dict(rows=65), lm.MARKOV_E_UNSUPPORTED),
+    (dict(mode=2 | lm.MARKOV_CACHE_F32), lm.MARKOV_E_UNSUPPORTED),  # a bad mode with a dtype flag
+    (dict(mode=lm.MARKOV_BASE_F32, bss=1000), lm.MARKOV_E_INVAL),  # flags do not skip the checks
+    (dict(mode=lm.MARKOV_CACHE_F32, cache=(1 << 20) + 8), lm.MARKOV_E_INVAL),
 ])
 def test_invalid_arguments_rejected_on_host(kw, code):
     assert _sample(**kw) == code
@@ -125,3 +128,16 @@ def test_binding_refuses_cpu_tensors():
     s = torch.zeros(1, dtype=torch.int64)
     with pytest.raises(ValueError):
         lm.markov_noise_fill(w.view(1, 1, 4), s)
+
+
+def test_dtype_flags_do_not_change_shape_queries():
+    for f in (0, lm.MARKOV_BASE_F32, lm.MARKOV_CACHE_F32, lm.MARKOV_BASE_F32 | lm.MARKOV_CACHE_F32):
+        assert lm.markov_workspace_bytes(3, 8, 4096, 256, f) == lm.markov_workspace_bytes(3, 8, 4096, 256, 0)
+        assert lm.markov_workspace_bytes(3, 8, 4096, 512, 1 | f) == lm.markov_workspace_bytes(3, 8, 4096, 512, 1)
+
+
+def test_binding_refuses_other_element_types():
+    import torch
+    base = torch.zeros(1, 1, 16, dtype=torch.float16)
+    with pytest.raises(TypeError):
+        lm.markov_chain_sample(base, base, base, base, base, base, base, base)

@@ -463,3 +463,55 @@ def test_bad_previous_token_is_reported():
     w = synth.make("t", 64, 256, 1, 1, seed=20)
     with pytest.raises(ValueError):
         oracle.chain(w.base, w.head, w.embed, np.array([64]), w.temperature, w.seeds)
+
+
+# ------------------------------------------------------- element types ---
+# The pages' sampler takes bf16 or fp32 base logits and a bf16 or fp32
+# draft-logits cache; cache_round rounds to the cache's type, so an fp32
+# cache holds x itself.
+
+def test_fp32_base_of_bf16_values_equals_bf16_base():
+    """fp32 base logits that are bf16 values give the bf16 chain exactly."""
+    w = synth.make("dt", 3000, 256, 3, 4, seed=61, temperature=[0.7, 0.0, 1.0], mult=0.5, cap=30.0)
+    t1, c1 = oracle.chain(w.base, w.head, w.embed, w.prev, w.temperature, w.seeds, mult=w.mult, cap=w.cap)
+    t2, c2 = oracle.chain(f32(w.base), w.head, w.embed, w.prev, w.temperature, w.seeds, mult=w.mult, cap=w.cap)
+    assert np.array_equal(t1, t2) and np.array_equal(c1, c2)
+
+
+def test_fp32_cache_is_base_plus_bias_and_tokens_are_argmax():
+    """Closed form: with an fp32 cache and no transform, cache = fp32(base +
+    f32(bias)) (numpy fp32 add) for the oracle's own bias (pinned above), and
+    each token is numpy's first argmax of cache / T + gumbel (fp32 ops)."""
+    V, N = 2048, 3
+    w = synth.make("dt2", V, 256, 1, N, seed=62, temperature=0.6)
+    rng = np.random.default_rng(63)
+    base = (rng.standard_normal((1, N, V)) * 3).astype(np.float32)  # not bf16 values
+    g = oracle.noise_fill(w.seeds, N, V)
+    toks, cache = oracle.chain(base, w.head, w.embed, w.prev, w.temperature, w.seeds, gumbel=g,
+                               cache_f32=True)
+    assert cache.dtype == np.float32
+    p = int(w.prev[0])
+    for i in range(N):
+        _, _, bias = oracle.step(base[0, i], w.head, w.embed, p, 0.6, g[0, i], with_bias=True)
+        expect = (base[0, i] + f32(bias)).astype(np.float32)
+        assert np.array_equal(cache[0, i], expect)
+        s = (cache[0, i] / np.float32(0.6)).astype(np.float32) + g[0, i]
+        assert toks[0, i] == int(np.argmax(s))
+        p = int(toks[0, i])
+
+
+def test_fp32_cache_inverse_cdf_vs_searchsorted():
+    """Mode 1 on an fp32 cache: numpy's searchsorted of u*S in the fp64
+    cumulative exp(z - max z), z = cache / T (no bf16 rounding anywhere)."""
+    V, N = 512, 4
+    w = synth.make("dt3", V, 256, 1, N, seed=64, temperature=1.5, mode=1)
+    rng = np.random.default_rng(65)
+    base = (rng.standard_normal((1, N, V)) * 2).astype(np.float32)
+    toks, cache = oracle.chain(base, w.head, w.embed, w.prev, w.temperature, w.seeds, mode=1,
+                               cache_f32=True)
+    for i in range(N):
+        z = (cache[0, i] / np.float32(1.5)).astype(np.float32).astype(np.float64)
+        cdf = np.cumsum(np.exp(z - z.max()))
+        u = oracle.uniform(oracle.hash_step(int(w.seeds[0]), 0, i))
+        k = int(np.searchsorted(cdf, u * cdf[-1], side="right"))
+        assert toks[0, i] == min(k, V - 1)
