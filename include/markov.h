@@ -51,7 +51,7 @@ typedef enum {
 #define MARKOV_CACHE_F32 0x20 /* the cache is fp32: cache_round keeps x unrounded */
 
 /* Limits of this build. */
-#define MARKOV_MAX_ROWS 64
+#define MARKOV_MAX_ROWS 4096 /* one launch takes 64; more run as consecutive launches */
 #define MARKOV_MAX_STEPS 256
 #define MARKOV_MAX_VOCAB (1 << 24)
 
@@ -145,7 +145,10 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
  *                   marks a padding row.  Distinct non-negative entries.
  *   output_multiplier  fp32 multiplier (1.0f: none); finite.
  *   soft_cap        fp32 soft cap (0: none); finite, >= 0.
- *   rows in [1, MARKOV_MAX_ROWS]; steps in [1, MARKOV_MAX_STEPS]; vocab a
+ *   rows in [1, MARKOV_MAX_ROWS] (more than 64 rows run as consecutive
+ *   launches of at most 64 rows on `stream`, each reading the head once;
+ *   row indices in the mode-1 hash and the identity state map stay the
+ *   call's); steps in [1, MARKOV_MAX_STEPS]; vocab a
  *   positive multiple of 16 up to MARKOV_MAX_VOCAB; rank 256 or 512;
  *   mode MARKOV_MODE_GUMBEL or MARKOV_MODE_INVCDF, with the element-type
  *   flags above (markov_workspace_bytes and markov_grid ignore them).

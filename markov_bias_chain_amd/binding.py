@@ -27,7 +27,7 @@ MARKOV_MODE_GUMBEL = 0
 MARKOV_MODE_INVCDF = 1
 MARKOV_BASE_F32 = 0x10
 MARKOV_CACHE_F32 = 0x20
-MARKOV_MAX_ROWS = 64
+MARKOV_MAX_ROWS = 4096
 MARKOV_MAX_STEPS = 256
 
 # every symbol include/markov.h declares

@@ -65,6 +65,7 @@ constexpr int kWaves = 8;                  // waves per workgroup
 constexpr int kThreads = kWaves * 64;      // 512 threads, one workgroup per CU
 constexpr int kSlots = 32;                 // 16-byte head vectors per lane per group
 constexpr int kAhead = 8;                  // request rows whose next-step inputs are prefetched
+constexpr int kLaunchRows = 64;            // request rows of one chain launch
 constexpr int kBatch = 8;                  // request rows per epilogue batch
 constexpr int kLanesPerRow = 8;            // lanes per request row in a batch
 static_assert(kAhead == kBatch, "prefetched rows form one epilogue batch");
@@ -333,8 +334,8 @@ __device__ __forceinline__ float log_f32_rn(float x) { return (float)log((double
 __global__ __launch_bounds__(256) void noise_fill_kernel(float* __restrict__ gumbel,
                                                          const int64_t* __restrict__ seeds,
                                                          int steps, int V) {
-  const int rs = blockIdx.y;  // row * steps + step
-  const int row = rs / steps, step = rs - row * steps;
+  const int step = blockIdx.y, row = blockIdx.z;
+  const int rs = row * steps + step;
   const int v0 = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (v0 >= V) return;  // V is a multiple of 16: a thread's 4 ids are all valid
   const uint64_t prefix = noise_prefix(seeds[row], row, step);
@@ -363,6 +364,7 @@ struct ChainParams {
   float mult, cap, inv_cap;
   int has_cap;
   int rows, N, V, NG, NC, G;
+  int row_base;  // the call's row index of this launch's row 0
   int64_t* tokens;
   long long tok_rs;
   void* cache;  // bf16 bits, or fp32 when cache_f32
@@ -564,18 +566,18 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   constexpr int ES = emb_stride<R>();  // LDS row stride of the embeddings
   constexpr int BS = bias_stride<R>(); // LDS row stride of a wave's bias tile
 
-  __shared__ int s_state[MARKOV_MAX_ROWS];
-  __shared__ int s_active[MARKOV_MAX_ROWS];
-  __shared__ float s_T[MARKOV_MAX_ROWS];
-  __shared__ int64_t s_seed[MARKOV_MAX_ROWS];  // mode 1: the rows' seeds
-  __shared__ int s_tok[MARKOV_MAX_ROWS];
-  __shared__ int s_need[MARKOV_MAX_ROWS];
-  __shared__ uint64_t s_dec[MARKOV_MAX_ROWS];
-  __shared__ uint64_t s_key[kWaves][MARKOV_MAX_ROWS];
-  __shared__ float s_wsum[kWaves][MARKOV_MAX_ROWS];
+  __shared__ int s_state[kLaunchRows];
+  __shared__ int s_active[kLaunchRows];
+  __shared__ float s_T[kLaunchRows];
+  __shared__ int64_t s_seed[kLaunchRows];  // mode 1: the rows' seeds
+  __shared__ int s_tok[kLaunchRows];
+  __shared__ int s_need[kLaunchRows];
+  __shared__ uint64_t s_dec[kLaunchRows];
+  __shared__ uint64_t s_key[kWaves][kLaunchRows];
+  __shared__ float s_wsum[kWaves][kLaunchRows];
   __shared__ float s_bias[kWaves][kRowPass * BS];  // each wave's [16][RPG] bias tile
   // the next step's base logits of every batch (inverse CDF, resident head, > kAhead rows)
-  __shared__ uint32_t s_pre[(MODE == 1 && RES && !SMALL) ? kWaves * (MARKOV_MAX_ROWS / kBatch) * (RPG / 16) * 64 : 1];
+  __shared__ uint32_t s_pre[(MODE == 1 && RES && !SMALL) ? kWaves * (kLaunchRows / kBatch) * (RPG / 16) * 64 : 1];
   __shared__ int s_abort;
   __shared__ uint32_t s_parity;
   extern __shared__ uint4 s_e[];  // [rows][ES] 16-byte vectors of the current embeddings
@@ -605,7 +607,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     s_abort = 0;
   }
   for (int b = tid; b < rows; b += kThreads) {
-    const int64_t st = p.state_idx ? p.state_idx[b] : b;
+    const int64_t st = p.state_idx ? p.state_idx[b] : p.row_base + b;
     const int64_t tok = p.prev[b];
     int active = st >= 0;
     if (active && st >= p.cache_states) {
@@ -726,7 +728,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // exchange and parked in LDS (s_pre, each wave's own lanes), so the local
   // work reads no global memory.
   constexpr bool stage = MODE == 1 && RES && !SMALL;
-  constexpr int kStageBatches = MARKOV_MAX_ROWS / kBatch;
+  constexpr int kStageBatches = kLaunchRows / kBatch;
   uint32_t pst[stage ? kStageBatches : 1][IPL / 2];  // bf16 pairs of every batch
   auto stage_load = [&](int i) {
     const int nbat = (rows + kBatch - 1) / kBatch;
@@ -1188,7 +1190,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             }
             const float incl = wave_incl_scan(lsum);
             const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
-            const float t = hash_uniform(noise_prefix(s_seed[b], b, i)) * total;
+            const float t = hash_uniform(noise_prefix(s_seed[b], p.row_base + b, i)) * total;
             // First chunk whose inclusive prefix exceeds t (else the last
             // chunk with weight, when rounding left none above t).
             int found = -1, last_pos = -1;
@@ -1232,7 +1234,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // w + 8 j, lane j polls row w + 8 j, all at once.
         {
           const int b = wave + kWaves * lane;
-          const bool mine = lane < MARKOV_MAX_ROWS / kWaves && b < rows && s_active[b];
+          const bool mine = lane < kLaunchRows / kWaves && b < rows && s_active[b];
           uint64_t d = 0;
           for (;;) {
             if (mine && d == 0) d = ld_agent(L.dec + (size_t)i * rows + b);
@@ -1333,7 +1335,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // H4: rows whose chunk another workgroup owns, polled all at once.
         {
           const int b = wave + kWaves * lane;
-          const bool mine = lane < MARKOV_MAX_ROWS / kWaves && b < rows && s_active[b] && s_need[b] == 1;
+          const bool mine = lane < kLaunchRows / kWaves && b < rows && s_active[b] && s_need[b] == 1;
           uint64_t d = 0;
           for (;;) {
             if (mine && d == 0) d = ld_agent(L.tok + (size_t)i * rows + b);
@@ -1446,7 +1448,7 @@ const void* kernel_for(int rank, int mode, int kind, bool dt) {
 }
 
 // Dynamic LDS above the default per-launch limit is opted into once per
-// process for every chain kernel (the embeddings of MARKOV_MAX_ROWS rows:
+// process for every chain kernel (the embeddings of kLaunchRows rows:
 // 33 KiB at r = 256, 65 KiB at r = 512).
 int prepare_kernels() {
   static std::once_flag once;
@@ -1458,7 +1460,7 @@ int prepare_kernels() {
           for (bool dt : {false, true}) {
           hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, kind, dt),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             MARKOV_MAX_ROWS * (rank / 8 + 1) * 16);
+                                             kLaunchRows * (rank / 8 + 1) * 16);
           if (e != hipSuccess && err == hipSuccess) err = e;
         }
   });
@@ -1500,7 +1502,7 @@ size_t markov_workspace_bytes(int rows, int steps, int vocab, int rank, int mode
   mode &= ~kDtypeFlags;
   Shape sh;
   if (check_shape(rows, steps, vocab, rank, mode, &sh) != MARKOV_OK) return 0;
-  return kHeader + 2 * half_bytes_needed(rows, steps, sh.NC, mode);
+  return kHeader + 2 * half_bytes_needed(rows < kLaunchRows ? rows : kLaunchRows, steps, sh.NC, mode);
 }
 
 int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps, int vocab,
@@ -1513,7 +1515,7 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps, 
   if (vocab < 16 || vocab % 16 != 0 || vocab > MARKOV_MAX_VOCAB)
     return fail(MARKOV_E_UNSUPPORTED, "vocab=%d is not a positive multiple of 16 up to %d", vocab,
                 MARKOV_MAX_VOCAB);
-  dim3 grid((vocab / 4 + 255) / 256, rows * steps);
+  dim3 grid((vocab / 4 + 255) / 256, steps, rows);
   hipLaunchKernelGGL(noise_fill_kernel, grid, dim3(256), 0, (hipStream_t)stream, gumbel, seeds, steps,
                      vocab);
   hipError_t e = hipGetLastError();
@@ -1556,59 +1558,70 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_
     return fail(MARKOV_E_INVAL, "tokens_row_stride=%lld < steps", (long long)tokens_row_stride);
   if (!isfinite(output_multiplier) || !isfinite(soft_cap) || soft_cap < 0.0f)
     return fail(MARKOV_E_INVAL, "output_multiplier must be finite and soft_cap finite and >= 0");
-  const size_t need = kHeader + 2 * half_bytes_needed(rows, steps, sh.NC, mode);
+  // Calls with more rows than one launch takes run as consecutive launches
+  // of at most kLaunchRows rows on the stream (each reads the head once);
+  // they use the workspace one after another.
+  const int lrows = rows < kLaunchRows ? rows : kLaunchRows;
+  const size_t need = kHeader + 2 * half_bytes_needed(lrows, steps, sh.NC, mode);
   if (workspace_bytes < need)
     return fail(MARKOV_E_INVAL, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
-  int G = 0;
-  bool res = false;
-  rc = pick_grid(rows, rank, mode, sh, &G, &res);
-  if (rc != MARKOV_OK) return rc;
-
-  ChainParams p;
-  p.base = base_logits;
-  p.base_f32 = base_f32;
-  p.base_rs = base_row_stride;
-  p.base_ss = base_step_stride;
-  p.head = head;
-  p.embed = embed;
-  p.prev = prev_tokens;
-  p.temp = temperature;
-  p.seeds = seeds;
-  p.gumbel = gumbel;
-  p.state_idx = state_idx;
-  p.mult = output_multiplier;
-  p.cap = soft_cap;
-  p.inv_cap = soft_cap > 0.0f ? 1.0f / soft_cap : 1.0f;
-  p.has_cap = soft_cap > 0.0f;
-  p.rows = rows;
-  p.N = steps;
-  p.V = vocab;
-  p.NG = sh.NG;
-  p.NC = sh.NC;
-  p.G = G;
-  p.tokens = draft_tokens;
-  p.tok_rs = tokens_row_stride;
-  p.cache = cache;
-  p.cache_f32 = cache_f32;
-  p.cache_rs = cache_state_stride;
-  p.cache_ss = cache_step_stride;
-  p.cache_states = cache_states;
-  p.ws = (unsigned char*)workspace;
-  p.ws_half = ((workspace_bytes - kHeader) / 2) & ~(size_t)255;
-
-  void* args[] = {&p};
-  const size_t shmem = (size_t)rows * (rank / 8 + 1) * 16;
-  const void* kern = kernel_for(rank, mode, kernel_kind(rows, mode, res), base_f32 || cache_f32);
   rc = prepare_kernels();
   if (rc != MARKOV_OK) return rc;
-  // A regular launch: the grid is at most one workgroup per CU and the
-  // kernel's resources admit only one per CU, so on an otherwise idle device
-  // every workgroup is resident at once; every cross-workgroup wait is
-  // bounded, so a grid that is not co-resident ends with
-  // MARKOV_DEVERR_TIMEOUT instead of hanging.
-  hipError_t e = hipLaunchKernel(kern, dim3(G), dim3(kThreads), args, (unsigned)shmem,
-                                 (hipStream_t)stream);
-  if (e != hipSuccess) return fail(MARKOV_E_HIP, "chain launch (grid %d): %s", G, hipGetErrorString(e));
+  const size_t besz = base_f32 ? 4 : 2;
+  for (int r0 = 0; r0 < rows; r0 += kLaunchRows) {
+    const int nr = rows - r0 < kLaunchRows ? rows - r0 : kLaunchRows;
+    int G = 0;
+    bool res = false;
+    rc = pick_grid(nr, rank, mode, sh, &G, &res);
+    if (rc != MARKOV_OK) return rc;
+
+    ChainParams p;
+    p.base = static_cast<const char*>(base_logits) + (size_t)r0 * (size_t)base_row_stride * besz;
+    p.base_f32 = base_f32;
+    p.base_rs = base_row_stride;
+    p.base_ss = base_step_stride;
+    p.head = head;
+    p.embed = embed;
+    p.prev = prev_tokens + r0;
+    p.temp = temperature + r0;
+    p.seeds = seeds ? seeds + r0 : nullptr;
+    p.gumbel = gumbel ? gumbel + (size_t)r0 * steps * vocab : nullptr;
+    p.state_idx = state_idx ? state_idx + r0 : nullptr;
+    p.mult = output_multiplier;
+    p.cap = soft_cap;
+    p.inv_cap = soft_cap > 0.0f ? 1.0f / soft_cap : 1.0f;
+    p.has_cap = soft_cap > 0.0f;
+    p.rows = nr;
+    p.row_base = r0;
+    p.N = steps;
+    p.V = vocab;
+    p.NG = sh.NG;
+    p.NC = sh.NC;
+    p.G = G;
+    p.tokens = draft_tokens + (size_t)r0 * tokens_row_stride;
+    p.tok_rs = tokens_row_stride;
+    p.cache = cache;
+    p.cache_f32 = cache_f32;
+    p.cache_rs = cache_state_stride;
+    p.cache_ss = cache_step_stride;
+    p.cache_states = cache_states;
+    p.ws = (unsigned char*)workspace;
+    p.ws_half = ((workspace_bytes - kHeader) / 2) & ~(size_t)255;
+
+    void* args[] = {&p};
+    const size_t shmem = (size_t)nr * (rank / 8 + 1) * 16;
+    const void* kern = kernel_for(rank, mode, kernel_kind(nr, mode, res), base_f32 || cache_f32);
+    // A regular launch: the grid is at most one workgroup per CU and the
+    // kernel's resources admit only one per CU, so on an otherwise idle
+    // device every workgroup is resident at once; every cross-workgroup wait
+    // is bounded, so a grid that is not co-resident ends with
+    // MARKOV_DEVERR_TIMEOUT instead of hanging.
+    hipError_t e = hipLaunchKernel(kern, dim3(G), dim3(kThreads), args, (unsigned)shmem,
+                                   (hipStream_t)stream);
+    if (e != hipSuccess)
+      return fail(MARKOV_E_HIP, "chain launch (rows %d..%d, grid %d): %s", r0, r0 + nr - 1, G,
+                  hipGetErrorString(e));
+  }
   return MARKOV_OK;
 }
 
@@ -1642,7 +1655,7 @@ int markov_grid(int rows, int steps, int vocab, int rank, int mode) {
   if (rc != MARKOV_OK) return rc;
   int G = 0;
   bool res = false;
-  rc = pick_grid(rows, rank, mode, sh, &G, &res);
+  rc = pick_grid(rows < kLaunchRows ? rows : kLaunchRows, rank, mode, sh, &G, &res);
   return rc != MARKOV_OK ? rc : G;
 }
 

@@ -50,7 +50,7 @@ def test_workspace_bytes():
 
 @pytest.mark.parametrize("args", [
     (0, 8, 1024, 256, 0),      # rows
-    (65, 8, 1024, 256, 0),
+    (4097, 8, 1024, 256, 0),
     (1, 0, 1024, 256, 0),      # steps
     (1, 257, 1024, 256, 0),
     (1, 8, 1000, 256, 0),      # vocab % 16
@@ -98,7 +98,7 @@ def _sample(**kw):
     (dict(states=0), lm.MARKOV_E_INVAL),
     (dict(rows=2, states=1, trs=8), lm.MARKOV_E_INVAL),          # no state_idx: states >= rows
     (dict(rank=384), lm.MARKOV_E_UNSUPPORTED),
-    (dict(rows=65), lm.MARKOV_E_UNSUPPORTED),
+    (dict(rows=4097), lm.MARKOV_E_UNSUPPORTED),
     (dict(mode=2 | lm.MARKOV_CACHE_F32), lm.MARKOV_E_UNSUPPORTED),  # a bad mode with a dtype flag
     (dict(mode=lm.MARKOV_BASE_F32, bss=1000), lm.MARKOV_E_INVAL),  # flags do not skip the checks
     (dict(mode=lm.MARKOV_CACHE_F32, cache=(1 << 20) + 8), lm.MARKOV_E_INVAL),
