@@ -1030,6 +1030,102 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // the next step's embedding is usually in flight before the exchange
         // ends.  The row goes straight into the LDS embedding buffer, which no
         // wave reads again in this step.
+        // More than kWaves rows with more than 64 workgroups: a two-level
+        // exchange whose waits cover all of a wave's rows at once (wave w
+        // serves rows w + 8 j).  Reducer r (workgroup r < NR): lane l polls
+        // slot 64 r + l of each of the wave's rows until every one has
+        // arrived, then publishes each row's maximum.  Every workgroup: lane
+        // j NRP + r polls reducer r's partial of the wave's row j, then takes
+        // the maximum over its NRP lanes.  (Polling the rows one after
+        // another cost a round trip per row.)
+        const int NRm = reducers_for(G);
+        const int NRSm = reducers_for(NC);
+        const bool many = !SMALL && rows > kWaves && NRm > 1;
+        if constexpr (!SMALL) if (many) {
+          const int nrw = rows > wave ? (rows - wave + kWaves - 1) / kWaves : 0;  // <= 8
+          constexpr int kMaxRW = kLaunchRows / kWaves;
+          if (wg < NRm) {
+            const int idx = wg * 64 + lane;
+            uint64_t x[kMaxRW];
+#pragma unroll
+            for (int j = 0; j < kMaxRW; ++j) {
+              const int b = wave + kWaves * j;
+              x[j] = (j < nrw && s_active[b] && idx < G) ? 0 : kNoCandidate;
+            }
+            for (;;) {
+              bool all = true;
+#pragma unroll
+              for (int j = 0; j < kMaxRW; ++j) {
+                if (x[j] == 0) x[j] = ld_agent(L.keys + ((size_t)i * rows + wave + kWaves * j) * NC + idx);
+                all = all && x[j] != 0;
+              }
+              if (__all(all)) break;
+              if (now_ticks() > deadline) {
+                slot_wait_abort();
+                break;
+              }
+              __builtin_amdgcn_s_sleep(1);
+            }
+#pragma unroll
+            for (int j = 0; j < kMaxRW; ++j) {
+              const int b = wave + kWaves * j;
+              if (j < nrw && s_active[b]) {
+                const uint64_t K = wave_max_u64(x[j] == 0 ? kNoCandidate : x[j]);
+                if (lane == 0) st_agent(L.part + ((size_t)i * rows + b) * NRSm + wg, K);
+              }
+            }
+          }
+          // Followers: NRP lanes per row (NRP a power of two >= NR).
+          int NRP = 1;
+          while (NRP < NRm) NRP <<= 1;
+          const int per_pass = 64 / NRP;
+          for (int j0 = 0; j0 < nrw; j0 += per_pass) {
+            const int j = j0 + lane / NRP, r = lane % NRP;
+            const int b = wave + kWaves * j;
+            const bool mine = j < nrw && r < NRm && s_active[b];
+            uint64_t x = mine ? 0 : kNoCandidate;
+            for (;;) {
+              if (x == 0) x = ld_agent(L.part + ((size_t)i * rows + b) * NRSm + r);
+              if (__all(x != 0)) break;
+              if (now_ticks() > deadline) {
+                slot_wait_abort();
+                if (x == 0) x = kNoCandidate;
+                break;
+              }
+              __builtin_amdgcn_s_sleep(1);
+            }
+            // maximum over the row's NRP lanes
+            for (int d = 1; d < NRP; d <<= 1) x = umax64(x, (uint64_t)__shfl_xor((long long)x, d));
+            uint32_t win = key_id(x);
+            if (win >= (uint32_t)V) win = 0;  // only after a timeout
+            // Each row's winner and, for the next step, its embedding: the
+            // loads of all the pass's rows are issued before any is stored.
+            const bool lead = r == 0 && j < nrw && s_active[b];
+            if (lead) s_tok[b] = (int)win;
+            if (i + 1 < N) {
+              constexpr int kHalf = kMaxRW / 2;
+#pragma unroll
+              for (int k0 = 0; k0 < kMaxRW; k0 += kHalf) {
+                uint4 ev[kHalf];
+#pragma unroll
+                for (int k = 0; k < kHalf; ++k) {
+                  const int jk = j0 + k0 + k;
+                  const int bk = wave + kWaves * jk;
+                  const uint32_t wk = (uint32_t)__shfl((int)win, (k0 + k) * NRP);
+                  ev[k] = make_uint4(0, 0, 0, 0);
+                  if (k0 + k < per_pass && jk < nrw && s_active[bk] && lane < KSEG)
+                    ev[k] = *reinterpret_cast<const uint4*>(p.embed + (size_t)wk * R + lane * 8);
+                }
+#pragma unroll
+                for (int k = 0; k < kHalf; ++k) {
+                  const int jk = j0 + k0 + k;
+                  const int bk = wave + kWaves * jk;
+                  if (k0 + k < per_pass && jk < nrw && s_active[bk] && lane < KSEG) s_e[bk * ES + lane] = ev[k];
+                }
+              }
+            }
+          }
+        }
         // A single row with more than 64 workgroups exchanges in two levels:
         // reducer r (workgroup r < NR) waits for slots 64 r .. 64 r + 63 and
         // publishes their maximum; every workgroup then polls the NR
@@ -1038,7 +1134,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // reducers each serve every row, were slower than all-to-all.)
         const int NR = rows == 1 ? reducers_for(G) : 1;
         const int NRS = reducers_for(NC);  // the part arrays' row stride
-        if (NR > 1 && wg < NR) {
+        if (!many && NR > 1 && wg < NR) {
           for (int b = wave; b < rows; b += kWaves) {
             if (!s_active[b]) continue;
             const uint64_t* slots = L.keys + ((size_t)i * rows + b) * NC;
@@ -1057,7 +1153,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             if (lane == 0) st_agent(L.part + ((size_t)i * rows + b) * NRS + wg, K);
           }
         }
-        for (int b = wave; b < rows; b += kWaves) {
+        for (int b = many ? rows : wave; b < rows; b += kWaves) {
           if (!s_active[b]) continue;
           const uint64_t* slots = NR > 1 ? L.part + ((size_t)i * rows + b) * NRS : L.keys + ((size_t)i * rows + b) * NC;
           const int n = NR > 1 ? NR : G;  // words polled: partials or slots

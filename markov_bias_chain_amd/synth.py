@@ -174,12 +174,22 @@ def large_vocab_stress() -> Workload:
     return w
 
 
+def dsv41_batch(rows: int) -> Workload:
+    """Beyond the five named workloads: a DeepSeek-sized batch of `rows`
+    Gumbel rows (N=8, T=1, base as the 1-row case), for the > 64-row path
+    (consecutive launches of 64 rows)."""
+    return make(f"dsv41_V129280_r256_rows{rows}_N8", 129280, 256, rows, 8,
+                seed=MASTER_SEED + 6 + rows, peaks=32, temperature=1.0)
+
+
 WORKLOADS = {
     "tiny_exact": tiny_exact,
     "dsv41_single_row": dsv41_single_row,
     "dsv41_eight_rows": dsv41_eight_rows,
     "dsv41_invcdf_64rows": dsv41_invcdf_64rows,
     "large_vocab_stress": large_vocab_stress,
+    "dsv41_64rows": functools.partial(dsv41_batch, 64),
+    "dsv41_256rows": functools.partial(dsv41_batch, 256),
 }
 
 
