@@ -1,15 +1,24 @@
 """Benchmark of the Markov draft-sampling chain on one MI355X.
 
-A step is one pass of the whole hot path over one batch: the Gumbel noise
-fill on a side stream (forked after the current stream's work and joined
-before the chain) and the persistent chain kernel.  The default workload is
+A step is one pass of the whole hot path over one batch: by default one
+launch of the persistent chain kernel that draws its Gumbel noise itself
+(MARKOV_NOISE_INLINE: the idle waves of each workgroup draw the next step's
+noise while the exchange is in flight); with --noise side, the noise fill
+kernel on a side stream (forked after the current stream's work and joined
+before the chain) and the chain reading it.  The default workload is
 the DeepSeek-V4.1-sized single request row: V=129280, r=256 (a 66 MB bf16
 head), rows=1, N=8 draft positions, T=0.7, synthetic inputs.
 
-Prints ONE JSON line.  `value` is draft tokens/s over the timed steps
-(back to back, inputs resident in HBM).  `roofline` is for the chain kernel:
-algorithmic bytes per launch (head once, base logits, noise, cache writes,
-embedding rows, tokens) over its average launch duration, measured with HIP
+Prints ONE JSON line.  `value` is draft tokens/s over the timed steps, run
+back to back with inputs resident in HBM: a step with inline noise is one
+kernel launch, issued eagerly; a step with side-stream noise (fork, noise,
+join, chain) is replayed as one HIP graph (the pages capture the sampler in
+graphs; this keeps the fork/join launch gaps out).  Both ways of issuing are
+reported (`eager_ms_per_step`, `graph_ms_per_step`).
+`roofline` is for the chain kernel:
+algorithmic bytes per launch (head once, base logits, noise read unless it
+is drawn inline, cache writes, embedding rows, tokens) over its average
+launch duration, measured with HIP
 events on the stream it runs on around `steps` back-to-back chain launches.
 Cold calls (a 1 GiB read between calls evicts the L2s and the 256 MB MALL
 with clean lines, outside the timed interval) are reported too.
@@ -47,9 +56,10 @@ def kernel_source_digest() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(noise: str):
     """HBM-side bytes per chain launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel code (else None)."""
+    summary, if it was taken on the current kernel code with the same noise
+    placement (else None)."""
     try:
         text = open(TRAFFIC_PROFILE).read()
     except OSError:
@@ -57,15 +67,17 @@ def measured_traffic():
     fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and " " not in line.split(": ")[0])
     if fields.get("kernel_code_sha256_prefix", "").strip() != kernel_source_digest():
         return None
+    if fields.get("noise", "side").strip() != noise:
+        return None
     return int(fields["traffic_bytes_per_launch"])
 
 
-def algorithmic_bytes(w) -> dict:
+def algorithmic_bytes(w, inline: bool) -> dict:
     """Bytes one chain call must move at minimum (padding rows excluded)."""
     real = w.real_rows
     head = w.V * w.r * 2
     base = real * w.N * w.V * 2
-    noise = real * w.N * w.V * 4 if w.mode == 0 else 0
+    noise = real * w.N * w.V * 4 if w.mode == 0 and not inline else 0
     cache = real * w.N * w.V * 2
     embed = real * w.N * w.r * 2
     tokens = real * w.N * 8
@@ -101,14 +113,16 @@ def draft_step_figures(w, hidden: int, dev, reps: int = 50) -> dict:
     """The pages' deployment shape around the chain, as context: a stand-in
     draft LM head (base logits = hidden states @ W with random bf16 weights
     [hidden, V]) runs on the current stream while the noise runs on a side
-    stream, then the chain; eager and captured as one HIP graph.  The LM
-    head is not part of the hot path and not part of `value`."""
+    stream, then the chain; eager and captured as one HIP graph.  Also the
+    same with the noise drawn inside the chain (LM head, then the chain).
+    The LM head is not part of the hot path and not part of `value`."""
     import torch
 
     from markov_bias_chain_amd import binding
     from markov_bias_chain_amd.device import DeviceChain
 
     d = DeviceChain(w, device=dev)
+    di = DeviceChain(w, device=dev, noise_inline=True)
     gen = torch.Generator(device=dev)
     gen.manual_seed(0x4D41524B)
     weight = torch.empty(hidden, w.V, dtype=torch.bfloat16, device=dev)
@@ -162,13 +176,32 @@ def draft_step_figures(w, hidden: int, dev, reps: int = 50) -> dict:
     same = bool((t_g == t_e).all() and (c_g == c_e).all())
     graph_us = timed(g.replay)
     binding.markov_status(d.workspace)
-    del g, d, weight, hs
+    del g
+    # inline noise: the LM head writes the inline chain's base logits
+    base2d_i = di.base.view(w.rows * w.N, w.V)
+
+    def step_inline():
+        torch.matmul(hs, weight, out=base2d_i)
+        di.chain()
+
+    chain_inline_us = timed(lambda: di.chain())
+    inline_eager_us = timed(step_inline)
+    step_inline()
+    torch.cuda.synchronize(dev)
+    gi = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gi):
+        step_inline()
+    inline_graph_us = timed(gi.replay)
+    binding.markov_status(di.workspace)
+    del gi, d, di, weight, hs
     torch.cuda.empty_cache()
     return {"lm_head_stand_in": f"[{w.rows * w.N}, {hidden}] @ [{hidden}, {w.V}] bf16 (torch.matmul)",
             "lm_head_us": lm_us, "noise_us": noise_us, "chain_us": chain_us,
             "eager_step_us": eager_us, "graph_step_us": graph_us,
             "noise_hidden_us": lm_us + noise_us + chain_us - eager_us,
-            "graph_replay_matches_eager": same}
+            "graph_replay_matches_eager": same,
+            "inline_noise": {"chain_us": chain_inline_us, "eager_step_us": inline_eager_us,
+                             "graph_step_us": inline_graph_us}}
 
 
 def main() -> int:
@@ -177,6 +210,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv41_single_row")
+    ap.add_argument("--noise", choices=("inline", "side"), default="inline",
+                    help="mode 0: noise drawn inside the chain kernel, or by the noise fill "
+                         "kernel on a side stream")
     ap.add_argument("--cold", type=int, default=50, help="cold calls timed after the main loop")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -203,19 +239,39 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    def measure(w, steps, warmup, cold_calls):
-        d = DeviceChain(w, device=dev)
+    def measure(w, steps, warmup, cold_calls, inline):
+        d = DeviceChain(w, device=dev, noise_inline=inline)
+        side = w.mode == 0 and not inline
         stream = torch.cuda.current_stream(dev)
         for _ in range(warmup):
             d.step()
         torch.cuda.synchronize()
         binding.markov_status(d.workspace)
+        # the steps issued eagerly, back to back
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            d.step()
+        torch.cuda.synchronize()
+        eager_wall = time.perf_counter() - t0
+        binding.markov_status(d.workspace)
+        # the steps as replays of one graph (noise fork/join + chain)
+        graph = d.capture_step()
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_wall = time.perf_counter() - t0
+        binding.markov_status(d.workspace)
+        del graph
+        # the steps again, each chain bracketed by events
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for k in range(steps):
-            if w.mode == 0:
+            if side:
                 d.side.wait_stream(stream)
                 d.noise(stream=d.side)
                 stream.wait_stream(d.side)
@@ -223,7 +279,6 @@ def main() -> int:
             d.chain(stream=stream)
             ev[k][1].record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         binding.markov_status(d.workspace)
         chain_ms = [a.elapsed_time(b) for a, b in ev]
         # the chain alone, back to back: the average launch duration
@@ -240,7 +295,7 @@ def main() -> int:
         sink = torch.empty((), dtype=torch.float32, device=dev)
         cold_ms = []
         for k in range(cold_calls):
-            if w.mode == 0:
+            if side:
                 d.noise(stream=stream)
             torch.sum(scratch, dim=0, out=sink)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -252,7 +307,12 @@ def main() -> int:
         binding.markov_status(d.workspace)
         del scratch, d
         torch.cuda.empty_cache()
-        return wall, chain_ms, cold_ms, b2b_ms
+        # the step as it is run: one eager launch, or one graph replay when
+        # the noise is forked onto a side stream
+        step_wall = graph_wall if side else eager_wall
+        return dict(step_wall=step_wall, eager_wall=eager_wall, graph_wall=graph_wall,
+                    chain_ms=chain_ms, cold_ms=cold_ms, b2b_ms=b2b_ms,
+                    issue="graph replay" if side else "eager launch")
 
     if args.calibrate_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -263,10 +323,12 @@ def main() -> int:
         del src, dst
 
     w = synth.workload(args.workload)
-    wall, chain_ms, cold_ms, b2b_ms = measure(w, args.steps, args.warmup, args.cold)
+    inline = args.noise == "inline" and w.mode == 0
+    m = measure(w, args.steps, args.warmup, args.cold, inline)
+    chain_ms, cold_ms, b2b_ms = m["chain_ms"], m["cold_ms"], m["b2b_ms"]
     tok_per_step = w.real_rows * w.N
-    ms_per_step = wall * 1e3 / args.steps
-    ab = algorithmic_bytes(w)
+    ms_per_step = m["step_wall"] * 1e3 / args.steps
+    ab = algorithmic_bytes(w, inline)
     chain_us = b2b_ms * 1e3
     chain_us_med = statistics.median(chain_ms) * 1e3
     cold_us_med = statistics.median(cold_ms) * 1e3 if cold_ms else None
@@ -279,6 +341,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "eager_ms_per_step": m["eager_wall"] * 1e3 / args.steps,
+        "graph_ms_per_step": m["graph_wall"] * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -287,7 +351,10 @@ def main() -> int:
         "config": {"workload": w.name, "V": w.V, "r": w.r, "rows": w.rows, "N": w.N,
                    "mode": "gumbel" if w.mode == 0 else "invcdf",
                    "grid": binding.markov_grid(w.rows, w.N, w.V, w.r, w.mode),
-                   "step": "noise fill on a side stream + chain kernel"},
+                   "noise": "inline" if inline else ("side stream" if w.mode == 0 else "none"),
+                   "step": ("chain kernel drawing its noise inline (one launch)" if inline
+                            else "chain kernel (one launch)" if w.mode == 1
+                            else "noise fill on a side stream + chain kernel") + ", " + m["issue"]},
         "chain_us_per_call": {"back_to_back_mean": chain_us,
                               "warm_event_mean": statistics.mean(chain_ms) * 1e3,
                               "warm_median": chain_us_med,
@@ -298,20 +365,30 @@ def main() -> int:
                       "cold": ab["head"] / (cold_us_med * 1e-6) / 1e9 if cold_us_med else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic() if args.workload == "dsv41_single_row" else None,
+                     "traffic": measured_traffic(args.noise) if args.workload == "dsv41_single_row" else None,
                      "kernel": "chain_kernel", "bytes_per_launch": ab["total"]},
     }
     if cold_us_med:
         ach_c = ab["total"] / (cold_us_med * 1e-6) / 1e9
         result["roofline_cold"] = {"achieved": ach_c, "frac": ach_c / HBM_PEAK_GBPS}
     if not args.no_extra and args.workload == "dsv41_single_row":
+        # the other noise placement of the same workload (one step, graph replay)
+        other = not inline
+        mo = measure(w, 100, 10, 0, other)
+        result["other_noise_placement"] = {
+            "noise": "inline" if other else "side stream", "issue": mo["issue"],
+            "ms_per_step": mo["step_wall"] * 1e3 / 100,
+            "draft_tokens_per_s": tok_per_step * 100 / mo["step_wall"],
+            "chain_us_back_to_back": mo["b2b_ms"] * 1e3}
         w8 = synth.workload("dsv41_eight_rows")
-        _, c8, k8, _ = measure(w8, 50, 10, 20)
+        m8 = measure(w8, 50, 10, 20, inline)
+        c8, k8 = m8["chain_ms"], m8["cold_ms"]
         us8 = statistics.median(c8) * 1e3
         result["rows8"] = {"workload": w8.name, "chain_us_warm_median": us8,
                            "chain_us_cold_median": statistics.median(k8) * 1e3,
                            "draft_tokens_per_s": w8.real_rows * w8.N / (us8 * 1e-6),
-                           "head_GBps_warm": algorithmic_bytes(w8)["head"] / (us8 * 1e-6) / 1e9}
+                           "step_tokens_per_s": w8.real_rows * w8.N * 50 / m8["step_wall"],
+                           "head_GBps_warm": algorithmic_bytes(w8, inline)["head"] / (us8 * 1e-6) / 1e9}
     if not args.no_extra and args.lm_hidden > 0:
         result["draft_step"] = draft_step_figures(w, args.lm_hidden, dev)
     if not args.no_cpu_baseline:

@@ -50,6 +50,14 @@ typedef enum {
 #define MARKOV_BASE_F32 0x10  /* base_logits are fp32 */
 #define MARKOV_CACHE_F32 0x20 /* the cache is fp32: cache_round keeps x unrounded */
 
+/* Noise placement, OR-ed into MARKOV_MODE_GUMBEL (sharded_markov page,
+ * fork_noise; fused_markov page, module docstring: Gumbel-max costs a hash
+ * and two logs per logit).  With MARKOV_NOISE_INLINE the chain kernel draws
+ * gumbel[b][i][v] itself, from seeds, bit-identical to what
+ * markov_noise_fill writes; `gumbel` is then not read and may be NULL, and
+ * `seeds` is required.  Without it the noise is read from `gumbel`. */
+#define MARKOV_NOISE_INLINE 0x40
+
 /* Limits of this build. */
 #define MARKOV_MAX_ROWS 4096 /* one launch takes 64; more run as consecutive launches */
 #define MARKOV_MAX_STEPS 256
@@ -136,11 +144,11 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
  *                   outside [0, vocab) sets MARKOV_DEVERR_BAD_TOKEN and makes
  *                   the row inert.
  *   temperature     device, fp32 [rows].
- *   seeds           device, int64 [rows]; read in MARKOV_MODE_INVCDF only
- *                   (may be NULL in MARKOV_MODE_GUMBEL).
+ *   seeds           device, int64 [rows]; read in MARKOV_MODE_INVCDF and
+ *                   with MARKOV_NOISE_INLINE (may be NULL otherwise).
  *   gumbel          device, fp32 [rows][steps][vocab] contiguous, as
  *                   markov_noise_fill writes it; read in MARKOV_MODE_GUMBEL
- *                   only (may be NULL in MARKOV_MODE_INVCDF).
+ *                   without MARKOV_NOISE_INLINE only (may be NULL otherwise).
  *   state_idx       device, int64 [rows], or NULL for the identity; negative
  *                   marks a padding row.  Distinct non-negative entries.
  *   output_multiplier  fp32 multiplier (1.0f: none); finite.
@@ -151,7 +159,8 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
  *   call's); steps in [1, MARKOV_MAX_STEPS]; vocab a
  *   positive multiple of 16 up to MARKOV_MAX_VOCAB; rank 256 or 512;
  *   mode MARKOV_MODE_GUMBEL or MARKOV_MODE_INVCDF, with the element-type
- *   flags above (markov_workspace_bytes and markov_grid ignore them).
+ *   flags above and, for MARKOV_MODE_GUMBEL, MARKOV_NOISE_INLINE
+ *   (markov_workspace_bytes and markov_grid ignore the flags).
  *   draft_tokens    device, int64 [rows][>= steps], row stride
  *                   tokens_row_stride, written for non-padding rows.
  *   cache           device, bf16 (fp32 with MARKOV_CACHE_F32)

@@ -27,6 +27,7 @@ MARKOV_MODE_GUMBEL = 0
 MARKOV_MODE_INVCDF = 1
 MARKOV_BASE_F32 = 0x10
 MARKOV_CACHE_F32 = 0x20
+MARKOV_NOISE_INLINE = 0x40  # mode 0: the chain draws the noise from seeds
 MARKOV_MAX_ROWS = 4096
 MARKOV_MAX_STEPS = 256
 

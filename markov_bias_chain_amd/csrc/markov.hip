@@ -13,6 +13,12 @@
 // Design (one GPU):
 //  * markov_noise_fill: one thread per 4 consecutive vocab ids, one 16-byte
 //    store; the (seed, row, step) part of the hash is computed per thread.
+//    Each fp32 log is the correctly rounded one, reached through a bucket
+//    table, a short fp64 series and a rounding-interval check (the fp64
+//    library log decides the rare undecided cases).
+//  * With MARKOV_NOISE_INLINE the chain kernel draws the same noise itself:
+//    for one row the waves that idle during the exchange draw the next
+//    step's values, so the noise costs no launch and no memory traffic.
 //  * markov_chain_sample: ONE persistent launch (at most one workgroup per
 //    CU) runs all N positions.  The vocabulary is cut into groups of
 //    16384 / r head rows (32 KiB of bf16 head each); a wavefront owns one
@@ -70,7 +76,7 @@ constexpr int kBatch = 8;                  // request rows per epilogue batch
 constexpr int kLanesPerRow = 8;            // lanes per request row in a batch
 static_assert(kAhead == kBatch, "prefetched rows form one epilogue batch");
 constexpr int kHeader = 256;               // workspace header bytes
-constexpr int kDtypeFlags = MARKOV_BASE_F32 | MARKOV_CACHE_F32;  // dtype bits of `mode`
+constexpr int kModeFlags = MARKOV_BASE_F32 | MARKOV_CACHE_F32 | MARKOV_NOISE_INLINE;  // flag bits of `mode`
 constexpr int kMaxPollPerLane = 16;        // slots one lane polls (<= 1024 per row)
 constexpr int kLeaderRegs = 4;             // inverse-CDF chunks per lane kept in registers by a leader
 constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz
@@ -327,7 +333,95 @@ __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memr
 
 // The correctly rounded fp32 natural log: fp64 log of the fp32 argument,
 // rounded once (fp32 log libraries are only faithfully rounded).
-__device__ __forceinline__ float log_f32_rn(float x) { return (float)log((double)x); }
+__device__ __noinline__ float log_f32_rn(float x) { return (float)log((double)x); }
+
+// A faster route to the same correctly rounded fp32 log of a positive
+// normal fp32 x.  x = m 2^e with m in [0.7, 1.4142); with the bucket centre
+// m_j = 1 + j/128 nearest m, c_j an fp32 value near 1/m_j and
+// r = m c_j - 1 (exact in fp64: 24-bit times 24-bit), ln x = e ln2 - ln c_j
+// + ln(1 + r), |r| < 0.0056, and ln(1 + r) is its Taylor series to r^7
+// (the rest is below 2^-62).  ln 2 is split as in fdlibm (ln2_hi has 32
+// significant bits, so e ln2_hi is exact).  The bucket of 1 has c = 1 and
+// ln c = 0, so results near 0 keep their relative accuracy; elsewhere
+// |ln m| <= ln2/2 cannot cancel e ln2.  The fp64 result is within 2^-44 of
+// ln x relatively; when that interval holds an fp32 rounding boundary
+// (about 2^-19 of the values) the fp64 library log decides.
+// The buckets j = -38 .. 53: g_log_c[j + 38] = c_j, g_log_nlc[j + 38] =
+// -ln(c_j) correctly rounded to fp64 (written by gen_log_table.py).
+#include "log_table.inc"
+struct LogTable {
+  float c[kLogTable];
+  double nlc[kLogTable];
+};
+// The fast part: sets ok = false (and returns garbage) when the library
+// log must decide.
+__device__ __forceinline__ float log_f32_try(float x, const LogTable& t, bool& ok) {
+  const uint32_t b = __float_as_uint(x);
+  int e = (int)(b >> 23) - 127;
+  float m = __uint_as_float((b & 0x7FFFFFu) | 0x3F800000u);  // [1, 2)
+  if (m >= 1.4140625f) {
+    m *= 0.5f;
+    e += 1;
+  }
+  const int k = (int)rintf((m - 1.0f) * 128.0f) + kLogTableBias;  // (m - 1) and * 128 are exact
+  const double r = fma((double)m, (double)t.c[k], -1.0);
+  double q = 1.0 / 7;
+  q = fma(q, r, -1.0 / 6);
+  q = fma(q, r, 1.0 / 5);
+  q = fma(q, r, -1.0 / 4);
+  q = fma(q, r, 1.0 / 3);
+  q = fma(q, r, -0.5);
+  const double lp = fma(q * r, r, r);  // ln(1 + r)
+  const double ln2_hi = 6.93147180369123816490e-01, ln2_lo = 1.90821492927058770002e-10;
+  const double y = fma((double)e, ln2_hi, (t.nlc[k] + lp) + (double)e * ln2_lo);
+  const double err = fabs(y) * 0x1p-44;
+  const float lo = (float)(y - err), hi = (float)(y + err);
+  ok = lo == hi;
+  return lo;
+}
+__device__ __forceinline__ void log_table_load(LogTable& t, int tid, int nthreads) {
+  for (int k = tid; k < kLogTable; k += nthreads) {
+    t.c[k] = g_log_c[k];
+    t.nlc[k] = g_log_nlc[k];
+  }
+}
+
+// Gumbel noise of M consecutive vocabulary ids v0 .. v0 + M - 1 of one
+// (seed, row, step) prefix: -log(-log u) with both logs correctly rounded.
+// The M evaluations are independent (their fast paths interleave); the
+// rare library-log fallbacks run afterwards.
+template <int M>
+__device__ __forceinline__ void gumbel_noise(uint64_t prefix, int v0, const LogTable& t, float* g) {
+  float u[M];
+  uint32_t bad = 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    u[j] = hash_uniform(splitmix64(prefix ^ (uint64_t)(v0 + j)));
+    bool ok;
+    g[j] = log_f32_try(u[j], t, ok);
+    bad |= (ok ? 0u : 1u) << j;
+  }
+  if (bad) {
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      if ((bad >> j) & 1u) g[j] = log_f32_rn(u[j]);
+  }
+  bad = 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    u[j] = -g[j];  // -log u, positive
+    bool ok;
+    g[j] = log_f32_try(u[j], t, ok);
+    bad |= (ok ? 0u : 1u) << j;
+  }
+  if (bad) {
+#pragma unroll
+    for (int j = 0; j < M; ++j)
+      if ((bad >> j) & 1u) g[j] = log_f32_rn(u[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < M; ++j) g[j] = -g[j];
+}
 
 // ============================================================== noise fill ==
 
@@ -336,15 +430,14 @@ __global__ __launch_bounds__(256) void noise_fill_kernel(float* __restrict__ gum
                                                          int steps, int V) {
   const int step = blockIdx.y, row = blockIdx.z;
   const int rs = row * steps + step;
+  __shared__ LogTable tab;
+  log_table_load(tab, threadIdx.x, 256);
+  __syncthreads();
   const int v0 = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (v0 >= V) return;  // V is a multiple of 16: a thread's 4 ids are all valid
   const uint64_t prefix = noise_prefix(seeds[row], row, step);
   float out[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float u = hash_uniform(splitmix64(prefix ^ (uint64_t)(v0 + j)));
-    out[j] = -log_f32_rn(-log_f32_rn(u));
-  }
+  gumbel_noise<4>(prefix, v0, tab, out);
   float4* dst = reinterpret_cast<float4*>(gumbel + (size_t)rs * V + v0);
   *dst = make_float4(out[0], out[1], out[2], out[3]);
 }
@@ -370,6 +463,7 @@ struct ChainParams {
   void* cache;  // bf16 bits, or fp32 when cache_f32
   long long cache_rs, cache_ss;
   int base_f32, cache_f32;
+  int noise_inline;  // mode 0: draw the Gumbel noise here from seeds (gumbel unused)
   long long cache_states;
   unsigned char* ws;
   unsigned long long ws_half;  // bytes per parity half
@@ -547,19 +641,21 @@ __device__ __forceinline__ float one_row_bias(const uint4 (&h)[kSlots], const ui
   }
 }
 
-// DT: base logits or cache may be fp32 (the element-type flags are read);
-// without it both are bf16.  RES: every workgroup owns exactly one chunk
-// (G == NC) and keeps its head in
-// VGPRs for the whole launch.  !RES: workgroups stride over the chunks and
-// stream the head from memory at every step.  SMALL (with RES): at most
-// kAhead request rows, whose next-step inputs are prefetched in registers
-// during the exchange.  ONE (with SMALL, mode 0): a single request row,
-// whose bias and epilogue stay in registers.
-template <int R, int MODE, bool RES, bool SMALL, bool ONE, bool DT>
+// FL: the flags of mode are read (fp32 base logits or cache, inline noise);
+// without it both are bf16 and the noise is read from memory.  RES: every
+// workgroup owns exactly one chunk (G == NC) and keeps its head in VGPRs
+// for the whole launch.  !RES: workgroups stride over the chunks and stream
+// the head from memory at every step.  SMALL (with RES): at most kAhead
+// request rows, whose next-step inputs are prefetched in registers during
+// the exchange.  ONE (with SMALL, mode 0): a single request row, whose bias
+// and epilogue stay in registers.  NZ (with ONE): the noise is drawn inline
+// without reading the flags.
+template <int R, int MODE, bool RES, bool SMALL, bool ONE, bool FL, bool NZ>
 __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
-  // Element types: only the DT variants read the flags (bf16 otherwise).
-  const bool base_f32 = DT && p.base_f32;
-  const bool cache_f32 = DT && p.cache_f32;
+  // Only the FL variants read the flags (bf16, noise from memory otherwise).
+  const bool base_f32 = FL && p.base_f32;
+  const bool cache_f32 = FL && p.cache_f32;
+  const bool nz_inline = MODE == 0 && (NZ || (FL && p.noise_inline));
   constexpr int RPG = 16384 / R;       // head rows per group
   constexpr int CHUNK = kWaves * RPG;  // vocab ids per chunk
   constexpr int KSEG = R / 8;          // 16-byte segments per head row
@@ -578,6 +674,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   __shared__ float s_bias[kWaves][kRowPass * BS];  // each wave's [16][RPG] bias tile
   // the next step's base logits of every batch (inverse CDF, resident head, > kAhead rows)
   __shared__ uint32_t s_pre[(MODE == 1 && RES && !SMALL) ? kWaves * (kLaunchRows / kBatch) * (RPG / 16) * 64 : 1];
+  __shared__ LogTable s_log;   // the noise's log table (mode 0, inline noise)
+  __shared__ float s_nz0[64];  // one row, inline noise: wave 0's next-step noise (reducers)
   __shared__ int s_abort;
   __shared__ uint32_t s_parity;
   extern __shared__ uint4 s_e[];  // [rows][ES] 16-byte vectors of the current embeddings
@@ -623,9 +721,10 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     s_state[b] = (int)st;
     s_active[b] = active;
     s_T[b] = p.temp[b];
-    if (MODE == 1) s_seed[b] = p.seeds[b];
+    if (MODE == 1 || nz_inline) s_seed[b] = p.seeds[b];
     s_tok[b] = active ? (int)tok : 0;
   }
+  if (MODE == 0 && nz_inline) log_table_load(s_log, tid, kThreads);
   __syncthreads();
   const uint32_t parity = s_parity & 1u;
   unsigned char* half = p.ws + kHeader + parity * p.ws_half;
@@ -637,14 +736,6 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       other[k] = make_uint4(0, 0, 0, 0);
   }
   const HalfLayout L = half_layout(half, rows, N, NC, MODE);
-  // Embeddings of the anchor tokens.
-  for (int k = tid; k < rows * KSEG; k += kThreads) {
-    const int b = k / KSEG, seg = k - b * KSEG;
-    if (s_active[b])
-      s_e[b * ES + seg] = *reinterpret_cast<const uint4*>(p.embed + (size_t)s_tok[b] * R + seg * 8);
-  }
-  __syncthreads();
-
   // ---- per-step inputs.
   // Single row (lane = vocab id): the base logit and noise of lane lr's id,
   // prefetched for the next step while the current step's exchange is in
@@ -654,6 +745,17 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   const bool own_res = (wg * kWaves + wave) < NG && v_res < V && lane_owns;
   uint32_t one_base = 0;
   float one_noise = 0.0f;
+  // Inline noise: waves 1 .. 7 draw the next step's noise here, while wave
+  // 0 alone waits for the exchange; wave 0 draws its own inside its first
+  // poll, behind the poll's loads, except in the reducer workgroups of the
+  // two-level exchange, whose wave 0 polls twice: there wave 1 draws it
+  // (into s_nz0).  Step 0's noise every wave draws here.
+  const bool one_nz = MODE == 0 && ONE && nz_inline;
+  const bool w0_by_w1 = one_nz && reducers_for(G) > 1 && wg < reducers_for(G);
+  auto draw_one = [&](int i) {
+    if (s_active[0] && own_res && s_T[0] > 0.0f)
+      gumbel_noise<1>(noise_prefix(s_seed[0], p.row_base, i), v_res, s_log, &one_noise);
+  };
   auto prefetch_one = [&](int i) {
     one_base = 0;
     one_noise = 0.0f;
@@ -662,7 +764,13 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       const long long at = (long long)i * p.base_ss + v_res;
       one_base = base_f32 ? reinterpret_cast<const uint32_t*>(p.base)[at]
                             : (uint32_t)reinterpret_cast<const uint16_t*>(p.base)[at] << 16;
-      if (MODE == 0 && s_T[0] > 0.0f) one_noise = p.gumbel[(size_t)i * V + v_res];
+      if (MODE == 0 && s_T[0] > 0.0f && !one_nz) one_noise = p.gumbel[(size_t)i * V + v_res];
+    }
+    if (one_nz && (wave != 0 || i == 0)) draw_one(i);
+    if (w0_by_w1 && wave == 1 && i > 0 && s_active[0] && s_T[0] > 0.0f) {
+      const int g0 = wg * kWaves;  // wave 0's group
+      const int v = g0 * RPG + lr;
+      if (g0 < NG && v < V && lane_owns) gumbel_noise<1>(noise_prefix(s_seed[0], p.row_base, i), v, s_log, &s_nz0[lane]);
     }
   };
   // Several rows: a batch of kBatch request rows is spread over the wave,
@@ -708,11 +816,21 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         }
       }
       if (MODE == 0 && s_T[b] > 0.0f) {
-        const float4* grow = reinterpret_cast<const float4*>(p.gumbel + ((size_t)b * N + i) * (size_t)V + v0);
+        if (nz_inline) {
+          // Prefetched rows draw it here, four ids at a time; the others in
+          // the epilogue (where fewer registers are live).
+          if constexpr (SMALL) {
+            const uint64_t pre = noise_prefix(s_seed[b], p.row_base + b, i);
 #pragma unroll
-        for (int e4 = 0; e4 < IPL / 4; ++e4) {
-          const float4 t = grow[e4];
-          in.nz[4 * e4] = t.x, in.nz[4 * e4 + 1] = t.y, in.nz[4 * e4 + 2] = t.z, in.nz[4 * e4 + 3] = t.w;
+            for (int e = 0; e < IPL; e += 4) gumbel_noise<4>(pre, v0 + e, s_log, in.nz + e);
+          }
+        } else {
+          const float4* grow = reinterpret_cast<const float4*>(p.gumbel + ((size_t)b * N + i) * (size_t)V + v0);
+#pragma unroll
+          for (int e4 = 0; e4 < IPL / 4; ++e4) {
+            const float4 t = grow[e4];
+            in.nz[4 * e4] = t.x, in.nz[4 * e4 + 1] = t.y, in.nz[4 * e4 + 2] = t.z, in.nz[4 * e4 + 3] = t.w;
+          }
         }
       }
     }
@@ -722,7 +840,22 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     if constexpr (ONE) prefetch_one(i);
     else load_rows(i, 0, wg * kWaves + wave, pre);
   };
-  if (ahead) prefetch(0);
+  // Embeddings of the anchor tokens; the first pass's loads are in flight
+  // during the step-0 prefetch (which may draw noise).
+  {
+    const int b = tid / KSEG, seg = tid - b * KSEG;
+    const bool mine = tid < rows * KSEG && s_active[b];
+    uint4 e = make_uint4(0, 0, 0, 0);
+    if (mine) e = *reinterpret_cast<const uint4*>(p.embed + (size_t)s_tok[b] * R + seg * 8);
+    if (ahead) prefetch(0);
+    if (mine) s_e[b * ES + seg] = e;
+  }
+  for (int k = tid + kThreads; k < rows * KSEG; k += kThreads) {
+    const int b = k / KSEG, seg = k - b * KSEG;
+    if (s_active[b])
+      s_e[b * ES + seg] = *reinterpret_cast<const uint4*>(p.embed + (size_t)s_tok[b] * R + seg * 8);
+  }
+  __syncthreads();
   // Inverse CDF with a resident head and more than kAhead rows: every
   // batch's base logits of the next step are loaded before the step's
   // exchange and parked in LDS (s_pre, each wave's own lanes), so the local
@@ -833,8 +966,19 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       for (int e = 0; e < IPL; ++e) z[e] = __fdiv_rn(z[e], T);
     }
     if (MODE == 0 && T > 0.0f) {
+      if (!SMALL && nz_inline && ok) {
+        const uint64_t pre = noise_prefix(s_seed[b], p.row_base + b, i);
 #pragma unroll
-      for (int e = 0; e < IPL; ++e) z[e] = __fadd_rn(z[e], in.nz[e]);
+        for (int e = 0; e < IPL; e += 2) {
+          float g2[2];
+          gumbel_noise<2>(pre, v0 + e, s_log, g2);
+          z[e] = __fadd_rn(z[e], g2[0]);
+          z[e + 1] = __fadd_rn(z[e + 1], g2[1]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < IPL; ++e) z[e] = __fadd_rn(z[e], in.nz[e]);
+      }
     }
     // This lane's best: the first NaN, else the first maximum (order keys
     // of z + 0, which makes -0 equal to +0).
@@ -900,6 +1044,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         const int v = g * RPG + lr;
         const bool own = g < NG && v < V && lane_owns;
         const float bsum = one_row_bias<R>(h, s_e, lane);
+        if (w0_by_w1 && wave == 0 && i > 0) one_noise = s_nz0[lane];
         uint32_t ord = 0;
         if (s_active[0] && own) {
           const float T = s_T[0];
@@ -1161,6 +1306,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           uint64_t best = kNoCandidate;
           uint32_t spec = 0xFFFFFFFFu;
           uint4 ev = make_uint4(0, 0, 0, 0);
+          bool first = true;
           for (;;) {
             bool all = true;
             uint64_t mine = kNoCandidate;
@@ -1175,6 +1321,10 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
                 }
               }
             }
+            // one row, inline noise: wave 0's next-step noise, drawn while
+            // the first poll's loads are in flight
+            if (one_nz && !w0_by_w1 && first && next) draw_one(i + 1);
+            first = false;
             best = wave_max_u64(mine);
             if (__all(all)) break;
             const uint32_t cand = key_id(best);
@@ -1516,31 +1666,35 @@ int check_shape(int rows, int steps, int vocab, int rank, int mode, Shape* sh) {
 
 // Kernel kinds: 0 streamed head, 1 resident head, 2 resident with at most
 // kAhead rows, 3 resident with one row (mode 0).
-template <int R, int MODE, bool DT>
+template <int R, int MODE, bool FL>
 const void* kernel_variant(int kind) {
   switch (kind) {
-    case 0: return (const void*)chain_kernel<R, MODE, false, false, false, DT>;
-    case 1: return (const void*)chain_kernel<R, MODE, true, false, false, DT>;
-    case 2: return (const void*)chain_kernel<R, MODE, true, true, false, DT>;
-    default: return (const void*)chain_kernel<R, MODE, true, true, MODE == 0, DT>;
+    case 0: return (const void*)chain_kernel<R, MODE, false, false, false, FL, false>;
+    case 1: return (const void*)chain_kernel<R, MODE, true, false, false, FL, false>;
+    case 2: return (const void*)chain_kernel<R, MODE, true, true, false, FL, false>;
+    case 3: return (const void*)chain_kernel<R, MODE, true, true, MODE == 0, FL, false>;
+    default: return (const void*)chain_kernel<R, MODE, true, true, MODE == 0, false, MODE == 0>;
   }
 }
 
+// Kernel kinds: 0 streamed head; 1 resident, more than kAhead rows; 2
+// resident, prefetched rows; 3 one row (mode 0); 4 one row drawing its noise
+// inline (mode 0, no flag reads).
 int kernel_kind(int rows, int mode, bool res) {
   if (!res) return 0;
   if (rows == 1 && mode == 0) return 3;
   return rows <= kAhead ? 2 : 1;
 }
 
-template <bool DT>
-const void* kernel_for_dt(int rank, int mode, int kind) {
-  if (rank == 256) return mode == 0 ? kernel_variant<256, 0, DT>(kind) : kernel_variant<256, 1, DT>(kind);
-  return mode == 0 ? kernel_variant<512, 0, DT>(kind) : kernel_variant<512, 1, DT>(kind);
+template <bool FL>
+const void* kernel_for_fl(int rank, int mode, int kind) {
+  if (rank == 256) return mode == 0 ? kernel_variant<256, 0, FL>(kind) : kernel_variant<256, 1, FL>(kind);
+  return mode == 0 ? kernel_variant<512, 0, FL>(kind) : kernel_variant<512, 1, FL>(kind);
 }
 
-// dt: base logits or cache fp32 (the kernels that read the element-type flags).
-const void* kernel_for(int rank, int mode, int kind, bool dt) {
-  return dt ? kernel_for_dt<true>(rank, mode, kind) : kernel_for_dt<false>(rank, mode, kind);
+// fl: a flag of mode is set (the kernels that read them).
+const void* kernel_for(int rank, int mode, int kind, bool fl) {
+  return fl ? kernel_for_fl<true>(rank, mode, kind) : kernel_for_fl<false>(rank, mode, kind);
 }
 
 // Dynamic LDS above the default per-launch limit is opted into once per
@@ -1552,9 +1706,9 @@ int prepare_kernels() {
   std::call_once(once, [] {
     for (int rank : {256, 512})
       for (int mode : {0, 1})
-        for (int kind = 0; kind < 4; ++kind)
-          for (bool dt : {false, true}) {
-          hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, kind, dt),
+        for (int kind = 0; kind < 5; ++kind)
+          for (bool fl : {false, true}) {
+          hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, kind, fl),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              kLaunchRows * (rank / 8 + 1) * 16);
           if (e != hipSuccess && err == hipSuccess) err = e;
@@ -1595,7 +1749,7 @@ int pick_grid(int rows, int rank, int mode, const Shape& sh, int* grid, bool* re
 extern "C" {
 
 size_t markov_workspace_bytes(int rows, int steps, int vocab, int rank, int mode) {
-  mode &= ~kDtypeFlags;
+  mode &= ~kModeFlags;
   Shape sh;
   if (check_shape(rows, steps, vocab, rank, mode, &sh) != MARKOV_OK) return 0;
   return kHeader + 2 * half_bytes_needed(rows < kLaunchRows ? rows : kLaunchRows, steps, sh.NC, mode);
@@ -1629,14 +1783,19 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_
                         size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   const int base_f32 = (mode & MARKOV_BASE_F32) != 0, cache_f32 = (mode & MARKOV_CACHE_F32) != 0;
-  mode &= ~kDtypeFlags;
+  const int noise_inline = (mode & MARKOV_NOISE_INLINE) != 0;
+  mode &= ~kModeFlags;
   Shape sh;
   int rc = check_shape(rows, steps, vocab, rank, mode, &sh);
   if (rc != MARKOV_OK) return rc;
+  if (noise_inline && mode != MARKOV_MODE_GUMBEL)
+    return fail(MARKOV_E_INVAL, "MARKOV_NOISE_INLINE applies to MARKOV_MODE_GUMBEL only");
+  if (noise_inline && !seeds) return fail(MARKOV_E_INVAL, "MARKOV_NOISE_INLINE needs seeds");
   if (!base_logits || !head || !embed || !prev_tokens || !temperature || !draft_tokens || !cache ||
       !workspace)
     return fail(MARKOV_E_INVAL, "a required pointer is null");
-  if (mode == MARKOV_MODE_GUMBEL && !gumbel) return fail(MARKOV_E_INVAL, "mode 0 needs gumbel noise");
+  if (mode == MARKOV_MODE_GUMBEL && !noise_inline && !gumbel)
+    return fail(MARKOV_E_INVAL, "mode 0 needs gumbel noise (or MARKOV_NOISE_INLINE)");
   if (mode == MARKOV_MODE_INVCDF && !seeds) return fail(MARKOV_E_INVAL, "mode 1 needs seeds");
   if (!aligned16(base_logits) || !aligned16(head) || !aligned16(embed) || !aligned16(cache) ||
       (gumbel && !aligned16(gumbel)))
@@ -1698,6 +1857,7 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_
     p.tok_rs = tokens_row_stride;
     p.cache = cache;
     p.cache_f32 = cache_f32;
+    p.noise_inline = noise_inline;
     p.cache_rs = cache_state_stride;
     p.cache_ss = cache_step_stride;
     p.cache_states = cache_states;
@@ -1706,7 +1866,15 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_
 
     void* args[] = {&p};
     const size_t shmem = (size_t)nr * (rank / 8 + 1) * 16;
-    const void* kern = kernel_for(rank, mode, kernel_kind(nr, mode, res), base_f32 || cache_f32);
+    // Inline noise: the one-row kernel has a variant that draws it with no
+    // flag reads; other kernels read the flag (FL).
+    int kind = kernel_kind(nr, mode, res);
+    bool fl = base_f32 || cache_f32;
+    if (noise_inline) {
+      if (kind == 3 && !fl) kind = 4;
+      else fl = true;
+    }
+    const void* kern = kernel_for(rank, mode, kind, fl);
     // A regular launch: the grid is at most one workgroup per CU and the
     // kernel's resources admit only one per CU, so on an otherwise idle
     // device every workgroup is resident at once; every cross-workgroup wait
@@ -1745,7 +1913,7 @@ int markov_set_grid(int g) { return g_grid_override.exchange(g < 0 ? 0 : g); }
 
 int markov_grid(int rows, int steps, int vocab, int rank, int mode) {
   g_last_error.clear();
-  mode &= ~kDtypeFlags;
+  mode &= ~kModeFlags;
   Shape sh;
   int rc = check_shape(rows, steps, vocab, rank, mode, &sh);
   if (rc != MARKOV_OK) return rc;

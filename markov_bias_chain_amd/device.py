@@ -23,8 +23,12 @@ class DeviceChain:
     """All device tensors of one workload, allocated once (so a HIP graph or
     a timing loop sees fixed addresses)."""
 
-    def __init__(self, w: Workload, device="cuda", token_fill: int = -7, cache_fill: int = 0xABCD):
+    def __init__(self, w: Workload, device="cuda", token_fill: int = -7, cache_fill: int = 0xABCD,
+                 noise_inline: bool = False):
+        """noise_inline (mode 0): the chain kernel draws the Gumbel noise
+        itself from the seeds; no noise buffer is allocated."""
         self.w = w
+        self.noise_inline = bool(noise_inline) and w.mode == 0
         dev = torch.device(device)
         self.device = dev
         self.head = to_device_bf16(w.head, dev)
@@ -36,7 +40,7 @@ class DeviceChain:
         self.temperature = torch.from_numpy(w.temperature).to(dev)
         self.state_idx = None if w.state_idx is None else torch.from_numpy(w.state_idx).to(dev)
         self.gumbel = torch.empty((w.rows, w.N, w.V), dtype=torch.float32, device=dev) \
-            if w.mode == 0 else None
+            if w.mode == 0 and not self.noise_inline else None
         self.tokens = torch.full((w.rows, w.N), token_fill, dtype=torch.int64, device=dev)
         if w.cache_f32:
             self.cache = torch.full((w.states, w.N, w.V), float("nan"), dtype=torch.float32, device=dev)
@@ -60,13 +64,14 @@ class DeviceChain:
             self.base, self.head, self.embed, self.prev, self.temperature, self.tokens,
             self.cache, self.workspace, gumbel=self.gumbel, seeds=self.seeds,
             state_idx=self.state_idx, output_multiplier=w.mult, soft_cap=w.cap,
-            mode=w.mode, stream=stream)
+            mode=w.mode | (lm.MARKOV_NOISE_INLINE if self.noise_inline else 0), stream=stream)
 
     def step(self) -> None:
         """One pass of the hot path: the noise on a side stream forked after
-        the current stream's work and joined before the chain, then the chain."""
+        the current stream's work and joined before the chain, then the chain
+        (with inline noise, the chain alone)."""
         cur = torch.cuda.current_stream(self.device)
-        if self.w.mode == 0:
+        if self.w.mode == 0 and not self.noise_inline:
             self.side.wait_stream(cur)
             self.noise(stream=self.side)
             cur.wait_stream(self.side)

@@ -1,0 +1,60 @@
+// The noise kernel's fp32 log, retyped for the host, against the fp64 libm
+// log rounded once to fp32 (the definition the noise uses), over every input
+// the Gumbel noise can present: u = (2k + 1) 2^-24 for k < 2^23 and -ln(u).
+// Also a strided sweep of fp32 values in [2^-30, 2^30).  Prints the counts.
+// Built with g++ -O2 -ffp-contract=off; fma() is the correctly rounded one.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#define __constant__ static const
+#include "../markov_bias_chain_amd/csrc/log_table.inc"
+
+static float asf(uint32_t b) { float f; std::memcpy(&f, &b, 4); return f; }
+static uint32_t asu(float f) { uint32_t b; std::memcpy(&b, &f, 4); return b; }
+static float ref_log(float x) { return (float)std::log((double)x); }
+static long fallbacks = 0;
+
+// Same operations, same order, as the kernel: bucket, r = m c - 1, Taylor
+// series to r^7 by Horner, e ln2 (hi/lo) + (-ln c + ln(1 + r)), and the
+// rounding-interval test with the library log when it fails.
+static float fast_log(float x) {
+  const uint32_t b = asu(x);
+  int e = (int)(b >> 23) - 127;
+  float m = asf((b & 0x7FFFFFu) | 0x3F800000u);
+  if (m >= 1.4140625f) { m *= 0.5f; e += 1; }
+  const int k = (int)std::rint((m - 1.0f) * 128.0f) + kLogTableBias;
+  const double r = std::fma((double)m, (double)g_log_c[k], -1.0);
+  double q = 1.0 / 7;
+  q = std::fma(q, r, -1.0 / 6);
+  q = std::fma(q, r, 1.0 / 5);
+  q = std::fma(q, r, -1.0 / 4);
+  q = std::fma(q, r, 1.0 / 3);
+  q = std::fma(q, r, -0.5);
+  const double lp = std::fma(q * r, r, r);
+  const double ln2_hi = 6.93147180369123816490e-01, ln2_lo = 1.90821492927058770002e-10;
+  const double y = std::fma((double)e, ln2_hi, (g_log_nlc[k] + lp) + (double)e * ln2_lo);
+  const double err = std::fabs(y) * 0x1p-44;
+  const float lo = (float)(y - err), hi = (float)(y + err);
+  if (lo == hi) return lo;
+  ++fallbacks;
+  return ref_log(x);
+}
+
+int main() {
+  long n = 0, bad = 0;
+  for (uint32_t k = 0; k < (1u << 23); ++k) {
+    const float u = (float)(2u * k + 1u) * 0x1p-24f;
+    const float a = ref_log(u);
+    bad += asu(fast_log(u)) != asu(a);
+    bad += asu(fast_log(-a)) != asu(ref_log(-a));
+    n += 2;
+  }
+  const long noise_fallbacks = fallbacks;
+  long n2 = 0, bad2 = 0;
+  for (uint32_t b = asu(0x1p-30f); b < asu(0x1p30f); b += 7, ++n2)
+    bad2 += asu(fast_log(asf(b))) != asu(ref_log(asf(b)));
+  std::printf("noise %ld %ld %ld sweep %ld %ld %ld\n", n, bad, noise_fallbacks, n2, bad2,
+              fallbacks - noise_fallbacks);
+  return 0;
+}

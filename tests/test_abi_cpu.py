@@ -102,10 +102,21 @@ def _sample(**kw):
     (dict(mode=2 | lm.MARKOV_CACHE_F32), lm.MARKOV_E_UNSUPPORTED),  # a bad mode with a dtype flag
     (dict(mode=lm.MARKOV_BASE_F32, bss=1000), lm.MARKOV_E_INVAL),  # flags do not skip the checks
     (dict(mode=lm.MARKOV_CACHE_F32, cache=(1 << 20) + 8), lm.MARKOV_E_INVAL),
+    (dict(mode=1 | lm.MARKOV_NOISE_INLINE), lm.MARKOV_E_INVAL),          # inline noise is mode 0's
+    (dict(mode=lm.MARKOV_NOISE_INLINE, seeds=None), lm.MARKOV_E_INVAL),  # it needs seeds
+    (dict(mode=lm.MARKOV_NOISE_INLINE, gumbel=None, wsb=64), lm.MARKOV_E_INVAL),  # gumbel may be NULL
 ])
 def test_invalid_arguments_rejected_on_host(kw, code):
     assert _sample(**kw) == code
     assert lm.markov_last_error()
+
+
+def test_inline_noise_needs_no_gumbel():
+    # the checks pass the missing noise and stop at the (too small) workspace
+    assert _sample(mode=lm.MARKOV_NOISE_INLINE, gumbel=None, wsb=64) == lm.MARKOV_E_INVAL
+    assert "workspace" in lm.markov_last_error()
+    assert _sample(mode=0, gumbel=None, wsb=64) == lm.MARKOV_E_INVAL
+    assert "gumbel" in lm.markov_last_error()
 
 
 def test_noise_fill_rejects_bad_arguments():
@@ -131,7 +142,8 @@ def test_binding_refuses_cpu_tensors():
 
 
 def test_dtype_flags_do_not_change_shape_queries():
-    for f in (0, lm.MARKOV_BASE_F32, lm.MARKOV_CACHE_F32, lm.MARKOV_BASE_F32 | lm.MARKOV_CACHE_F32):
+    for f in (0, lm.MARKOV_BASE_F32, lm.MARKOV_CACHE_F32, lm.MARKOV_BASE_F32 | lm.MARKOV_CACHE_F32,
+              lm.MARKOV_NOISE_INLINE):
         assert lm.markov_workspace_bytes(3, 8, 4096, 256, f) == lm.markov_workspace_bytes(3, 8, 4096, 256, 0)
         assert lm.markov_workspace_bytes(3, 8, 4096, 512, 1 | f) == lm.markov_workspace_bytes(3, 8, 4096, 512, 1)
 
