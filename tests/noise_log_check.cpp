@@ -15,28 +15,28 @@ static uint32_t asu(float f) { uint32_t b; std::memcpy(&b, &f, 4); return b; }
 static float ref_log(float x) { return (float)std::log((double)x); }
 static long fallbacks = 0;
 
-// Same operations, same order, as the kernel: bucket, r = m c - 1, Taylor
-// series to r^7 by Horner, e ln2 (hi/lo) + (-ln c + ln(1 + r)), and the
-// rounding-interval test with the library log when it fails.
+// Same operations, same order, as the kernel: bucket, r = m c - 1 in fp64,
+// the r^4 tail of ln(1 + r) in fp32, r - r^2/2 + r^3/3 in fp64, + e ln2 -
+// ln c, and the test of the 29 bits below fp32 precision against the
+// rounding midpoint, with the library log when it fails.
 static float fast_log(float x) {
   const uint32_t b = asu(x);
   int e = (int)(b >> 23) - 127;
   float m = asf((b & 0x7FFFFFu) | 0x3F800000u);
   if (m >= 1.4140625f) { m *= 0.5f; e += 1; }
-  const int k = (int)std::rint((m - 1.0f) * 128.0f) + kLogTableBias;
+  const int k = (int)std::rint(std::fmaf(m, 128.0f, -128.0f)) + kLogTableBias;
   const double r = std::fma((double)m, (double)g_log_c[k], -1.0);
-  double q = 1.0 / 7;
-  q = std::fma(q, r, -1.0 / 6);
-  q = std::fma(q, r, 1.0 / 5);
-  q = std::fma(q, r, -1.0 / 4);
-  q = std::fma(q, r, 1.0 / 3);
-  q = std::fma(q, r, -0.5);
-  const double lp = std::fma(q * r, r, r);
-  const double ln2_hi = 6.93147180369123816490e-01, ln2_lo = 1.90821492927058770002e-10;
-  const double y = std::fma((double)e, ln2_hi, (g_log_nlc[k] + lp) + (double)e * ln2_lo);
-  const double err = std::fabs(y) * 0x1p-44;
-  const float lo = (float)(y - err), hi = (float)(y + err);
-  if (lo == hi) return lo;
+  const float rf = (float)r;
+  float q = std::fmaf(-1.0f / 6.0f, rf, 0.2f);
+  q = std::fmaf(q, rf, -0.25f);
+  const float r2 = rf * rf;
+  const float tail = (q * r2) * r2;
+  const double lp = std::fma(r * r, std::fma(r, 1.0 / 3.0, -0.5), r) + (double)tail;
+  const double y = std::fma((double)e, 0x1.62e42fefa39efp-1, g_log_nlc[k] + lp);
+  uint64_t yb;
+  std::memcpy(&yb, &y, 8);
+  const int d = (int)((uint32_t)yb & 0x1FFFFFFFu) - (1 << 28);
+  if ((d < 0 ? -d : d) > (1 << 12)) return (float)y;
   ++fallbacks;
   return ref_log(x);
 }

@@ -1,5 +1,5 @@
 """The noise kernel's table-driven fp32 log (its bucket table, Taylor series
-and rounding-interval test) returns the correctly rounded log on every input
+and rounding-midpoint test) returns the correctly rounded log on every input
 the Gumbel noise presents: checked exhaustively on the host with the same
 fp64 operations (CPU only; the GPU noise parity tests cover the kernel)."""
 
@@ -23,5 +23,5 @@ def test_fast_log_exhaustive(tmp_path):
     n2, bad2, fb2 = map(int, out[5:8])
     assert n == 2 ** 24 and bad == 0
     assert n2 > 7 * 10 ** 7 and bad2 == 0
-    # the library-log fallback is rare (about 2^-19 of the inputs)
-    assert fb < n // 10000 and fb2 < n2 // 10000
+    # the library-log fallback is rare (about 2^-16 of the inputs)
+    assert fb < n // 20000 and fb2 < n2 // 20000
