@@ -464,7 +464,6 @@ struct ChainParams {
   void* cache;  // bf16 bits, or fp32 when cache_f32
   long long cache_rs, cache_ss;
   int base_f32, cache_f32;
-  int noise_inline;  // mode 0: draw the Gumbel noise here from seeds (gumbel unused)
   long long cache_states;
   unsigned char* ws;
   unsigned long long ws_half;  // bytes per parity half
@@ -642,21 +641,21 @@ __device__ __forceinline__ float one_row_bias(const uint4 (&h)[kSlots], const ui
   }
 }
 
-// FL: the flags of mode are read (fp32 base logits or cache, inline noise);
-// without it both are bf16 and the noise is read from memory.  RES: every
+// FL: the element-type flags of mode are read (fp32 base logits or cache);
+// without it both are bf16.  RES: every
 // workgroup owns exactly one chunk (G == NC) and keeps its head in VGPRs
 // for the whole launch.  !RES: workgroups stride over the chunks and stream
 // the head from memory at every step.  SMALL (with RES): at most kAhead
 // request rows, whose next-step inputs are prefetched in registers during
 // the exchange.  ONE (with SMALL, mode 0): a single request row, whose bias
-// and epilogue stay in registers.  NZ (with ONE): the noise is drawn inline
-// without reading the flags.
+// and epilogue stay in registers.  NZ (mode 0): the noise is drawn inline
+// from the seeds instead of read from memory.
 template <int R, int MODE, bool RES, bool SMALL, bool ONE, bool FL, bool NZ>
 __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // Only the FL variants read the flags (bf16, noise from memory otherwise).
   const bool base_f32 = FL && p.base_f32;
   const bool cache_f32 = FL && p.cache_f32;
-  const bool nz_inline = MODE == 0 && (NZ || (FL && p.noise_inline));
+  const bool nz_inline = MODE == 0 && NZ;
   constexpr int RPG = 16384 / R;       // head rows per group
   constexpr int CHUNK = kWaves * RPG;  // vocab ids per chunk
   constexpr int KSEG = R / 8;          // 16-byte segments per head row
@@ -818,8 +817,9 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       }
       if (MODE == 0 && s_T[b] > 0.0f) {
         if (nz_inline) {
-          // Prefetched rows draw it here, four ids at a time; the others in
-          // the epilogue (where fewer registers are live).
+          // Prefetched rows draw it here, four ids at a time (right after
+          // the publication, before the exchange's polls); the others in the
+          // epilogue (where fewer registers are live).
           if constexpr (SMALL) {
             const uint64_t pre = noise_prefix(s_seed[b], p.row_base + b, i);
 #pragma unroll
@@ -1311,7 +1311,22 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           for (;;) {
             bool all = true;
             uint64_t mine = kNoCandidate;
-            for (int k0 = 0; k0 < n; k0 += 256) {  // 4 words per lane per batch
+            uint64_t xs[4];  // the first 256 words: 4 per lane
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int idx = lane + 64 * k;
+              xs[k] = idx < n ? ld_agent(slots + idx) : kNoCandidate;
+            }
+            // One row, inline noise: wave 0's next-step values, drawn while
+            // the first round's loads are in flight.
+            if (one_nz && !w0_by_w1 && first && next) draw_one(i + 1);
+            first = false;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              all = all && (xs[k] != 0);
+              mine = umax64(mine, xs[k]);
+            }
+            for (int k0 = 256; k0 < n; k0 += 256) {  // 4 more words per lane per batch
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
                 const int idx = k0 + lane + 64 * k;
@@ -1322,10 +1337,6 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
                 }
               }
             }
-            // one row, inline noise: wave 0's next-step noise, drawn while
-            // the first poll's loads are in flight
-            if (one_nz && !w0_by_w1 && first && next) draw_one(i + 1);
-            first = false;
             best = wave_max_u64(mine);
             if (__all(all)) break;
             const uint32_t cand = key_id(best);
@@ -1667,35 +1678,35 @@ int check_shape(int rows, int steps, int vocab, int rank, int mode, Shape* sh) {
 
 // Kernel kinds: 0 streamed head, 1 resident head, 2 resident with at most
 // kAhead rows, 3 resident with one row (mode 0).
-template <int R, int MODE, bool FL>
+template <int R, int MODE, bool FL, bool NZ>
 const void* kernel_variant(int kind) {
   switch (kind) {
-    case 0: return (const void*)chain_kernel<R, MODE, false, false, false, FL, false>;
-    case 1: return (const void*)chain_kernel<R, MODE, true, false, false, FL, false>;
-    case 2: return (const void*)chain_kernel<R, MODE, true, true, false, FL, false>;
-    case 3: return (const void*)chain_kernel<R, MODE, true, true, MODE == 0, FL, false>;
-    default: return (const void*)chain_kernel<R, MODE, true, true, MODE == 0, false, MODE == 0>;
+    case 0: return (const void*)chain_kernel<R, MODE, false, false, false, FL, NZ>;
+    case 1: return (const void*)chain_kernel<R, MODE, true, false, false, FL, NZ>;
+    case 2: return (const void*)chain_kernel<R, MODE, true, true, false, FL, NZ>;
+    default: return (const void*)chain_kernel<R, MODE, true, true, MODE == 0, FL, NZ>;
   }
 }
 
 // Kernel kinds: 0 streamed head; 1 resident, more than kAhead rows; 2
-// resident, prefetched rows; 3 one row (mode 0); 4 one row drawing its noise
-// inline (mode 0, no flag reads).
+// resident, prefetched rows; 3 one row (mode 0).
 int kernel_kind(int rows, int mode, bool res) {
   if (!res) return 0;
   if (rows == 1 && mode == 0) return 3;
   return rows <= kAhead ? 2 : 1;
 }
 
-template <bool FL>
+template <bool FL, bool NZ>
 const void* kernel_for_fl(int rank, int mode, int kind) {
-  if (rank == 256) return mode == 0 ? kernel_variant<256, 0, FL>(kind) : kernel_variant<256, 1, FL>(kind);
-  return mode == 0 ? kernel_variant<512, 0, FL>(kind) : kernel_variant<512, 1, FL>(kind);
+  if (rank == 256) return mode == 0 ? kernel_variant<256, 0, FL, NZ>(kind) : kernel_variant<256, 1, FL, false>(kind);
+  return mode == 0 ? kernel_variant<512, 0, FL, NZ>(kind) : kernel_variant<512, 1, FL, false>(kind);
 }
 
-// fl: a flag of mode is set (the kernels that read them).
-const void* kernel_for(int rank, int mode, int kind, bool fl) {
-  return fl ? kernel_for_fl<true>(rank, mode, kind) : kernel_for_fl<false>(rank, mode, kind);
+// fl: fp32 base logits or cache (the kernels that read those flags); nz:
+// inline noise (mode 0; ignored in mode 1).
+const void* kernel_for(int rank, int mode, int kind, bool fl, bool nz) {
+  if (fl) return nz ? kernel_for_fl<true, true>(rank, mode, kind) : kernel_for_fl<true, false>(rank, mode, kind);
+  return nz ? kernel_for_fl<false, true>(rank, mode, kind) : kernel_for_fl<false, false>(rank, mode, kind);
 }
 
 // Dynamic LDS above the default per-launch limit is opted into once per
@@ -1707,9 +1718,9 @@ int prepare_kernels() {
   std::call_once(once, [] {
     for (int rank : {256, 512})
       for (int mode : {0, 1})
-        for (int kind = 0; kind < 5; ++kind)
-          for (bool fl : {false, true}) {
-          hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, kind, fl),
+        for (int kind = 0; kind < 4; ++kind)
+          for (int flags = 0; flags < 4; ++flags) {
+          hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, kind, flags & 1, flags & 2),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              kLaunchRows * (rank / 8 + 1) * 16);
           if (e != hipSuccess && err == hipSuccess) err = e;
@@ -1736,7 +1747,7 @@ int pick_grid(int rows, int rank, int mode, const Shape& sh, int* grid, bool* re
   if (g > 64 * kMaxPollPerLane) g = 64 * kMaxPollPerLane;
   const bool resident = (g == sh.NC);
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel_for(rank, mode, kernel_kind(rows, mode, resident), false),
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel_for(rank, mode, kernel_kind(rows, mode, resident), false, false),
                                                     kThreads, shmem);
   if (e != hipSuccess) return fail(MARKOV_E_HIP, "occupancy query: %s", hipGetErrorString(e));
   if (per_cu < 1) return fail(MARKOV_E_HIP, "the chain kernel does not fit on a compute unit");
@@ -1858,7 +1869,6 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_
     p.tok_rs = tokens_row_stride;
     p.cache = cache;
     p.cache_f32 = cache_f32;
-    p.noise_inline = noise_inline;
     p.cache_rs = cache_state_stride;
     p.cache_ss = cache_step_stride;
     p.cache_states = cache_states;
@@ -1867,15 +1877,7 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_
 
     void* args[] = {&p};
     const size_t shmem = (size_t)nr * (rank / 8 + 1) * 16;
-    // Inline noise: the one-row kernel has a variant that draws it with no
-    // flag reads; other kernels read the flag (FL).
-    int kind = kernel_kind(nr, mode, res);
-    bool fl = base_f32 || cache_f32;
-    if (noise_inline) {
-      if (kind == 3 && !fl) kind = 4;
-      else fl = true;
-    }
-    const void* kern = kernel_for(rank, mode, kind, fl);
+    const void* kern = kernel_for(rank, mode, kernel_kind(nr, mode, res), base_f32 || cache_f32, noise_inline);
     // A regular launch: the grid is at most one workgroup per CU and the
     // kernel's resources admit only one per CU, so on an otherwise idle
     // device every workgroup is resident at once; every cross-workgroup wait
