@@ -387,41 +387,57 @@ __device__ __forceinline__ void log_table_load(LogTable& t, int tid, int nthread
   }
 }
 
-// Gumbel noise of M consecutive vocabulary ids v0 .. v0 + M - 1 of one
-// (seed, row, step) prefix: -log(-log u) with both logs correctly rounded.
-// The M evaluations are independent (their fast paths interleave); the
-// rare library-log fallbacks run afterwards.
+// The uniforms of M consecutive vocabulary ids v0 .. v0 + M - 1 of one
+// (seed, row, step) prefix.
 template <int M>
-__device__ __forceinline__ void gumbel_noise(uint64_t prefix, int v0, const LogTable& t, float* g) {
-  float u[M];
+__device__ __forceinline__ void noise_uniforms(uint64_t prefix, int v0, float* u) {
+#pragma unroll
+  for (int j = 0; j < M; ++j) u[j] = hash_uniform(splitmix64(prefix ^ (uint64_t)(v0 + j)));
+}
+
+// Gumbel noise -log(-log u) of M uniforms, both logs correctly rounded.  The
+// M evaluations are independent (their fast paths interleave); the rare
+// library-log fallbacks run afterwards.
+template <int M>
+__device__ __forceinline__ void gumbel_from_uniforms(const float* u, const LogTable& t, float* g) {
+  float x[M];
   uint32_t bad = 0;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
-    u[j] = hash_uniform(splitmix64(prefix ^ (uint64_t)(v0 + j)));
+    x[j] = u[j];
     bool ok;
-    g[j] = log_f32_try(u[j], t, ok);
+    g[j] = log_f32_try(x[j], t, ok);
     bad |= (ok ? 0u : 1u) << j;
   }
   if (bad) {
 #pragma unroll
     for (int j = 0; j < M; ++j)
-      if ((bad >> j) & 1u) g[j] = log_f32_rn(u[j]);
+      if ((bad >> j) & 1u) g[j] = log_f32_rn(x[j]);
   }
   bad = 0;
 #pragma unroll
   for (int j = 0; j < M; ++j) {
-    u[j] = -g[j];  // -log u, positive
+    x[j] = -g[j];  // -log u, positive
     bool ok;
-    g[j] = log_f32_try(u[j], t, ok);
+    g[j] = log_f32_try(x[j], t, ok);
     bad |= (ok ? 0u : 1u) << j;
   }
   if (bad) {
 #pragma unroll
     for (int j = 0; j < M; ++j)
-      if ((bad >> j) & 1u) g[j] = log_f32_rn(u[j]);
+      if ((bad >> j) & 1u) g[j] = log_f32_rn(x[j]);
   }
 #pragma unroll
   for (int j = 0; j < M; ++j) g[j] = -g[j];
+}
+
+// Gumbel noise of M consecutive vocabulary ids v0 .. v0 + M - 1 of one
+// (seed, row, step) prefix.
+template <int M>
+__device__ __forceinline__ void gumbel_noise(uint64_t prefix, int v0, const LogTable& t, float* g) {
+  float u[M];
+  noise_uniforms<M>(prefix, v0, u);
+  gumbel_from_uniforms<M>(u, t, g);
 }
 
 // ============================================================== noise fill ==
@@ -433,12 +449,14 @@ __global__ __launch_bounds__(256) void noise_fill_kernel(float* __restrict__ gum
   const int rs = row * steps + step;
   __shared__ LogTable tab;
   log_table_load(tab, threadIdx.x, 256);
-  __syncthreads();
+  // the hashes while the table's loads are in flight
   const int v0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  float u[4];
+  noise_uniforms<4>(noise_prefix(seeds[row], row, step), v0, u);
+  __syncthreads();
   if (v0 >= V) return;  // V is a multiple of 16: a thread's 4 ids are all valid
-  const uint64_t prefix = noise_prefix(seeds[row], row, step);
   float out[4];
-  gumbel_noise<4>(prefix, v0, tab, out);
+  gumbel_from_uniforms<4>(u, tab, out);
   float4* dst = reinterpret_cast<float4*>(gumbel + (size_t)rs * V + v0);
   *dst = make_float4(out[0], out[1], out[2], out[3]);
 }
@@ -548,6 +566,20 @@ __device__ __forceinline__ uint4 load_head_tile(const uint16_t* __restrict__ hea
   const int row = g * (16384 / R) + 16 * t + (lane & 15);
   if (row >= V) return make_uint4(0, 0, 0, 0);
   return *reinterpret_cast<const uint4*>(head + (size_t)row * R + 32 * kt + 8 * (lane >> 4));
+}
+
+// The same tile with rows at or beyond V read from row V - 1 instead of set
+// to zero: one unconditional load, whose wait can be counted past later
+// loads.  The sums of those rows are never used (every epilogue checks
+// v < V), so their values do not matter.
+template <int R>
+__device__ __forceinline__ uint4 load_head_tile_clamped(const uint16_t* __restrict__ head, int g, int s,
+                                                        int lane, int V) {
+  constexpr int KT = R / 32;
+  const int t = s / KT, kt = s - (s / KT) * KT;
+  const int row = g * (16384 / R) + 16 * t + (lane & 15);
+  const int rc = row < V ? row : V - 1;
+  return *reinterpret_cast<const uint4*>(head + (size_t)rc * R + 32 * kt + 8 * (lane >> 4));
 }
 
 // Row stride (floats) of a wave's bias tile in LDS: RPG + 4 keeps the 16
@@ -693,20 +725,48 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   const bool lane_owns = (R == 256) || lane < 32;
 
   // ---- prologue: rows, parity, the resident head into VGPRs.
+  // The rows' data, the call parity and the noise's log table are loaded
+  // before the head: loads complete in order, so waiting for them does not
+  // wait for the head, which streams in while the prologue goes on.
+  // (Unconditional loads from clamped indices, so that the waits for them
+  // are counted past the head's loads.)
+  static_assert(kLaunchRows <= kThreads && kLogTable <= kThreads, "one prologue load per thread");
+  const int b_row = tid;
+  const bool row_thread = b_row < rows;
+  const int b_ld = row_thread ? b_row : 0;
+  const int64_t* st_src = p.state_idx ? p.state_idx : p.prev;
+  const int64_t r_sti = st_src[b_ld];
+  const int64_t r_tok = p.prev[b_ld];
+  const float r_T = p.temp[b_ld];
+  const int64_t r_seed = (MODE == 1 || nz_inline) ? p.seeds[b_ld] : 0;
+  const bool tab_thread = MODE == 0 && nz_inline && tid < kLogTable;
+  float t_c = 0.0f;
+  double t_nlc = 0.0;
+  if (MODE == 0 && nz_inline) {
+    const int k = tid < kLogTable ? tid : 0;
+    t_c = g_log_c[k];
+    t_nlc = g_log_nlc[k];
+  }
+  const uint32_t par = ld_agent32(header);
   uint4 h[kSlots];
   if constexpr (RES) {
     const int g0 = wg * kWaves + wave;  // this wave's group
 #pragma unroll
     for (int s = 0; s < kSlots; ++s)
-      h[s] = g0 < NG ? load_head_tile<R>(p.head, g0, s, lane, V) : make_uint4(0, 0, 0, 0);
+      h[s] = load_head_tile_clamped<R>(p.head, g0 < NG ? g0 : NG - 1, s, lane, V);
   }
   if (tid == 0) {
-    s_parity = ld_agent32(header);
+    s_parity = par;
     s_abort = 0;
   }
-  for (int b = tid; b < rows; b += kThreads) {
-    const int64_t st = p.state_idx ? p.state_idx[b] : p.row_base + b;
-    const int64_t tok = p.prev[b];
+  if (tab_thread) {
+    s_log.c[tid] = t_c;
+    s_log.nlc[tid] = t_nlc;
+  }
+  if (row_thread) {
+    const int b = b_row;
+    const int64_t st = p.state_idx ? r_sti : p.row_base + b_row;
+    const int64_t tok = r_tok;
     int active = st >= 0;
     if (active && st >= p.cache_states) {
       active = 0;
@@ -720,12 +780,14 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     }
     s_state[b] = (int)st;
     s_active[b] = active;
-    s_T[b] = p.temp[b];
-    if (MODE == 1 || nz_inline) s_seed[b] = p.seeds[b];
+    s_T[b] = r_T;
+    s_seed[b] = r_seed;
     s_tok[b] = active ? (int)tok : 0;
   }
-  if (MODE == 0 && nz_inline) log_table_load(s_log, tid, kThreads);
-  __syncthreads();
+  // An LDS-only barrier: the head's loads stay in flight.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   const uint32_t parity = s_parity & 1u;
   unsigned char* half = p.ws + kHeader + parity * p.ws_half;
   {
