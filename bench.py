@@ -1,11 +1,12 @@
 """Benchmark of the Markov draft-sampling chain on one MI355X.
 
-A step is one pass of the whole hot path over one batch: by default one
-launch of the persistent chain kernel that draws its Gumbel noise itself
-(MARKOV_NOISE_INLINE: the idle waves of each workgroup draw the next step's
-noise while the exchange is in flight); with --noise side, the noise fill
-kernel on a side stream (forked after the current stream's work and joined
-before the chain) and the chain reading it.  The default workload is
+A step is one pass of the whole hot path over one batch: for up to 8 rows
+(the default, --noise auto) one launch of the persistent chain kernel that
+draws its Gumbel noise itself (MARKOV_NOISE_INLINE: the idle waves of each
+workgroup draw the next step's noise while the exchange is in flight); for
+larger batches, or with --noise side, the noise fill kernel on a side stream
+(forked after the current stream's work and joined before the chain) and the
+chain reading it.  The default workload is
 the DeepSeek-V4.1-sized single request row: V=129280, r=256 (a 66 MB bf16
 head), rows=1, N=8 draft positions, T=0.7, synthetic inputs.
 
@@ -56,10 +57,9 @@ def kernel_source_digest() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def measured_traffic(noise: str):
-    """HBM-side bytes per chain launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel code with the same noise
-    placement (else None)."""
+def profile_fields(noise: str):
+    """The committed rocprofv3 counter summary's fields, if it was taken on
+    the current kernel code with the same noise placement (else None)."""
     try:
         text = open(TRAFFIC_PROFILE).read()
     except OSError:
@@ -69,7 +69,28 @@ def measured_traffic(noise: str):
         return None
     if fields.get("noise", "side").strip() != noise:
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return fields
+
+
+def measured_traffic(noise: str):
+    """HBM-side bytes per chain launch (FETCH_SIZE + WRITE_SIZE, calibrated)."""
+    f = profile_fields(noise)
+    return int(f["traffic_bytes_per_launch"]) if f else None
+
+
+def head_residency(w, inline: bool, noise: str):
+    """How much of the head traffic the resident head saves: without it every
+    one of the N steps reads the head; with it the head comes from beyond the
+    L2s (FETCH_SIZE, less the other algorithmic reads) about once per call."""
+    f = profile_fields(noise)
+    if not f or "fetch_bytes_per_launch" not in f:
+        return None
+    ab = algorithmic_bytes(w, inline)
+    other = ab["base"] + ab["noise"] + ab["embed"] + w.real_rows * 8
+    head_fetched = int(f["fetch_bytes_per_launch"]) - other
+    return {"head_bytes": ab["head"], "steps": w.N, "head_bytes_fetched_per_call": head_fetched,
+            "head_reads_per_call": head_fetched / ab["head"],
+            "on_chip_fraction": 1.0 - head_fetched / (w.N * ab["head"])}
 
 
 def algorithmic_bytes(w, inline: bool) -> dict:
@@ -210,9 +231,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="dsv41_single_row")
-    ap.add_argument("--noise", choices=("inline", "side"), default="inline",
+    ap.add_argument("--noise", choices=("auto", "inline", "side"), default="auto",
                     help="mode 0: noise drawn inside the chain kernel, or by the noise fill "
-                         "kernel on a side stream")
+                         "kernel on a side stream; auto: inline up to 8 rows (the chain's idle "
+                         "waves draw it), side stream beyond")
     ap.add_argument("--cold", type=int, default=50, help="cold calls timed after the main loop")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -323,7 +345,8 @@ def main() -> int:
         del src, dst
 
     w = synth.workload(args.workload)
-    inline = args.noise == "inline" and w.mode == 0
+    noise = args.noise if args.noise != "auto" else ("inline" if w.real_rows <= 8 else "side")
+    inline = noise == "inline" and w.mode == 0
     m = measure(w, args.steps, args.warmup, args.cold, inline)
     chain_ms, cold_ms, b2b_ms = m["chain_ms"], m["cold_ms"], m["b2b_ms"]
     tok_per_step = w.real_rows * w.N
@@ -365,9 +388,11 @@ def main() -> int:
                       "cold": ab["head"] / (cold_us_med * 1e-6) / 1e9 if cold_us_med else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(args.noise) if args.workload == "dsv41_single_row" else None,
+                     "traffic": measured_traffic(noise) if args.workload == "dsv41_single_row" else None,
                      "kernel": "chain_kernel", "bytes_per_launch": ab["total"]},
     }
+    if args.workload == "dsv41_single_row":
+        result["head_residency"] = head_residency(w, inline, noise)
     if cold_us_med:
         ach_c = ab["total"] / (cold_us_med * 1e-6) / 1e9
         result["roofline_cold"] = {"achieved": ach_c, "frac": ach_c / HBM_PEAK_GBPS}

@@ -97,6 +97,23 @@ def test_inline_r512_rows9():
     _same(w)
 
 
+@pytest.mark.parametrize("V,r,rows,N,T,grid", [
+    (16, 256, 1, 5, 1.0, 0),          # the smallest vocabulary: one group of one chunk
+    (4096 + 16, 512, 1, 6, 0.8, 0),   # r = 512, one row, ragged last group
+    (4096 + 16, 512, 1, 6, 0.8, 3),   # the same on a streamed head
+    (2048, 256, 1, 256, 1.3, 0),      # the most steps a call takes
+    (2048, 256, 2, 3, 0.0, 0),        # argmax rows draw no noise
+])
+def test_inline_edge_shapes(V, r, rows, N, T, grid):
+    w = synth.make(f"inl_edge_{V}_{r}_{rows}_{N}", V, r, rows, N, seed=96 + N, weights="int",
+                   base_std=2.0, temperature=np.full(rows, T, dtype=np.float32))
+    t, c = _same(w, grid)
+    g = oracle.noise_fill(w.seeds, w.N, w.V)
+    ref_t, ref_c = oracle.chain(w.base, w.head, w.embed, w.prev, w.temperature, w.seeds, gumbel=g)
+    assert np.array_equal(t, ref_t)
+    assert np.array_equal(c, ref_c)
+
+
 def test_inline_graph_replays():
     w = synth.make("inlg", 8192 + 16, 256, 1, 5, seed=94, weights="int", base_std=2.0)
     d = DeviceChain(w, noise_inline=True)
