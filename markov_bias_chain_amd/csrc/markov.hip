@@ -331,6 +331,16 @@ __device__ __forceinline__ void st_agent32(uint32_t* p, uint32_t v) {
 
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
+// c / T correctly rounded to fp32 (the IEEE quotient), as c times rT, the
+// fp64 reciprocal of T correctly rounded, rounded once to fp32.  For fp32 c
+// and T > 0 the fp64 product is within 2^-52 of c / T relatively, and a
+// quotient of two fp32 numbers is never within 2^-51 of its magnitude of an
+// fp32 rounding midpoint (c 2^j - M T, with M the midpoint's odd 25-bit
+// significand, is a nonzero integer), so both round the same way; T = +inf
+// gives 0 (or NaN for an infinite c) as the quotient does.  Three fp64/fp32
+// operations instead of the division's scale / reciprocal / fma / fixup.
+__device__ __forceinline__ float div_by_recip(float c, double rT) { return (float)((double)c * rT); }
+
 // The correctly rounded fp32 natural log: fp64 log of the fp32 argument,
 // rounded once (fp32 log libraries are only faithfully rounded).
 __device__ __noinline__ float log_f32_rn(float x) { return (float)log((double)x); }
@@ -697,6 +707,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   __shared__ int s_state[kLaunchRows];
   __shared__ int s_active[kLaunchRows];
   __shared__ float s_T[kLaunchRows];
+  __shared__ double s_rT[kLaunchRows];  // RN64(1 / T) of the rows with T > 0
   __shared__ int64_t s_seed[kLaunchRows];  // mode 1: the rows' seeds
   __shared__ int s_tok[kLaunchRows];
   __shared__ int s_need[kLaunchRows];
@@ -781,6 +792,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     s_state[b] = (int)st;
     s_active[b] = active;
     s_T[b] = r_T;
+    s_rT[b] = r_T > 0.0f ? 1.0 / (double)r_T : 0.0;
     s_seed[b] = r_seed;
     s_tok[b] = active ? (int)tok : 0;
   }
@@ -979,6 +991,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     const int v0 = g * RPG + q * IPL;
     const bool ok = rr < nb && g < NG && v0 < V && s_active[b];
     const float T = s_T[b];
+    const double rT = s_rT[b];
     float bsum[IPL];
 #pragma unroll
     for (int e4 = 0; e4 < IPL / 4; ++e4) {
@@ -1026,7 +1039,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     // Scores: T <= 0 is argmax; c / 1 is exact.
     if (T > 0.0f && T != 1.0f) {
 #pragma unroll
-      for (int e = 0; e < IPL; ++e) z[e] = __fdiv_rn(z[e], T);
+      for (int e = 0; e < IPL; ++e) z[e] = div_by_recip(z[e], rT);
     }
     if (MODE == 0 && T > 0.0f) {
       if (!SMALL && nz_inline && ok) {
@@ -1125,7 +1138,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             z = bf16_to_f32(cb);
           }
           if (T > 0.0f) {
-            if (T != 1.0f) z = __fdiv_rn(z, T);  // c / 1 is exact
+            if (T != 1.0f) z = div_by_recip(z, s_rT[0]);  // c / 1 is exact
             z = __fadd_rn(z, one_noise);
           }
           ord = score_ord(z);
@@ -1586,6 +1599,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           const int o = (int)(d >> 32) - 1;
           const float tl = __uint_as_float((uint32_t)d);
           const float T = s_T[b];
+          const double rT = s_rT[b];
           constexpr int PER = CHUNK / 64;  // ids per lane
           const int v0 = o * CHUNK + lane * PER;
           const long long at = (long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss + v0;
@@ -1620,7 +1634,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
 #pragma unroll
           for (int k = 0; k < PER; ++k) {
             const float c = __uint_as_float(cw[k]);
-            z[k] = v0 < V ? (T != 1.0f ? __fdiv_rn(c, T) : c) : -INFINITY;
+            z[k] = v0 < V ? (T != 1.0f ? div_by_recip(c, rT) : c) : -INFINITY;
             m = fmaxf(m, z[k]);
           }
           m = order_key_inv(wave_imax(order_key(m)));  // chunk maximum (no NaN: the decision excludes it)
