@@ -1227,10 +1227,16 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   {
     // The step loop: local work, publication, then the exchange of the
     // step (its tail overlaps the fetch of the next embedding).
+    // Inverse CDF: a wave that leads a row (H2 below) stages its next base
+    // logits after its decisions, not before: the leaders' polls would
+    // otherwise wait behind the staging loads (loads complete in order).
+    bool leader_wave = false;
+    if constexpr (MODE == 1)
+      for (int b = wg; b < rows; b += G) leader_wave = leader_wave || (((b / G) % kWaves) == wave && s_active[b]);
     for (int i = 0; i < N; ++i) {
       local_work(i);
       if (MODE == 1 && ahead && i + 1 < N) prefetch(i + 1);
-      if (stage && !base_f32 && i + 1 < N) {
+      if (stage && !base_f32 && i + 1 < N && !leader_wave) {
         // Parked at once: the wait for the loads overlaps the wait for the
         // other workgroups' partials.
         stage_load(i + 1);
@@ -1563,6 +1569,10 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           }
           if (lane == 0) st_agent(L.dec + (size_t)i * rows + b, dec);
         }
+        if (stage && !base_f32 && i + 1 < N && leader_wave) {
+          stage_load(i + 1);
+          stage_park();
+        }
         // H3: every workgroup reads every row's decision; wave w serves rows
         // w + 8 j, lane j polls row w + 8 j, all at once.
         {
@@ -1690,13 +1700,30 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       // ---- the winners: tokens out, next embeddings in.
       write_tokens(i);
       if (MODE == 1 && i + 1 < N) {
-        for (int k = tid; k < rows * KSEG; k += kThreads) {
-          const int b = k / KSEG, seg = k - b * KSEG;
-          if (s_active[b]) {
-            // A winner is always a valid id; the clamp only keeps the gather in
-            // bounds should that ever fail.
-            const uint32_t t = (uint32_t)s_tok[b] < (uint32_t)V ? (uint32_t)s_tok[b] : 0u;
-            s_e[b * ES + seg] = *reinterpret_cast<const uint4*>(p.embed + (size_t)t * R + seg * 8);
+        // The next embeddings: every load of a batch is issued before any is
+        // stored (one round trip per batch, not per row).
+        constexpr int kEmbPer = kLaunchRows * (R / 8) / kThreads;  // 16-byte pieces per thread: 4 or 8
+        constexpr int kEmbBatch = 2;
+#pragma unroll 1
+        for (int j0 = 0; j0 < kEmbPer; j0 += kEmbBatch) {
+          uint4 ev[kEmbBatch];
+#pragma unroll
+          for (int j = 0; j < kEmbBatch; ++j) {
+            const int k = tid + (j0 + j) * kThreads;
+            const int b = k / KSEG, seg = k - b * KSEG;
+            ev[j] = make_uint4(0, 0, 0, 0);
+            if (k < rows * KSEG && s_active[b]) {
+              // A winner is always a valid id; the clamp only keeps the
+              // gather in bounds should that ever fail.
+              const uint32_t t = (uint32_t)s_tok[b] < (uint32_t)V ? (uint32_t)s_tok[b] : 0u;
+              ev[j] = *reinterpret_cast<const uint4*>(p.embed + (size_t)t * R + seg * 8);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < kEmbBatch; ++j) {
+            const int k = tid + (j0 + j) * kThreads;
+            const int b = k / KSEG, seg = k - b * KSEG;
+            if (k < rows * KSEG && s_active[b]) s_e[b * ES + seg] = ev[j];
           }
         }
         __syncthreads();
