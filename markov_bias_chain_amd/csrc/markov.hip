@@ -79,6 +79,8 @@ constexpr int kHeader = 256;               // workspace header bytes
 constexpr int kModeFlags = MARKOV_BASE_F32 | MARKOV_CACHE_F32 | MARKOV_NOISE_INLINE;  // flag bits of `mode`
 constexpr int kMaxPollPerLane = 16;        // slots one lane polls (<= 1024 per row)
 constexpr int kLeaderRegs = 4;             // inverse-CDF chunks per lane kept in registers by a leader
+constexpr int kPartCopies = 16;            // one row: copies of each step's reducer partials
+constexpr int kPartStride = 64;            // u64 words from one copy to the next (512 bytes)
 constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz
 
 // ----------------------------------------------------------- bf16 helpers --
@@ -493,8 +495,11 @@ struct ChainParams {
 // most once per call, and 0 means "not written yet"):
 //   keys [N][rows][NC] u64     candidate keys (mode 0: one per workgroup,
 //                               mode 1: one per chunk)
-//   mode 0:
+//   mode 0, more than one row:
 //   part [N][rows][NR] u64     reducer r's maximum over slots 64 r .. 64 r + 63
+//   mode 0, one row (when there are reducers):
+//   part [N][kPartCopies][kPartStride] u64   reducer r's maximum in word r of
+//                               every copy; workgroup g polls copy g % kPartCopies
 //   mode 1:
 //   dec  [N][rows]     u64     the leader's decision for the row
 //   tok  [N][rows]     u64     the owner's token for the row
@@ -516,10 +521,26 @@ __host__ __device__ inline size_t half_bytes_needed(int rows, int N, int NC, int
   size_t b = slots * 8;
   if (mode == 1) {
     b += (size_t)N * rows * 16 + slots * 4;
+  } else if (rows == 1 && reducers_for(NC) > 1) {
+    b += (size_t)N * kPartCopies * kPartStride * 8;
   } else {
     b += (size_t)N * rows * reducers_for(NC) * 8;
   }
   return (b + 255) & ~(size_t)255;
+}
+
+// A call of more than kLaunchRows rows runs as launches of kLaunchRows rows
+// and one of the rest, one after another in the same workspace: its half
+// must hold the larger of their layouts.
+__host__ inline size_t call_half_bytes(int rows, int N, int NC, int mode) {
+  const int full = rows < kLaunchRows ? rows : kLaunchRows;
+  size_t b = half_bytes_needed(full, N, NC, mode);
+  const int tail = rows % kLaunchRows;
+  if (rows > kLaunchRows && tail != 0) {
+    const size_t t = half_bytes_needed(tail, N, NC, mode);
+    if (t > b) b = t;
+  }
+  return b;
 }
 
 __device__ inline HalfLayout half_layout(unsigned char* half, int rows, int N, int NC, int mode) {
@@ -751,6 +772,15 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     t_nlc = g_log_nlc[k];
   }
   const uint32_t par = ld_agent32(header);
+  // One row: the step-0 base logit (bf16 bits) of this lane's vocabulary id;
+  // its first use comes after the head is issued, so its wait does not wait
+  // for the head.  (Shifted where it was loaded, it held the step-0 noise
+  // draw back until the whole head had arrived.)
+  uint32_t b0_bits = 0;
+  if constexpr (ONE && !FL) {
+    const int v = (wg * kWaves + wave) * RPG + lr;
+    b0_bits = reinterpret_cast<const uint16_t*>(p.base)[v < V ? v : V - 1];
+  }
   uint4 h[kSlots];
   if constexpr (RES) {
     const int g0 = wg * kWaves + wave;  // this wave's group
@@ -828,8 +858,11 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     if (s_active[0] && own_res) {
       // the base logit as fp32 bits (a bf16 value widened)
       const long long at = (long long)i * p.base_ss + v_res;
-      one_base = base_f32 ? reinterpret_cast<const uint32_t*>(p.base)[at]
-                            : (uint32_t)reinterpret_cast<const uint16_t*>(p.base)[at] << 16;
+      if (!FL && i == 0)
+        one_base = b0_bits << 16;
+      else
+        one_base = base_f32 ? reinterpret_cast<const uint32_t*>(p.base)[at]
+                              : (uint32_t)reinterpret_cast<const uint16_t*>(p.base)[at] << 16;
       if (MODE == 0 && s_T[0] > 0.0f && !one_nz) one_noise = p.gumbel[(size_t)i * V + v_res];
     }
     if (one_nz && (wave != 0 || i == 0)) draw_one(i);
@@ -1352,7 +1385,6 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // (Measured: one row 43.7 -> 41.0 us per call; several rows, whose
         // reducers each serve every row, were slower than all-to-all.)
         const int NR = rows == 1 ? reducers_for(G) : 1;
-        const int NRS = reducers_for(NC);  // the part arrays' row stride
         if (!many && NR > 1 && wg < NR) {
           for (int b = wave; b < rows; b += kWaves) {
             if (!s_active[b]) continue;
@@ -1369,12 +1401,15 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
               __builtin_amdgcn_s_sleep(1);
             }
             const uint64_t K = wave_max_u64(x == 0 ? kNoCandidate : x);
-            if (lane == 0) st_agent(L.part + ((size_t)i * rows + b) * NRS + wg, K);
+            // Every copy gets it: each copy's line is polled by G / kPartCopies
+            // workgroups instead of all G.
+            if (lane < kPartCopies) st_agent(L.part + ((size_t)i * kPartCopies + lane) * kPartStride + wg, K);
           }
         }
         for (int b = many ? rows : wave; b < rows; b += kWaves) {
           if (!s_active[b]) continue;
-          const uint64_t* slots = NR > 1 ? L.part + ((size_t)i * rows + b) * NRS : L.keys + ((size_t)i * rows + b) * NC;
+          const uint64_t* slots = NR > 1 ? L.part + ((size_t)i * kPartCopies + wg % kPartCopies) * kPartStride
+                                         : L.keys + ((size_t)i * rows + b) * NC;
           const int n = NR > 1 ? NR : G;  // words polled: partials or slots
           const bool next = i + 1 < N;
           uint64_t best = kNoCandidate;
@@ -1859,7 +1894,7 @@ size_t markov_workspace_bytes(int rows, int steps, int vocab, int rank, int mode
   mode &= ~kModeFlags;
   Shape sh;
   if (check_shape(rows, steps, vocab, rank, mode, &sh) != MARKOV_OK) return 0;
-  return kHeader + 2 * half_bytes_needed(rows < kLaunchRows ? rows : kLaunchRows, steps, sh.NC, mode);
+  return kHeader + 2 * call_half_bytes(rows, steps, sh.NC, mode);
 }
 
 int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps, int vocab,
@@ -1923,8 +1958,7 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_
   // Calls with more rows than one launch takes run as consecutive launches
   // of at most kLaunchRows rows on the stream (each reads the head once);
   // they use the workspace one after another.
-  const int lrows = rows < kLaunchRows ? rows : kLaunchRows;
-  const size_t need = kHeader + 2 * half_bytes_needed(lrows, steps, sh.NC, mode);
+  const size_t need = kHeader + 2 * call_half_bytes(rows, steps, sh.NC, mode);
   if (workspace_bytes < need)
     return fail(MARKOV_E_INVAL, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
   rc = prepare_kernels();

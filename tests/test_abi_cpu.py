@@ -32,11 +32,15 @@ def test_library_exports_every_declared_symbol():
 def test_workspace_bytes():
     # header + two halves; mode 0: an 8-byte key per (step, row, chunk) and an
     # 8-byte reducer partial per (step, row, 64 chunks) (512-id chunks at
-    # r=256)
+    # r=256); one row keeps 16 copies of each step's partials, 512 bytes apart
     chunks = -(-129280 // 512)
     red = -(-chunks // 64)
-    half = -(-(8 * 1 * chunks * 8 + 8 * 1 * red * 8) // 256) * 256
+    half = -(-(8 * 1 * chunks * 8 + 8 * 16 * 64 * 8) // 256) * 256
     assert lm.markov_workspace_bytes(1, 8, 129280, 256, 0) == 256 + 2 * half
+    # one row without reducers (at most 64 chunks): one partial word per step, no copies
+    assert lm.markov_workspace_bytes(1, 8, 4096, 256, 0) == 256 + 2 * (-(-(8 * 8 * 8 + 8 * 8) // 256) * 256)
+    # more than 64 rows: launches of 64 rows and of the rest share the workspace
+    assert lm.markov_workspace_bytes(65, 8, 129280, 256, 0) == lm.markov_workspace_bytes(64, 8, 129280, 256, 0)
     half9 = -(-(8 * 9 * chunks * 8 + 8 * 9 * red * 8) // 256) * 256
     assert lm.markov_workspace_bytes(9, 8, 129280, 256, 0) == 256 + 2 * half9
     # mode 1 adds 4-byte sums and two 8-byte words per (step, row), no partials
