@@ -1384,7 +1384,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // partials instead of all G slots, which keeps the polled lines few.
         // (Measured: one row 43.7 -> 41.0 us per call; several rows, whose
         // reducers each serve every row, were slower than all-to-all.)
-        const int NR = rows == 1 ? reducers_for(G) : 1;
+        // (The resident many-row kernel never runs one row.)
+        const int NR = (rows == 1 && (SMALL || !RES)) ? reducers_for(G) : 1;
         if (!many && NR > 1 && wg < NR) {
           for (int b = wave; b < rows; b += kWaves) {
             if (!s_active[b]) continue;
