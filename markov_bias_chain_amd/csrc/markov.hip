@@ -42,10 +42,11 @@
 //    all slots, so there is no contended atomic and no second flag.  A zero
 //    slot means "not arrived"; real keys are never zero.  Alternate calls use
 //    alternate halves of the workspace and each call clears the half the
-//    next call will use, so no reset launch is needed.  A single row on more
-//    than 64 workgroups exchanges in two levels (4 reducer workgroups, whose
-//    partials everyone polls).  While polling, each wave fetches the
-//    embedding of the best key seen so far.
+//    next call will use, so no reset launch is needed.  A single row (or up
+//    to 8 rows on a streamed head) on more than 64 workgroups exchanges in
+//    two levels: 4 reducer workgroups write their partials into 16 copies,
+//    each polled by a sixteenth of the workgroups.  While polling, each wave
+//    fetches the embedding of the best key seen so far.
 //  * Mode 1 (inverse CDF) publishes per-chunk (max key, sum of exp) partials;
 //    a leader workgroup per row locates the chunk holding u * S, the chunk's
 //    owner scans it in vocabulary order and publishes the token.
@@ -79,7 +80,7 @@ constexpr int kHeader = 256;               // workspace header bytes
 constexpr int kModeFlags = MARKOV_BASE_F32 | MARKOV_CACHE_F32 | MARKOV_NOISE_INLINE;  // flag bits of `mode`
 constexpr int kMaxPollPerLane = 16;        // slots one lane polls (<= 1024 per row)
 constexpr int kLeaderRegs = 4;             // inverse-CDF chunks per lane kept in registers by a leader
-constexpr int kPartCopies = 16;            // one row: copies of each step's reducer partials
+constexpr int kPartCopies = 16;            // <= kWaves rows: copies of each step's reducer partials
 constexpr int kPartStride = 64;            // u64 words from one copy to the next (512 bytes)
 constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz
 
@@ -495,11 +496,12 @@ struct ChainParams {
 // most once per call, and 0 means "not written yet"):
 //   keys [N][rows][NC] u64     candidate keys (mode 0: one per workgroup,
 //                               mode 1: one per chunk)
-//   mode 0, more than one row:
+//   mode 0, more than kWaves rows:
 //   part [N][rows][NR] u64     reducer r's maximum over slots 64 r .. 64 r + 63
-//   mode 0, one row (when there are reducers):
-//   part [N][kPartCopies][kPartStride] u64   reducer r's maximum in word r of
-//                               every copy; workgroup g polls copy g % kPartCopies
+//   mode 0, at most kWaves rows (when there are reducers):
+//   part [N][rows][kPartCopies][kPartStride] u64   reducer r's maximum in
+//                               word r of every copy; workgroup g polls copy
+//                               g % kPartCopies
 //   mode 1:
 //   dec  [N][rows]     u64     the leader's decision for the row
 //   tok  [N][rows]     u64     the owner's token for the row
@@ -515,14 +517,16 @@ struct HalfLayout {
 
 // Reducer workgroups of the two-level mode-0 exchange (slots per reducer: 64).
 __host__ __device__ inline int reducers_for(int NC) { return (NC + 63) / 64; }
+// Whether the partials of a launch of `rows` rows are kept in copies.
+__host__ __device__ inline bool copied_parts(int rows, int NC) { return rows <= kWaves && reducers_for(NC) > 1; }
 
 __host__ __device__ inline size_t half_bytes_needed(int rows, int N, int NC, int mode) {
   const size_t slots = (size_t)N * rows * NC;
   size_t b = slots * 8;
   if (mode == 1) {
     b += (size_t)N * rows * 16 + slots * 4;
-  } else if (rows == 1 && reducers_for(NC) > 1) {
-    b += (size_t)N * kPartCopies * kPartStride * 8;
+  } else if (copied_parts(rows, NC)) {
+    b += (size_t)N * rows * kPartCopies * kPartStride * 8;
   } else {
     b += (size_t)N * rows * reducers_for(NC) * 8;
   }
@@ -1378,14 +1382,17 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             }
           }
         }
-        // A single row with more than 64 workgroups exchanges in two levels:
-        // reducer r (workgroup r < NR) waits for slots 64 r .. 64 r + 63 and
-        // publishes their maximum; every workgroup then polls the NR
-        // partials instead of all G slots, which keeps the polled lines few.
-        // (Measured: one row 43.7 -> 41.0 us per call; several rows, whose
-        // reducers each serve every row, were slower than all-to-all.)
-        // (The resident many-row kernel never runs one row.)
-        const int NR = (rows == 1 && (SMALL || !RES)) ? reducers_for(G) : 1;
+        // One row, or at most kWaves rows on a streamed head, with more than
+        // 64 workgroups exchange in two levels: wave b of reducer r
+        // (workgroup r < NR) waits for row b's slots 64 r .. 64 r + 63 and
+        // publishes their maximum into every copy of the row's partials;
+        // wave b of every workgroup then polls the NR partials of its own
+        // copy instead of all G slots, which keeps the polled lines few and
+        // each polled by G / kPartCopies workgroups.  (Measured per call: one
+        // row 41.5 -> 40.0 us, r = 512 streamed with 8 rows 756 -> 741 us;
+        // resident 8 rows 54.0 -> 57.6 us, so the resident kernels of 2 to 8
+        // rows keep the all-to-all and do not compile this path.)
+        const int NR = (RES ? ONE : rows <= kWaves) ? reducers_for(G) : 1;
         if (!many && NR > 1 && wg < NR) {
           for (int b = wave; b < rows; b += kWaves) {
             if (!s_active[b]) continue;
@@ -1402,14 +1409,13 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
               __builtin_amdgcn_s_sleep(1);
             }
             const uint64_t K = wave_max_u64(x == 0 ? kNoCandidate : x);
-            // Every copy gets it: each copy's line is polled by G / kPartCopies
-            // workgroups instead of all G.
-            if (lane < kPartCopies) st_agent(L.part + ((size_t)i * kPartCopies + lane) * kPartStride + wg, K);
+            if (lane < kPartCopies)
+              st_agent(L.part + (((size_t)i * rows + b) * kPartCopies + lane) * kPartStride + wg, K);
           }
         }
         for (int b = many ? rows : wave; b < rows; b += kWaves) {
           if (!s_active[b]) continue;
-          const uint64_t* slots = NR > 1 ? L.part + ((size_t)i * kPartCopies + wg % kPartCopies) * kPartStride
+          const uint64_t* slots = NR > 1 ? L.part + (((size_t)i * rows + b) * kPartCopies + wg % kPartCopies) * kPartStride
                                          : L.keys + ((size_t)i * rows + b) * NC;
           const int n = NR > 1 ? NR : G;  // words polled: partials or slots
           const bool next = i + 1 < N;

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 def test_workspace_bytes():
     # header + two halves; mode 0: an 8-byte key per (step, row, chunk) and an
     # 8-byte reducer partial per (step, row, 64 chunks) (512-id chunks at
-    # r=256); one row keeps 16 copies of each step's partials, 512 bytes apart
+    # r=256); up to 8 rows keep 16 copies of each step's partials, 512 bytes apart
     chunks = -(-129280 // 512)
     red = -(-chunks // 64)
     half = -(-(8 * 1 * chunks * 8 + 8 * 16 * 64 * 8) // 256) * 256
@@ -48,7 +48,7 @@ def test_workspace_bytes():
     assert lm.markov_workspace_bytes(64, 8, 129280, 256, 1) == 256 + 2 * half1
     # r=512 chunks hold 256 ids
     c5 = 262144 // 256
-    half5 = -(-(16 * 8 * c5 * 8 + 16 * 8 * (c5 // 64) * 8) // 256) * 256
+    half5 = -(-(16 * 8 * c5 * 8 + 16 * 8 * 16 * 64 * 8) // 256) * 256  # <= 8 rows: partial copies
     assert lm.markov_workspace_bytes(8, 16, 262144, 512, 0) == 256 + 2 * half5
 
 
