@@ -114,6 +114,31 @@ def test_inline_edge_shapes(V, r, rows, N, T, grid):
     assert np.array_equal(c, ref_c)
 
 
+@pytest.mark.parametrize("V,r,rows,N", [
+    (8192 + 16, 256, 8, 10),   # 8 rows (one T = 0), more steps than the named workload
+    (8192 + 16, 512, 3, 14),   # r = 512, a prefetched batch of 3 rows
+    (4096 + 16, 256, 1, 53),   # one row, many steps
+])
+def test_inline_noise_batches_and_steps(V, r, rows, N):
+    # Inline draws must give the side-stream kernel's values and, on
+    # integer weights, the oracle's tokens and cache.
+    w = synth.make(f"inl_ahead_{r}_{rows}_{N}", V, r, rows, N, seed=97 + N, weights="int", base_std=2.0,
+                   temperature=np.array([1.0, 0.6, 0.0, 1.5, 1.0, 0.8, 1.2, 0.9][:rows], dtype=np.float32))
+    t, c = _same(w)
+    g = oracle.noise_fill(w.seeds, w.N, w.V)
+    ref_t, ref_c = oracle.chain(w.base, w.head, w.embed, w.prev, w.temperature, w.seeds, gumbel=g)
+    assert np.array_equal(t, ref_t)
+    assert np.array_equal(c, ref_c)
+
+
+@pytest.mark.parametrize("rows", [1, 3])
+def test_inline_noise_fp32_dtypes(rows):
+    # The flag-reading kernels (fp32 base logits and cache) draw inline too.
+    w = synth.make(f"inl_f32_{rows}", 8192 + 16, 256, rows, 9, seed=98 + rows, base_f32=True, cache_f32=True,
+                   temperature=np.array([0.9, 1.1, 0.0][:rows], dtype=np.float32))
+    _same(w)
+
+
 def test_inline_graph_replays():
     w = synth.make("inlg", 8192 + 16, 256, 1, 5, seed=94, weights="int", base_std=2.0)
     d = DeviceChain(w, noise_inline=True)
