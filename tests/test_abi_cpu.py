@@ -43,8 +43,9 @@ def test_workspace_bytes():
     assert lm.markov_workspace_bytes(65, 8, 129280, 256, 0) == lm.markov_workspace_bytes(64, 8, 129280, 256, 0)
     half9 = -(-(8 * 9 * chunks * 8 + 8 * 9 * red * 8) // 256) * 256
     assert lm.markov_workspace_bytes(9, 8, 129280, 256, 0) == 256 + 2 * half9
-    # mode 1 adds 4-byte sums and two 8-byte words per (step, row), no partials
-    half1 = -(-(8 * 64 * chunks * 12 + 8 * 64 * 16) // 256) * 256
+    # mode 1 adds 4-byte sums and two 8-byte words per (step, row), each in
+    # 16 copies, no partials
+    half1 = -(-(8 * 64 * chunks * 12 + 8 * 16 * 64 * 16) // 256) * 256
     assert lm.markov_workspace_bytes(64, 8, 129280, 256, 1) == 256 + 2 * half1
     # r=512 chunks hold 256 ids
     c5 = 262144 // 256
