@@ -107,84 +107,12 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
-// ------------------------------------------------------- lane exchanges --
-// xor-partner exchanges within a wave64, on the cheapest path for each
-// distance: DPP quad permutes (1, 2), DPP row rotate by 8 (= xor 8 inside a
-// 16-lane row), ds_swizzle bit-mask mode (4, 16), ds_bpermute (32).
-
-__device__ __forceinline__ int xsh1(int v) { return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false); }
-__device__ __forceinline__ int xsh2(int v) { return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false); }
-__device__ __forceinline__ int xsh4(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x101F); }
-__device__ __forceinline__ int xsh8(int v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); }
-__device__ __forceinline__ int xsh16(int v) { return __builtin_amdgcn_ds_swizzle(v, 0x401F); }
-__device__ __forceinline__ int xsh32(int v) { return __shfl_xor(v, 32); }
-
-template <int M>
-__device__ __forceinline__ float xshf(float x) {
-  int v = __float_as_int(x);
-  if constexpr (M == 1) v = xsh1(v);
-  else if constexpr (M == 2) v = xsh2(v);
-  else if constexpr (M == 4) v = xsh4(v);
-  else if constexpr (M == 8) v = xsh8(v);
-  else if constexpr (M == 16) v = xsh16(v);
-  else v = xsh32(v);
-  return __int_as_float(v);
-}
-
-template <int M>
-__device__ __forceinline__ uint64_t xshk(uint64_t k) {
-  int lo = (int)(uint32_t)k, hi = (int)(uint32_t)(k >> 32);
-  if constexpr (M == 1) { lo = xsh1(lo); hi = xsh1(hi); }
-  else if constexpr (M == 2) { lo = xsh2(lo); hi = xsh2(hi); }
-  else if constexpr (M == 4) { lo = xsh4(lo); hi = xsh4(hi); }
-  else if constexpr (M == 8) { lo = xsh8(lo); hi = xsh8(hi); }
-  else if constexpr (M == 16) { lo = xsh16(lo); hi = xsh16(hi); }
-  else { lo = xsh32(lo); hi = xsh32(hi); }
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
-  k = umax64(k, xshk<1>(k));
-  k = umax64(k, xshk<2>(k));
-  k = umax64(k, xshk<4>(k));
-  k = umax64(k, xshk<8>(k));
-  k = umax64(k, xshk<16>(k));
-  k = umax64(k, xshk<32>(k));
-  return k;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-  x += xshf<1>(x);
-  x += xshf<2>(x);
-  x += xshf<4>(x);
-  x += xshf<8>(x);
-  x += xshf<16>(x);
-  x += xshf<32>(x);
-  return x;
-}
 
 // Reductions over a whole wave on the DPP/readlane path (no LDS-latency
 // swizzles): fold within each 16-lane row with quad permutes and row
 // mirrors, then combine the four rows' lanes 0, 16, 32, 48 through scalars.
 // Each result is the same value in every lane.
-__device__ __forceinline__ float row_fold_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));
-  return x;
-}
-__device__ __forceinline__ float lanes_0_16_32_48_sum(float x) {
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
-  return (a + b) + (c + d);
-}
-__device__ __forceinline__ float wave_sum_fast(float x) { return lanes_0_16_32_48_sum(row_fold_sum(x)); }
-
 __device__ __forceinline__ uint32_t row_fold_umax(uint32_t x) {
   x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));
   x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));
