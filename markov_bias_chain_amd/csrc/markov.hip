@@ -1420,6 +1420,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           uint32_t sc[kLeaderRegs];
 #pragma unroll
           for (int k = 0; k < kLeaderRegs; ++k) kc[k] = 0, sc[k] = 0;
+          // The row's uniform depends on no partial: drawn before the wait.
+          const float u = hash_uniform(noise_prefix(s_seed[b], p.row_base + b, i));
           // Slot k of this lane: (key, sum bits), 0 where the chunk does not exist.
           auto slot = [&](int k, uint64_t& key, uint32_t& sum) {
             const int c = lane * KPL + k;
@@ -1486,22 +1488,40 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
               e = expf(mc - M);
               return __uint_as_float(sum & 0x7FFFFFFFu) * e;
             };
+            // (With the slots in registers the weights are kept for the
+            // search below instead of being computed twice.)
+            float wk[kLeaderRegs], ek[kLeaderRegs];
             float lsum = 0.0f;
-            for (int k = 0; k < KPL; ++k) {
-              float e;
-              lsum += weight(k, e);
+            if (regs) {
+#pragma unroll
+              for (int k = 0; k < kLeaderRegs; ++k) {
+                ek[k] = 0.0f;
+                wk[k] = k < KPL ? weight(k, ek[k]) : 0.0f;
+                if (k < KPL) lsum += wk[k];
+              }
+            } else {
+              for (int k = 0; k < KPL; ++k) {
+                float e;
+                lsum += weight(k, e);
+              }
             }
             const float incl = wave_incl_scan(lsum);
             const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
-            const float t = hash_uniform(noise_prefix(s_seed[b], p.row_base + b, i)) * total;
+            const float t = u * total;
             // First chunk whose inclusive prefix exceeds t (else the last
             // chunk with weight, when rounding left none above t).
             int found = -1, last_pos = -1;
             float before = 0.0f, wfound = 0.0f, last_before = 0.0f, last_w = 0.0f;
             float run = incl - lsum;
             for (int k = 0; k < KPL; ++k) {
-              float e;
-              const float w = weight(k, e);
+              float e, w;
+              if (regs) {
+#pragma unroll
+                for (int r2 = 0; r2 < kLeaderRegs; ++r2)
+                  if (r2 == k) w = wk[r2], e = ek[r2];
+              } else {
+                w = weight(k, e);
+              }
               const int c = lane * KPL + k;
               if (found < 0 && run + w > t) {
                 found = c;
