@@ -945,7 +945,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // store (one vector per lane), score; then per row the best (score, id)
   // key of the wave's group and, in mode 1, the group's sum of exp(z - max).
   // sbt is the wave's bias tile row block of the batch (row rr at rr * BS).
-  auto epilogue_rows = [&](int i, int b0, int nb, int g, const float* sbt, const LaneIn& in) {
+  auto epilogue_rows = [&](int i, int b0, int nb, int g, const float* sbt, const LaneIn& in, bool nz_ready) {
     const int b = b0 + rr;
     const int v0 = g * RPG + q * IPL;
     const bool ok = rr < nb && g < NG && v0 < V && s_active[b];
@@ -1001,7 +1001,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       for (int e = 0; e < IPL; ++e) z[e] = div_by_recip(z[e], rT);
     }
     if (MODE == 0 && T > 0.0f) {
-      if (!SMALL && nz_inline && ok) {
+      if (!SMALL && nz_inline && ok && !nz_ready) {
         const uint64_t pre = noise_prefix(s_seed[b], p.row_base + b, i);
 #pragma unroll
         for (int e = 0; e < IPL; e += 2) {
@@ -1117,6 +1117,20 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       // (staged base logits hold bf16 only; fp32 ones are loaded per batch)
       const bool staged = stage && !base_f32;
       if (!ahead && !staged) load_rows(i, 0, g, cur);
+      // Streamed head, inline noise: the first batch's noise is drawn here,
+      // while the group's head tiles are still arriving, not in the epilogue.
+      bool nz0 = false;
+      if constexpr (!RES && MODE == 0) {
+        if (nz_inline) {
+          const int b = rr, v0 = g * RPG + q * IPL;
+          if (b < rows && g < NG && v0 < V && s_active[b] && s_T[b] > 0.0f) {
+            const uint64_t pk = noise_prefix(s_seed[b], p.row_base + b, i);
+#pragma unroll
+            for (int e = 0; e < IPL; e += 4) gumbel_noise<4>(pk, v0 + e, s_log, cur.nz + e);
+          }
+          nz0 = true;
+        }
+      }
       for (int t = 0; t < nbat; ++t) {
         const int b0 = t * kBatch;
         if ((t & 1) == 0) {
@@ -1125,13 +1139,13 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         }
         const int nb = rows - b0 < kBatch ? rows - b0 : kBatch;
         if constexpr (ahead) {
-          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, pre);
+          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, pre, false);
         } else if (staged) {
           stage_fetch(t, cur);
-          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur);
+          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur, false);
         } else {
           if (t + 1 < nbat) load_rows(i, b0 + kBatch, g, nxt);
-          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur);
+          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur, t == 0 && nz0);
           cur = nxt;
         }
       }
