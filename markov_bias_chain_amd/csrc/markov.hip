@@ -49,7 +49,8 @@
 //    fetches the embedding of the best key seen so far.
 //  * Mode 1 (inverse CDF) publishes per-chunk (max key, sum of exp) partials;
 //    a leader workgroup per row locates the chunk holding u * S, the chunk's
-//    owner scans it in vocabulary order and publishes the token.
+//    owner scans it in vocabulary order and publishes the token (decisions
+//    and tokens are written in 16 copies, like the one-row partials).
 
 #include <hip/hip_runtime.h>
 
