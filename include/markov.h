@@ -4,12 +4,12 @@
  *
  * The method (vLLM API page "vllm.models.deepseek_v41.nvidia.specialized_
  * decode.sampling.sharded_markov", module docstring and its per-call
- * diagram): after the draft backbone has produced base logits for N draft
- * positions, the draft tokens are drawn one position at a time.  Position i
- * adds the low-rank transition bias bf16(markov_head[V, r] . markov_embed
- * [previous token]) to its base logits, rounds the result into a bf16
- * draft-logits cache, and samples the token; that token is the previous token
- * of position i + 1.
+ * diagram): the draft backbone first yields base logits for all N draft
+ * positions; the tokens then follow sequentially.  For position i the
+ * low-rank transition bias bf16(markov_head[V, r] . markov_embed[previous
+ * token]) is added to that position's base logits, the sum is rounded into a
+ * bf16 draft-logits cache, and a token is sampled from it, which in turn is
+ * the previous token of position i + 1.
  *
  * Conventions for every entry point:
  *  - Pointers marked "device" are HIP device pointers owned by the caller; the
@@ -74,6 +74,13 @@ typedef enum {
  * `vocab`, rank dim `rank`, sampling `mode`).  Returns 0 for an unsupported
  * shape.  Host only.
  *
+ * The pages keep the chain's exchange state in persistent buffers allocated
+ * once, before any graph capture, so that graphs keep their addresses
+ * (sharded_markov page, DSparkShardedMarkovSampler: the zeroed mailbox and
+ * staging buffer; muse_spark markov page, MarkovSampler.__init__: the per-call
+ * buffers and the per-row arrival counters, zeroed per call).  Here that
+ * state is this caller-owned workspace.
+ *
  * The workspace holds the per-position exchange slots of the workgroups (two
  * halves used by alternate calls) and a small header (call parity, error
  * word).  The caller allocates it, zeroes it ONCE, and passes the same
@@ -109,7 +116,22 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
 
 /*
  * markov_chain_sample: the whole N-position chain for `rows` request rows in
- * one persistent cooperative launch.
+ * one persistent launch (sharded_markov page, module docstring: one kernel
+ * runs the whole chain and keeps the head in registers, so it is read once).
+ *
+ * Launch and co-residency: the launch is a regular one (not a cooperative
+ * launch) of at most one 512-thread workgroup per compute unit, and the
+ * kernel's registers admit only one workgroup per compute unit.  Its
+ * workgroups wait for one another at every position, so they must all be
+ * resident at once: THE CALLER MUST NOT RUN OTHER KERNELS CONCURRENTLY ON THE
+ * SAME DEVICE (on other streams, or other processes) that could keep compute
+ * units from the chain.  Nothing at launch time checks this.  Every
+ * cross-workgroup wait is bounded instead (sharded_markov page,
+ * DSparkShardedMarkovSampler: timeout_ms bounds every cross-rank wait), by 2 s
+ * unless markov_set_wait_limit says otherwise; a wait that gives up sets
+ * MARKOV_DEVERR_TIMEOUT, the call then writes unspecified tokens (possibly
+ * none) and cache values, and THE WORKSPACE MUST BE ZEROED AGAIN before its
+ * next use.  markov_status reports the condition.
  *
  * For each row b with state s = state_idx[b] >= 0, starting from
  * p = prev_tokens[b], for i = 0 .. steps-1 in order
@@ -175,9 +197,9 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
  *                   256-byte aligned, zeroed once before the first call.
  *
  * Errors: MARKOV_E_INVAL / MARKOV_E_UNSUPPORTED for bad arguments (checked on
- * the host before anything is enqueued), MARKOV_E_HIP if the launch fails
- * (e.g. the grid cannot be co-resident).  Device-side conditions (bad anchor
- * token, a wait that timed out) are reported by markov_status.
+ * the host before anything is enqueued), MARKOV_E_HIP if a HIP query or the
+ * launch itself fails.  Device-side conditions (bad anchor token or state
+ * index, a wait that gave up) are reported by markov_status.
  */
 int markov_chain_sample(const void* base_logits, int64_t base_row_stride,
                         int64_t base_step_stride, const uint16_t* head,
@@ -203,7 +225,10 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride,
 int markov_status(void* workspace, void* stream);
 
 /* markov_last_error: the reason for the calling thread's last error ("" if
- * none).  The pointer stays valid until the thread's next libmarkov call. */
+ * none), in the manner of the pages' reason strings for configurations a
+ * sampler cannot serve (sharded_markov page, unsupported_reason; muse_spark
+ * markov page, unsupported).  The pointer stays valid until the thread's
+ * next libmarkov call. */
 const char* markov_last_error(void);
 
 /*
@@ -214,6 +239,17 @@ const char* markov_last_error(void);
  * value.
  */
 int markov_set_grid(int g);
+
+/*
+ * markov_set_wait_limit: testing and debugging knob.  Sets the bound, in
+ * microseconds, of every cross-workgroup wait of later markov_chain_sample
+ * calls (sharded_markov page, DSparkShardedMarkovSampler: timeout_ms bounds
+ * every cross-rank wait); a negative value restores the default of 2 s.  With
+ * 0 a wait gives up as soon as one poll finds a slot still empty, so a test
+ * can drive the timeout path from the host while every workgroup still
+ * exits normally.  Process-wide; returns the previous bound in microseconds.
+ */
+long long markov_set_wait_limit(long long us);
 
 /* markov_grid: the number of workgroups markov_chain_sample would launch for
  * this shape on the current device under the current markov_set_grid value,

@@ -39,6 +39,7 @@ EXPORTS = (
     "markov_status",
     "markov_last_error",
     "markov_set_grid",
+    "markov_set_wait_limit",
     "markov_grid",
 )
 
@@ -78,6 +79,8 @@ def load():
         lib.markov_last_error.argtypes = []
         lib.markov_set_grid.restype = i32
         lib.markov_set_grid.argtypes = [i32]
+        lib.markov_set_wait_limit.restype = ctypes.c_longlong
+        lib.markov_set_wait_limit.argtypes = [ctypes.c_longlong]
         lib.markov_grid.restype = i32
         lib.markov_grid.argtypes = [i32] * 5
         _lib = lib
@@ -213,6 +216,12 @@ def markov_last_error() -> str:
 
 def markov_set_grid(g: int) -> int:
     return int(load().markov_set_grid(int(g)))
+
+
+def markov_set_wait_limit(us: int) -> int:
+    """Bound (microseconds) of the chain's cross-workgroup waits; negative
+    restores the default.  Returns the previous bound."""
+    return int(load().markov_set_wait_limit(int(us)))
 
 
 def markov_grid(rows: int, steps: int, vocab: int, rank: int, mode: int = 0) -> int:

@@ -84,7 +84,8 @@ constexpr int kLeaderRegs = 4;             // inverse-CDF chunks per lane kept i
 constexpr int kPartCopies = 16;            // <= kWaves rows: copies of each step's reducer partials
 constexpr int kPartStride = 64;            // u64 words from one copy to the next (512 bytes)
 constexpr int kDecCopies = 16;             // inverse CDF: copies of each step's decisions and tokens
-constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz
+constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz (the default wait limit)
+constexpr long long kTicksPerUs = 100;                       // s_memrealtime runs at 100 MHz
 
 // ----------------------------------------------------------- bf16 helpers --
 
@@ -420,6 +421,7 @@ struct ChainParams {
   long long cache_states;
   unsigned char* ws;
   unsigned long long ws_half;  // bytes per parity half
+  unsigned long long wait_ticks;  // bound of every cross-workgroup wait (s_memrealtime ticks)
 };
 
 // Workspace half layout (slot arrays of one parity; every slot is written at
@@ -677,7 +679,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   const int wg = blockIdx.x;
   const int rows = p.rows, N = p.N, V = p.V, G = p.G, NC = p.NC, NG = p.NG;
   uint32_t* header = reinterpret_cast<uint32_t*>(p.ws);
-  const uint64_t deadline = now_ticks() + kTimeoutTicks;
+  const uint64_t deadline = now_ticks() + p.wait_ticks;
   // In the epilogue lane l owns group row lr (r = 512 groups have 32 rows:
   // lanes 32..63 have none).
   const int lr = (R == 256) ? lane : (lane & 31);
@@ -1035,11 +1037,15 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     const uint32_t gnan = group8_umin(enan < IPL ? (uint32_t)v0 + enan : 0xFFFFFFFFu);
     float wsum = 0.0f;
     if (MODE == 1) {
+      // The same expf as the owner's scan of the chosen chunk, so that the
+      // leader's chunk weights and the owner's in-chunk CDF are built from
+      // the same exponentials (a cruder exp here would shift draws near a
+      // chunk's upper edge onto its last id).
       const float m = order_key_inv(gmax);
       float s = 0.0f;
       if (ok && gmax != INT_MIN && isfinite(m)) {
 #pragma unroll
-        for (int e = 0; e < IPL; ++e) s += isnan(z[e]) ? 0.0f : __expf(z[e] - m);
+        for (int e = 0; e < IPL; ++e) s += isnan(z[e]) ? 0.0f : expf(z[e] - m);
       }
       wsum = group8_sum(s);
     }
@@ -1523,8 +1529,11 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             const float incl = wave_incl_scan(lsum);
             const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
             const float t = u * total;
-            // First chunk whose inclusive prefix exceeds t (else the last
-            // chunk with weight, when rounding left none above t).
+            // First chunk with weight whose inclusive prefix exceeds t (else
+            // the last chunk with weight, when rounding left none above t).
+            // The weight test matters: a lane past the last chunk, or a
+            // chunk of -inf logits, starts at a running sum that rounding
+            // may put above t, and must never be chosen.
             int found = -1, last_pos = -1;
             float before = 0.0f, wfound = 0.0f, last_before = 0.0f, last_w = 0.0f;
             float run = incl - lsum;
@@ -1538,7 +1547,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
                 w = weight(k, e);
               }
               const int c = lane * KPL + k;
-              if (found < 0 && run + w > t) {
+              if (found < 0 && w > 0.0f && run + w > t) {
                 found = c;
                 before = run;
                 wfound = e;
@@ -1564,6 +1573,9 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
               tl = (t - __shfl(last_before, src)) / __shfl(last_w, src);
             }
             if (!(tl >= 0.0f)) tl = 0.0f;
+            // (Every chosen chunk has weight, hence exists; the clamp only
+            // keeps the owner's reads inside the vocabulary should that fail.)
+            if ((unsigned)o >= (unsigned)NC) o = NC - 1;
             dec = ((uint64_t)(uint32_t)(o + 1) << 32) | __float_as_uint(tl);
           }
           // Every copy gets it: each copy's lines are polled by G / kDecCopies
@@ -1592,13 +1604,20 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             __builtin_amdgcn_s_sleep(1);
           }
           if (mine) {
+            // (A word that is not a valid decision, which only a workspace
+            // left dirty by a timed-out call can hold, yields token 0 instead
+            // of a chunk or token outside the vocabulary.)
+            const int o = (int)(d >> 32) - 1;
             if (d >> 63) {
-              s_tok[b] = (int)(uint32_t)d;
+              const uint32_t tk = (uint32_t)d;
+              s_tok[b] = tk < (uint32_t)V ? (int)tk : 0;
               s_need[b] = 0;
-            } else {
-              const int o = (int)(d >> 32) - 1;
+            } else if ((unsigned)o < (unsigned)NC) {
               s_dec[b] = d;
               s_need[b] = (o % G == wg) ? 2 : 1;
+            } else {
+              s_tok[b] = 0;
+              s_need[b] = 0;
             }
           }
         }
@@ -1691,7 +1710,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             }
             __builtin_amdgcn_s_sleep(1);
           }
-          if (mine) s_tok[b] = (int)(uint32_t)d;
+          if (mine) s_tok[b] = (uint32_t)d < (uint32_t)V ? (int)(uint32_t)d : 0;
         }
       }
       __syncthreads();
@@ -1738,6 +1757,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
 
 thread_local std::string g_last_error;
 std::atomic<int> g_grid_override{0};
+std::atomic<unsigned long long> g_wait_ticks{kTimeoutTicks};
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
@@ -1859,44 +1879,15 @@ int pick_grid(int rows, int rank, int mode, const Shape& sh, int* grid, bool* re
   return MARKOV_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t markov_workspace_bytes(int rows, int steps, int vocab, int rank, int mode) {
-  mode &= ~kModeFlags;
-  Shape sh;
-  if (check_shape(rows, steps, vocab, rank, mode, &sh) != MARKOV_OK) return 0;
-  return kHeader + 2 * call_half_bytes(rows, steps, sh.NC, mode);
-}
-
-int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps, int vocab,
-                      void* stream) {
-  g_last_error.clear();
-  if (!gumbel || !seeds) return fail(MARKOV_E_INVAL, "null gumbel or seeds");
-  if (!aligned16(gumbel)) return fail(MARKOV_E_INVAL, "gumbel is not 16-byte aligned");
-  if (rows < 1 || rows > MARKOV_MAX_ROWS || steps < 1 || steps > MARKOV_MAX_STEPS)
-    return fail(MARKOV_E_UNSUPPORTED, "rows=%d steps=%d out of range", rows, steps);
-  if (vocab < 16 || vocab % 16 != 0 || vocab > MARKOV_MAX_VOCAB)
-    return fail(MARKOV_E_UNSUPPORTED, "vocab=%d is not a positive multiple of 16 up to %d", vocab,
-                MARKOV_MAX_VOCAB);
-  dim3 grid((vocab / 4 + 255) / 256, steps, rows);
-  hipLaunchKernelGGL(noise_fill_kernel, grid, dim3(256), 0, (hipStream_t)stream, gumbel, seeds, steps,
-                     vocab);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(MARKOV_E_HIP, "noise launch: %s", hipGetErrorString(e));
-  return MARKOV_OK;
-}
-
-int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_step_stride,
-                        const uint16_t* head, const uint16_t* embed, const int64_t* prev_tokens,
-                        const float* temperature, const int64_t* seeds, const float* gumbel,
-                        const int64_t* state_idx, float output_multiplier, float soft_cap, int rows,
-                        int steps, int vocab, int rank, int mode, int64_t* draft_tokens,
-                        int64_t tokens_row_stride, void* cache, int64_t cache_states,
-                        int64_t cache_state_stride, int64_t cache_step_stride, void* workspace,
-                        size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+// The chain entry point's argument checks and launches.
+int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_step_stride,
+                 const uint16_t* head, const uint16_t* embed, const int64_t* prev_tokens,
+                 const float* temperature, const int64_t* seeds, const float* gumbel,
+                 const int64_t* state_idx, float output_multiplier, float soft_cap, int rows,
+                 int steps, int vocab, int rank, int mode, int64_t* draft_tokens,
+                 int64_t tokens_row_stride, void* cache, int64_t cache_states,
+                 int64_t cache_state_stride, int64_t cache_step_stride, void* workspace,
+                 size_t workspace_bytes, void* stream) {
   const int base_f32 = (mode & MARKOV_BASE_F32) != 0, cache_f32 = (mode & MARKOV_CACHE_F32) != 0;
   const int noise_inline = (mode & MARKOV_NOISE_INLINE) != 0;
   mode &= ~kModeFlags;
@@ -1976,6 +1967,7 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_
     p.cache_states = cache_states;
     p.ws = (unsigned char*)workspace;
     p.ws_half = ((workspace_bytes - kHeader) / 2) & ~(size_t)255;
+    p.wait_ticks = g_wait_ticks.load();
 
     void* args[] = {&p};
     const size_t shmem = (size_t)nr * (rank / 8 + 1) * 16;
@@ -1992,6 +1984,50 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_
                   hipGetErrorString(e));
   }
   return MARKOV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t markov_workspace_bytes(int rows, int steps, int vocab, int rank, int mode) {
+  mode &= ~kModeFlags;
+  Shape sh;
+  if (check_shape(rows, steps, vocab, rank, mode, &sh) != MARKOV_OK) return 0;
+  return kHeader + 2 * call_half_bytes(rows, steps, sh.NC, mode);
+}
+
+int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps, int vocab,
+                      void* stream) {
+  g_last_error.clear();
+  if (!gumbel || !seeds) return fail(MARKOV_E_INVAL, "null gumbel or seeds");
+  if (!aligned16(gumbel)) return fail(MARKOV_E_INVAL, "gumbel is not 16-byte aligned");
+  if (rows < 1 || rows > MARKOV_MAX_ROWS || steps < 1 || steps > MARKOV_MAX_STEPS)
+    return fail(MARKOV_E_UNSUPPORTED, "rows=%d steps=%d out of range", rows, steps);
+  if (vocab < 16 || vocab % 16 != 0 || vocab > MARKOV_MAX_VOCAB)
+    return fail(MARKOV_E_UNSUPPORTED, "vocab=%d is not a positive multiple of 16 up to %d", vocab,
+                MARKOV_MAX_VOCAB);
+  dim3 grid((vocab / 4 + 255) / 256, steps, rows);
+  hipLaunchKernelGGL(noise_fill_kernel, grid, dim3(256), 0, (hipStream_t)stream, gumbel, seeds, steps,
+                     vocab);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MARKOV_E_HIP, "noise launch: %s", hipGetErrorString(e));
+  return MARKOV_OK;
+}
+
+int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_step_stride,
+                        const uint16_t* head, const uint16_t* embed, const int64_t* prev_tokens,
+                        const float* temperature, const int64_t* seeds, const float* gumbel,
+                        const int64_t* state_idx, float output_multiplier, float soft_cap, int rows,
+                        int steps, int vocab, int rank, int mode, int64_t* draft_tokens,
+                        int64_t tokens_row_stride, void* cache, int64_t cache_states,
+                        int64_t cache_state_stride, int64_t cache_step_stride, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return chain_sample(base_logits, base_row_stride, base_step_stride, head, embed, prev_tokens,
+                      temperature, seeds, gumbel, state_idx, output_multiplier, soft_cap, rows, steps,
+                      vocab, rank, mode, draft_tokens, tokens_row_stride, cache, cache_states,
+                      cache_state_stride, cache_step_stride, workspace, workspace_bytes, stream);
 }
 
 int markov_status(void* workspace, void* stream) {
@@ -2015,6 +2051,11 @@ int markov_status(void* workspace, void* stream) {
 const char* markov_last_error(void) { return g_last_error.c_str(); }
 
 int markov_set_grid(int g) { return g_grid_override.exchange(g < 0 ? 0 : g); }
+
+long long markov_set_wait_limit(long long us) {
+  const unsigned long long t = us < 0 ? kTimeoutTicks : (unsigned long long)us * kTicksPerUs;
+  return (long long)(g_wait_ticks.exchange(t) / kTicksPerUs);
+}
 
 int markov_grid(int rows, int steps, int vocab, int rank, int mode) {
   g_last_error.clear();

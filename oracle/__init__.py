@@ -17,6 +17,7 @@ from .oracle import (  # noqa: F401
     gumbel,
     hash_step,
     hash_vocab,
+    log_f32,
     noise_fill,
     splitmix64,
     splitmix64_mix,

@@ -56,6 +56,7 @@ def _load():
             "orc_hash_step": (ctypes.c_uint64, [ctypes.c_int64] * 3),
             "orc_hash_vocab": (ctypes.c_uint64, [ctypes.c_uint64, ctypes.c_int64]),
             "orc_uniform": (ctypes.c_float, [ctypes.c_uint64]),
+            "orc_log_f32": (ctypes.c_float, [ctypes.c_float]),
             "orc_gumbel": (ctypes.c_float, [ctypes.c_float]),
             "orc_noise_fill": (None, [_f32p, _i64p, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
             "orc_uniform_range": (None, [_f32p] + [ctypes.c_int64] * 5),
@@ -141,6 +142,11 @@ def hash_vocab(prefix: int, v: int) -> int:
 
 def uniform(h: int) -> float:
     return float(_load().orc_uniform(h & 0xFFFFFFFFFFFFFFFF))
+
+
+def log_f32(x: float) -> float:
+    """The oracle's fp32 natural log (the one inside the Gumbel draw)."""
+    return float(_load().orc_log_f32(x))
 
 
 def gumbel(u: float) -> float:

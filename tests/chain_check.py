@@ -16,8 +16,9 @@ tokens.  At every position it checks:
     the device's own cache explains it (the device token is what the
     sampling rule gives on the device cache, evaluated here in the same fp32
     precision), the two caches differ, and the oracle's decision margin is
-    within what those cache differences can move; the row's walk then stops,
-    since later positions follow a different previous token.
+    within what those cache differences can move.  The walk then goes on
+    teacher-forced: the oracle's next position starts from the device's
+    token, as the device's did, so every later position is still compared.
 For the inverse CDF, a draw whose u * S falls within WINDOW * S of a bin
 edge may also land in the neighbouring bin (fp32 partial sums on the device,
 fp64 on the oracle).
@@ -25,7 +26,9 @@ fp64 on the oracle).
 
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 
 import numpy as np
 
@@ -149,87 +152,135 @@ class Stats:
     cache_one_ulp: int = 0
     walked_rows: int = 0
 
+    @property
+    def cache_beyond_1ulp(self) -> int:
+        return self.cache_elems - self.cache_one_ulp
+
+    def merge(self, o: "Stats") -> None:
+        self.pairs += o.pairs
+        self.token_match += o.token_match
+        self.mismatches += o.mismatches
+        self.cache_elems += o.cache_elems
+        self.cache_exact += o.cache_exact
+        self.cache_one_ulp += o.cache_one_ulp
+        self.walked_rows += o.walked_rows
+
     def summary(self) -> str:
         return (f"pairs={self.pairs} token_match={self.token_match} "
                 f"mismatch={len(self.mismatches)} cache_exact={self.cache_exact}/{self.cache_elems} "
-                f"within_1ulp={self.cache_one_ulp}")
+                f"within_1ulp={self.cache_one_ulp} beyond_1ulp={self.cache_beyond_1ulp}")
 
 
-def walk(w, tok_gpu, cache_gpu, gumbel, rows=None, exact=False) -> Stats:
+def record(name: str, st: "Stats | None", **extra) -> None:
+    """Append the counts of a parity check as one JSON line to the file named
+    by MARKOV_PARITY_LOG, if set (the parity figures quoted in the design
+    notes come from these lines)."""
+    path = os.environ.get("MARKOV_PARITY_LOG")
+    if not path:
+        return
+    import json
+    line = {"check": name}
+    if st is not None:
+        line.update(pairs=st.pairs, token_match=st.token_match, mismatches=len(st.mismatches),
+                    cache_elems=st.cache_elems, cache_exact=st.cache_exact,
+                    cache_beyond_1ulp=st.cache_beyond_1ulp, walked_rows=st.walked_rows)
+    line.update(extra)
+    with open(path, "a") as f:
+        f.write(json.dumps(line) + "\n")
+
+
+def walk(w, tok_gpu, cache_gpu, gumbel, rows=None, exact=False, workers=None, absdot=None) -> Stats:
     """Walk `rows` (default: all) of workload w; gumbel[rows, N, V] is the
     noise both sides used (mode 0).  exact=True demands bit-identical caches
-    and tokens."""
-    st = Stats()
+    and tokens.  Rows are walked in parallel threads (the oracle's C calls
+    release the interpreter lock)."""
     sidx = np.arange(w.rows) if w.state_idx is None else w.state_idx
-    rows = range(w.rows) if rows is None else rows
+    rows = [b for b in (range(w.rows) if rows is None else rows) if int(sidx[b]) >= 0]
+    if absdot is None and not exact:
+        absdot = AbsDot(w)
+    st = Stats()
+    if workers is None:
+        workers = min(16, os.cpu_count() or 1, max(1, len(rows)))
+    if workers <= 1:
+        for b in rows:
+            st.merge(_walk_row(w, b, int(sidx[b]), tok_gpu, cache_gpu, gumbel, exact, absdot))
+        return st
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        futs = [ex.submit(_walk_row, w, b, int(sidx[b]), tok_gpu, cache_gpu, gumbel, exact, absdot)
+                for b in rows]
+        for f in futs:
+            st.merge(f.result())
+    return st
+
+
+def _walk_row(w, b, s, tok_gpu, cache_gpu, gumbel, exact, absdot) -> Stats:
+    """One row of `walk` (state index s >= 0)."""
+    st = Stats()
     V = w.V
-    absdot = None if exact else AbsDot(w)
-    for b in rows:
-        s = int(sidx[b])
-        if s < 0:
+    st.walked_rows += 1
+    p = int(w.prev[b])
+    T = float(w.temperature[b])
+    for i in range(w.N):
+        g = gumbel[b, i] if (w.mode == 0 and gumbel is not None) else None
+        u = oracle.uniform(oracle.hash_step(int(w.seeds[b]), b, i)) if w.mode == 1 else 0.0
+        tok_o, c_o, diag, bias_o = oracle.step(w.base[b, i], w.head, w.embed, p, T, g, u=u,
+                                               mult=w.mult, cap=w.cap, mode=w.mode,
+                                               with_diag=True, with_bias=True,
+                                               cache_f32=w.cache_f32)
+        c_g = cache_gpu[s, i, :V]
+        nan_o, nan_g = np.isnan(cache_values(c_o)), np.isnan(cache_values(c_g))
+        assert np.array_equal(nan_o, nan_g), f"row {b} step {i}: NaN positions differ"
+        d = np.abs(cache_ordinal(c_o) - cache_ordinal(c_g))
+        d[nan_o] = 0
+        st.cache_elems += V
+        same = (d == 0)
+        st.cache_exact += int(same.sum())
+        st.cache_one_ulp += int((d <= 1).sum())
+        if exact:
+            assert same.all(), f"row {b} step {i}: {int((~same).sum())} cache elements differ"
+        else:
+            fo = cache_values(c_o).astype(np.float64)
+            fg = cache_values(c_g).astype(np.float64)
+            fin = ~nan_o & np.isfinite(fo) & np.isfinite(fg)
+            assert np.array_equal(fo[~nan_o & ~fin], fg[~nan_o & ~fin]), f"row {b} step {i}: infinities differ"
+            tol_bias = bias_tolerance(bias_o, absdot(p), w.r)
+            bound = (tol_bias * abs(w.mult)
+                     + cache_spacing(c_o, np.maximum(np.abs(fo), np.abs(fg))))
+            bad = fin & (np.abs(fo - fg) > bound)
+            assert not bad.any(), (f"row {b} step {i}: {int(bad.sum())} cache values beyond the "
+                                   f"bias-implied bound, e.g. v={int(np.flatnonzero(bad)[0])}")
+        t_g = int(tok_gpu[b, i])
+        st.pairs += 1
+        if t_g == tok_o:
+            st.token_match += 1
+            p = tok_o
             continue
-        st.walked_rows += 1
-        p = int(w.prev[b])
-        T = float(w.temperature[b])
-        for i in range(w.N):
-            g = gumbel[b, i] if (w.mode == 0 and gumbel is not None) else None
-            u = oracle.uniform(oracle.hash_step(int(w.seeds[b]), b, i)) if w.mode == 1 else 0.0
-            tok_o, c_o, diag, bias_o = oracle.step(w.base[b, i], w.head, w.embed, p, T, g, u=u,
-                                                   mult=w.mult, cap=w.cap, mode=w.mode,
-                                                   with_diag=True, with_bias=True,
-                                                   cache_f32=w.cache_f32)
-            c_g = cache_gpu[s, i, :V]
-            nan_o, nan_g = np.isnan(cache_values(c_o)), np.isnan(cache_values(c_g))
-            assert np.array_equal(nan_o, nan_g), f"row {b} step {i}: NaN positions differ"
-            d = np.abs(cache_ordinal(c_o) - cache_ordinal(c_g))
-            d[nan_o] = 0
-            st.cache_elems += V
-            same = (d == 0)
-            st.cache_exact += int(same.sum())
-            st.cache_one_ulp += int((d <= 1).sum())
-            if exact:
-                assert same.all(), f"row {b} step {i}: {int((~same).sum())} cache elements differ"
-            else:
-                fo = cache_values(c_o).astype(np.float64)
-                fg = cache_values(c_g).astype(np.float64)
-                fin = ~nan_o & np.isfinite(fo) & np.isfinite(fg)
-                assert np.array_equal(fo[~nan_o & ~fin], fg[~nan_o & ~fin]), f"row {b} step {i}: infinities differ"
-                tol_bias = bias_tolerance(bias_o, absdot(p), w.r)
-                bound = (tol_bias * abs(w.mult)
-                         + cache_spacing(c_o, np.maximum(np.abs(fo), np.abs(fg))))
-                bad = fin & (np.abs(fo - fg) > bound)
-                assert not bad.any(), (f"row {b} step {i}: {int(bad.sum())} cache values beyond the "
-                                       f"bias-implied bound, e.g. v={int(np.flatnonzero(bad)[0])}")
-            t_g = int(tok_gpu[b, i])
-            st.pairs += 1
-            if t_g == tok_o:
-                st.token_match += 1
-                p = tok_o
-                continue
-            assert not exact, f"row {b} step {i}: token {t_g} != oracle {tok_o}"
-            assert 0 <= t_g < V, f"row {b} step {i}: token {t_g} out of range"
-            caches_differ = not same.all()
-            if w.mode == 0 or T <= 0 or diag[3] == 1.0:
-                # Argmax-type decision: the device token must be the rule's
-                # pick on the device cache (+ the same noise), and the oracle's
-                # margin must be within the score change the cache moved.
-                s_g = scores(c_g, T, g if w.mode == 0 else None)
-                s_o = scores(c_o, T, g if w.mode == 0 else None)
-                assert t_g == pick_max(s_g), f"row {b} step {i}: device token is not its own argmax"
-                assert caches_differ, f"row {b} step {i}: identical caches but tokens differ"
-                moved = abs(float(s_o[tok_o]) - float(s_g[tok_o])) + abs(float(s_o[t_g]) - float(s_g[t_g]))
-                margin = float(diag[0]) - float(s_o[t_g])
-                assert margin <= moved + 1e-12, f"row {b} step {i}: margin {margin} > moved {moved}"
-            else:
-                k_g, cdf, t = inv_cdf_bin(c_g, T, u)
-                if t_g != k_g:
-                    # every edge between the two bins lies within the window of u*S
-                    lo, hi = min(t_g, k_g), max(t_g, k_g)
-                    edges = cdf[lo:hi]
-                    assert np.all(np.abs(t - edges) <= WINDOW * cdf[-1]), \
-                        f"row {b} step {i}: device bin {t_g} vs its own cache's {k_g}"
-                assert caches_differ or diag[2] <= WINDOW, \
-                    f"row {b} step {i}: identical caches, bin {t_g} vs {tok_o}, edge distance {diag[2]}"
-            st.mismatches.append((b, i, tok_o, t_g))
-            break  # later positions would follow a different previous token
+        assert not exact, f"row {b} step {i}: token {t_g} != oracle {tok_o}"
+        assert 0 <= t_g < V, f"row {b} step {i}: token {t_g} out of range"
+        caches_differ = not same.all()
+        if w.mode == 0 or T <= 0 or diag[3] == 1.0:
+            # Argmax-type decision: the device token must be the rule's
+            # pick on the device cache (+ the same noise), and the oracle's
+            # margin must be within the score change the cache moved.
+            s_g = scores(c_g, T, g if w.mode == 0 else None)
+            s_o = scores(c_o, T, g if w.mode == 0 else None)
+            assert t_g == pick_max(s_g), f"row {b} step {i}: device token is not its own argmax"
+            assert caches_differ, f"row {b} step {i}: identical caches but tokens differ"
+            moved = abs(float(s_o[tok_o]) - float(s_g[tok_o])) + abs(float(s_o[t_g]) - float(s_g[t_g]))
+            margin = float(diag[0]) - float(s_o[t_g])
+            assert margin <= moved + 1e-12, f"row {b} step {i}: margin {margin} > moved {moved}"
+        else:
+            k_g, cdf, t = inv_cdf_bin(c_g, T, u)
+            if t_g != k_g:
+                # every edge between the two bins lies within the window of u*S
+                lo, hi = min(t_g, k_g), max(t_g, k_g)
+                edges = cdf[lo:hi]
+                assert np.all(np.abs(t - edges) <= WINDOW * cdf[-1]), \
+                    f"row {b} step {i}: device bin {t_g} vs its own cache's {k_g}"
+            assert caches_differ or diag[2] <= WINDOW, \
+                f"row {b} step {i}: identical caches, bin {t_g} vs {tok_o}, edge distance {diag[2]}"
+        st.mismatches.append((b, i, tok_o, t_g))
+        # teacher-forced: the device's next position started from its
+        # own token, so the oracle's does too
+        p = t_g
     return st

@@ -14,6 +14,7 @@ static float asf(uint32_t b) { float f; std::memcpy(&f, &b, 4); return f; }
 static uint32_t asu(float f) { uint32_t b; std::memcpy(&b, &f, 4); return b; }
 static float ref_log(float x) { return (float)std::log((double)x); }
 static long fallbacks = 0;
+static bool list_fallbacks = false;  // print the inputs the fast path leaves to the library
 
 // Same operations, same order, as the kernel: bucket, r = m c - 1 in fp64,
 // the r^4 tail of ln(1 + r) in fp32, r - r^2/2 + r^3/3 in fp64, + e ln2 -
@@ -38,10 +39,21 @@ static float fast_log(float x) {
   const int d = (int)((uint32_t)yb & 0x1FFFFFFFu) - (1 << 28);
   if ((d < 0 ? -d : d) > (1 << 12)) return (float)y;
   ++fallbacks;
+  if (list_fallbacks) std::printf("%08x\n", b);
   return ref_log(x);
 }
 
-int main() {
+int main(int argc, char** argv) {
+  // --list: only print (one hex bit pattern per line) the noise inputs on
+  // which the fast path could not decide the rounding.
+  if (argc > 1 && std::strcmp(argv[1], "--list") == 0) {
+    list_fallbacks = true;
+    for (uint32_t k = 0; k < (1u << 23); ++k) {
+      const float u = (float)(2u * k + 1u) * 0x1p-24f;
+      fast_log(-fast_log(u));
+    }
+    return 0;
+  }
   long n = 0, bad = 0;
   for (uint32_t k = 0; k < (1u << 23); ++k) {
     const float u = (float)(2u * k + 1u) * 0x1p-24f;

@@ -515,3 +515,168 @@ def test_fp32_cache_inverse_cdf_vs_searchsorted():
         u = oracle.uniform(oracle.hash_step(int(w.seeds[0]), 0, i))
         k = int(np.searchsorted(cdf, u * cdf[-1], side="right"))
         assert toks[0, i] == min(k, V - 1)
+
+
+# ------------------------------------------- the fp32 log, correctly rounded --
+# The noise's fp32 logs are defined as ln(x) correctly rounded to fp32
+# (sharded_markov page, _shard_noise_kernel: fp32 noise; the reading takes
+# the correctly rounded log so that two libraries agree).  These pins compute
+# that value with Python's decimal module at 50 digits, independently of any
+# libm, and compare the oracle's log with it bit for bit.
+
+def _ln_rn32(x) -> np.float32:
+    """ln(x) for an fp32 x > 0, correctly rounded to fp32, from a 50-digit
+    decimal logarithm: the nearest of the three fp32 values around it (a
+    logarithm of an fp32 value other than 1 is never an fp32 midpoint)."""
+    from decimal import Decimal, localcontext
+    x = np.float32(x)
+    with localcontext() as ctx:
+        ctx.prec = 50
+        d = Decimal(float(x)).ln()
+        f = np.float32(float(d))
+        cands = (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf)))
+        errs = [abs(Decimal(float(c)) - d) for c in cands]
+    return cands[int(np.argmin(errs))]
+
+
+def test_log_f32_correctly_rounded_on_sampled_noise_inputs():
+    """10^5 uniforms u of the noise and their -ln u: both fp32 logs of the
+    Gumbel draw equal the decimal log correctly rounded to fp32."""
+    rng = np.random.default_rng(21)
+    ks = rng.integers(0, 1 << 23, 100_000)
+    ks[:4] = [0, 1, (1 << 23) - 1, 1 << 22]  # the extremes of u and u = 1/2 + 2^-24
+    for k in ks:
+        u = np.float32((2 * int(k) + 1) * 2.0**-24)
+        inner = np.float32(oracle.log_f32(float(u)))
+        assert inner == _ln_rn32(u), (hex(int(k)), float(u))
+        y = np.float32(-inner)
+        outer = np.float32(oracle.log_f32(float(y)))
+        assert outer == _ln_rn32(y), (hex(int(k)), float(y))
+        assert np.float32(oracle.gumbel(float(u))) == np.float32(-outer)
+
+
+def test_log_f32_correctly_rounded_on_hard_inputs(tmp_path):
+    """The noise inputs whose fp64 logarithm lies so close to an fp32
+    rounding midpoint that the device's table-driven log leaves them to the
+    library (listed by tests/noise_log_check.cpp --list over all 2^24 noise
+    inputs): the oracle's log is the correctly rounded one there too."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("needs g++")
+    exe = str(tmp_path / "noise_log_check")
+    subprocess.run(["g++", "-O2", "-ffp-contract=off", "-std=c++17",
+                    os.path.join(os.path.dirname(__file__), "noise_log_check.cpp"), "-o", exe],
+                   check=True)
+    out = subprocess.run([exe, "--list"], check=True, capture_output=True, text=True).stdout.split()
+    xs = np.array([int(h, 16) for h in out], dtype=np.uint32).view(np.float32)
+    assert len(xs) > 50
+    for x in xs:
+        assert np.float32(oracle.log_f32(float(x))) == _ln_rn32(x), float(x)
+
+
+# --------------------------------------------------- the hash, restated --
+# DESIGN's reading of the noise hash, restated here in plain Python integers:
+# sm(x) is one SplitMix64 output for state x (Steele, Lea and Flood, OOPSLA
+# 2014; its finaliser constants are pinned by the published vectors above),
+# the prefix absorbs seed, row and step in that order, then the global vocab
+# id; the uniform is (2k + 1) 2^-24 with k the top 23 bits.
+
+def _sm(x: int) -> int:
+    z = (x + GAMMA) & M64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & M64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & M64
+    return z ^ (z >> 31)
+
+
+def _prefix(seed: int, row: int, step: int) -> int:
+    h = _sm(seed & M64)
+    h = _sm(h ^ (row & M64))
+    return _sm(h ^ (step & M64))
+
+
+@pytest.mark.parametrize("seed,row,step", [
+    (0, 0, 0), (1, 0, 0), (-1, 0, 0), (-(2**63), 5, 7), (2**63 - 1, 63, 255),
+    (0x4D41524B02, 3, 1), (-123456789, 4095, 15), (42, 1, 2), (42, 2, 1),
+])
+def test_hash_and_uniform_restated_in_python_integers(seed, row, step):
+    h2 = _prefix(seed, row, step)
+    assert oracle.hash_step(seed, row, step) == h2
+    assert Fraction(oracle.uniform(h2)) == Fraction(2 * (h2 >> 41) + 1, 1 << 24)
+    for v in (0, 1, 15, 16, 4095, 129279, 262143, (1 << 24) - 1):
+        h3 = _sm(h2 ^ v)
+        assert oracle.hash_vocab(h2, v) == h3
+        assert Fraction(oracle.uniform(h3)) == Fraction(2 * (h3 >> 41) + 1, 1 << 24)
+    # the noise of a small row, element by element
+    g = oracle.noise_fill(np.array([seed], dtype=np.int64), step + 1, 16)[0, step]
+    for v in range(16):
+        u = np.float32((2 * (_sm(_prefix(seed, 0, step) ^ v) >> 41) + 1) * 2.0**-24)
+        assert g[v] == -_ln_rn32(-_ln_rn32(u))
+
+
+# ------------------------------------------------------ diagnostics pins --
+# The oracle's diagnostics (used by the parity walk to explain a device token
+# that differs from the oracle's) on hand-built vectors whose answers are
+# exact: a zero head makes the bias 0, so the cache holds the base logits.
+
+def _step_diag(vals, T, mode, u=0.0):
+    V = len(vals)
+    base = bf16(np.asarray(vals, dtype=np.float32))
+    head = np.zeros((V, 16), dtype=np.uint16)
+    embed = np.zeros((V, 16), dtype=np.uint16)
+    g = np.zeros(V, dtype=np.float32) if mode == 0 else None
+    tok, _, diag = oracle.step(base, head, embed, 0, T, g, u=u, mode=mode, with_diag=True)
+    return tok, diag
+
+
+@pytest.mark.parametrize("vals,tok,best,second,second_at,nan", [
+    ([1, 5, 3, 5, 2], 1, 5, 5, 3, 0),          # tie: the lower id wins, the other is runner-up
+    ([1, 5, 3, 4, 2], 1, 5, 4, 3, 0),
+    ([-3, -1, -2, -7], 1, -1, -2, 2, 0),
+    ([2, np.nan, 9, np.nan], 1, None, 9, 2, 1),  # NaN decides; runner-up ignores NaNs
+    ([0.0, -0.0, -1.0], 0, 0, 0, 1, 0),        # -0 equals +0
+    ([np.inf, 3, np.inf], 0, np.inf, np.inf, 2, 0),
+])
+def test_diag_of_the_argmax_rule(vals, tok, best, second, second_at, nan):
+    t, d = _step_diag(vals, 0.0, 0)
+    assert t == tok
+    if best is None:
+        assert np.isnan(d[0])
+    else:
+        assert d[0] == best
+    assert d[1] == second and d[2] == second_at and d[3] == nan
+
+
+@pytest.mark.parametrize("u,tok,dist,across", [
+    (0.625, 2, 0.125, 1),    # t = 2.5: midway in bin 2 (cdf 2 .. 3); ties go to the lower edge
+    (0.5625, 2, 0.0625, 1),  # t = 2.25: nearer the lower edge, id 1 across it
+    (0.6875, 2, 0.0625, 3),  # t = 2.75: nearer the upper edge, id 3 across it
+    (0.125, 0, 0.125, -1),   # t = 0.5 in bin 0: the lower edge has nothing across
+    (0.9375, 3, 0.0625, -1), # t = 3.75: the top edge has nothing across
+])
+def test_diag_of_the_inverse_cdf(u, tok, dist, across):
+    """Four equal weights (all logits 0): cdf = 1, 2, 3, 4, S = 4, t = 4u,
+    all exact in fp64."""
+    t, d = _step_diag([0, 0, 0, 0], 1.0, 1, u=u)
+    assert t == tok
+    assert d[0] == 4 * u and d[1] == 4.0 and d[2] == dist and d[3] == 0 and d[4] == across
+
+
+def test_inverse_cdf_nan_diag_and_trailing_zero_weights():
+    t, d = _step_diag([0, np.nan, 0], 1.0, 1, u=0.5)
+    assert t == 1 and d[3] == 1 and d[4] == -1
+    # -inf logits carry no weight: t = 3.75 lies in bin 3 (cdf 3 .. 4); the
+    # id across the nearer (upper) edge is 4, though it has no weight
+    t, d = _step_diag([0, 0, 0, 0, -np.inf, -np.inf], 1.0, 1, u=0.9375)
+    assert t == 3 and d[1] == 4.0 and d[2] == 0.0625 and d[4] == 4
+
+
+def test_inverse_cdf_no_bin_fallback():
+    """The hash's u is at most 1 - 2^-24, so t = u S stays below the total and
+    some bin always exceeds it; u = 1 (reachable through the step call
+    only) leaves none, and the rule then takes the last id with weight, not
+    a trailing id of weight 0."""
+    vals = [0, -1, 0, 0, 0, -np.inf, -np.inf, -np.inf]
+    assert _step_diag(vals, 1.0, 1, u=1.0)[0] == 4
+    assert _step_diag(vals, 1.0, 1, u=1.0 - 2.0**-24)[0] == 4
+    assert _step_diag([0, 0, 0, 0], 1.0, 1, u=1.0)[0] == 3

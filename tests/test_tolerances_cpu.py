@@ -58,3 +58,49 @@ def test_bias_tolerance_special_values():
     one = synth.to_bf16_bits(np.array([1.0], np.float32))
     t = chain_check.bias_tolerance(one, np.array([0.0]), 256)
     assert t[0] == 2.0**-7
+
+
+# ------------------------------------------------------------ the walk --
+# The parity walk run on the oracle's own outputs, with mistakes planted in
+# copies of them on the CPU: it must accept the oracle, reject a token its
+# cache does not explain, and accept (and walk past) one its cache does.
+
+def _oracle_run(w):
+    import oracle
+    g = oracle.noise_fill(w.seeds, w.N, w.V)
+    t, c = oracle.chain(w.base, w.head, w.embed, w.prev, w.temperature, w.seeds, gumbel=g)
+    return g, t, c
+
+
+def test_walk_accepts_the_oracle_and_rejects_an_unexplained_token():
+    import pytest
+    from markov_bias_chain_amd import synth
+    w = synth.make("walk", 512, 256, 2, 4, seed=3, temperature=[1.0, 0.0])
+    g, t, c = _oracle_run(w)
+    st = chain_check.walk(w, t, c, g)
+    assert st.token_match == st.pairs == 8 and not st.mismatches
+    assert chain_check.walk(w, t, c, g, exact=True).token_match == 8
+    bad = t.copy()
+    bad[0, 1] = (bad[0, 1] + 1) % w.V
+    with pytest.raises(AssertionError):
+        chain_check.walk(w, bad, c, g)
+
+
+def test_walk_accepts_an_explained_flip_and_continues_from_the_device_token():
+    """Zero head (bias 0), greedy rows: the cache is the base logits.  At
+    step 1 ids 10 and 5 are one bf16 ulp apart (2 and 2 - 2^-7).  A 'device'
+    whose cache holds id 10 one ulp lower ties the two and takes id 5: the
+    walk must accept it (one-ulp cache difference, device token = its own
+    argmax, margin = the move) and compare the later steps too."""
+    from markov_bias_chain_amd import synth
+    w = synth.make("flip", 256, 256, 1, 4, seed=4, weights="zero", base_std=0.5, temperature=0.0)
+    w.base[0, 1, 10] = synth.to_bf16_bits(np.array([2.0], np.float32))[0]
+    w.base[0, 1, 5] = synth.to_bf16_bits(np.array([2.0 - 2.0**-7], np.float32))[0]
+    g, t, c = _oracle_run(w)
+    assert t[0, 1] == 10
+    dev_t, dev_c = t.copy(), c.copy()
+    dev_c[0, 1, 10] = w.base[0, 1, 5]
+    dev_t[0, 1] = 5
+    st = chain_check.walk(w, dev_t, dev_c, g)
+    assert st.pairs == 4 and st.token_match == 3 and st.mismatches == [(0, 1, 10, 5)]
+    assert st.cache_beyond_1ulp == 0
