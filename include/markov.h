@@ -215,12 +215,49 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride,
                         size_t workspace_bytes, void* stream);
 
 /*
+ * markov_chain_sample_noalloc: markov_chain_sample without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture
+ * that may not call hipMalloc, tight serving loops, harnesses that forbid
+ * allocation.  It takes the same arguments but workspace and
+ * workspace_bytes, runs the same kernels and writes the same outputs; the
+ * call allocates and frees nothing.  The chain's exchange state lives in a
+ * static device array of MARKOV_NOALLOC_MAX_BYTES bytes inside the library,
+ * one per device it runs on, held until the process ends.
+ *
+ * Limits and sharing:
+ *  - a call shape whose markov_workspace_bytes exceeds
+ *    MARKOV_NOALLOC_MAX_BYTES is refused with MARKOV_E_UNSUPPORTED;
+ *  - every call on one device uses that device's one array, which keeps the
+ *    last call's state: calls that overlap in time on one device (other
+ *    streams or threads without ordering) race and give wrong results;
+ *  - the first call on a device also enqueues on `stream` a one-time kernel
+ *    that zeroes the array (made outside graph capture, it stays out of any
+ *    graph);
+ *  - device errors are read with markov_status(NULL, stream); after
+ *    MARKOV_DEVERR_TIMEOUT that call zeroes the array again itself.
+ */
+#define MARKOV_NOALLOC_MAX_BYTES ((size_t)8 << 20)
+int markov_chain_sample_noalloc(const void* base_logits, int64_t base_row_stride,
+                                int64_t base_step_stride, const uint16_t* head,
+                                const uint16_t* embed, const int64_t* prev_tokens,
+                                const float* temperature, const int64_t* seeds,
+                                const float* gumbel, const int64_t* state_idx,
+                                float output_multiplier, float soft_cap, int rows,
+                                int steps, int vocab, int rank, int mode,
+                                int64_t* draft_tokens, int64_t tokens_row_stride,
+                                void* cache, int64_t cache_states,
+                                int64_t cache_state_stride,
+                                int64_t cache_step_stride, void* stream);
+
+/*
  * markov_status: synchronises `stream`, then reads and clears the device
  * error word of `workspace` (sharded_markov page, DSparkShardedMarkovSampler:
  * cross-workgroup waits are bounded and report instead of hanging).
  * Returns MARKOV_OK, or MARKOV_E_DEVICE with the error bits described by
  * markov_last_error().  After a MARKOV_DEVERR_TIMEOUT the workspace must be
- * zeroed again before the next call.
+ * zeroed again before the next call.  With workspace NULL it reads the
+ * array of markov_chain_sample_noalloc on the current device (MARKOV_OK if
+ * no such call has run there) and zeroes that array after a timeout.
  */
 int markov_status(void* workspace, void* stream);
 

@@ -36,6 +36,7 @@ EXPORTS = (
     "markov_workspace_bytes",
     "markov_noise_fill",
     "markov_chain_sample",
+    "markov_chain_sample_noalloc",
     "markov_status",
     "markov_last_error",
     "markov_set_grid",
@@ -73,6 +74,10 @@ def load():
         lib.markov_chain_sample.argtypes = [
             vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, f32, f32,
             i32, i32, i32, i32, i32, vp, i64, vp, i64, i64, i64, vp, sz, vp]
+        lib.markov_chain_sample_noalloc.restype = i32
+        lib.markov_chain_sample_noalloc.argtypes = [
+            vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, f32, f32,
+            i32, i32, i32, i32, i32, vp, i64, vp, i64, i64, i64, vp]
         lib.markov_status.restype = i32
         lib.markov_status.argtypes = [vp, vp]
         lib.markov_last_error.restype = ctypes.c_char_p
@@ -147,7 +152,7 @@ def markov_noise_fill(gumbel: torch.Tensor, seeds: torch.Tensor, stream=None) ->
 def markov_chain_sample(base_logits: torch.Tensor, head: torch.Tensor, embed: torch.Tensor,
                         prev_tokens: torch.Tensor, temperature: torch.Tensor,
                         draft_tokens: torch.Tensor, cache: torch.Tensor,
-                        workspace: torch.Tensor, *, gumbel: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None, *, gumbel: torch.Tensor | None = None,
                         seeds: torch.Tensor | None = None,
                         state_idx: torch.Tensor | None = None,
                         output_multiplier: float = 1.0, soft_cap: float = 0.0,
@@ -155,7 +160,8 @@ def markov_chain_sample(base_logits: torch.Tensor, head: torch.Tensor, embed: to
     """Run the whole chain: draft_tokens[rows, >=N] (int64) and
     cache[states, N, >=V] (bf16 or fp32) are written in place.  base_logits
     are bf16 or fp32; the element types are passed to the library as flags
-    of `mode`."""
+    of `mode`.  workspace None calls markov_chain_sample_noalloc (the
+    library's own static scratch; no device memory is allocated)."""
     dev = base_logits.device
     _need(base_logits, (torch.bfloat16, torch.float32), "base_logits", dev)
     _need(head, torch.bfloat16, "head", dev, contiguous=True)
@@ -164,7 +170,8 @@ def markov_chain_sample(base_logits: torch.Tensor, head: torch.Tensor, embed: to
     _need(temperature, torch.float32, "temperature", dev, contiguous=True)
     _need(draft_tokens, torch.int64, "draft_tokens", dev)
     _need(cache, (torch.bfloat16, torch.float32), "cache", dev)
-    _need(workspace, torch.uint8, "workspace", dev, contiguous=True)
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace", dev, contiguous=True)
     if base_logits.dim() != 3 or base_logits.stride(2) != 1:
         raise ValueError("base_logits must be [rows, N, V] with unit last stride")
     rows, steps, vocab = base_logits.shape
@@ -192,21 +199,35 @@ def markov_chain_sample(base_logits: torch.Tensor, head: torch.Tensor, embed: to
         _need(state_idx, torch.int64, "state_idx", dev, contiguous=True)
         if state_idx.shape != (rows,):
             raise ValueError("state_idx must be [rows]")
-    _check(load().markov_chain_sample(
-        _ptr(base_logits), base_logits.stride(0), base_logits.stride(1),
-        _ptr(head), _ptr(embed), _ptr(prev_tokens), _ptr(temperature), _ptr(seeds),
-        _ptr(gumbel), _ptr(state_idx), float(output_multiplier), float(soft_cap),
-        rows, steps, vocab, rank,
-        int(mode) | (MARKOV_BASE_F32 if base_logits.dtype == torch.float32 else 0)
-        | (MARKOV_CACHE_F32 if cache.dtype == torch.float32 else 0),
-        _ptr(draft_tokens), draft_tokens.stride(0),
-        _ptr(cache), cache.shape[0], cache.stride(0), cache.stride(1),
-        _ptr(workspace), workspace.numel(), _stream(stream)))
+    args = (_ptr(base_logits), base_logits.stride(0), base_logits.stride(1),
+            _ptr(head), _ptr(embed), _ptr(prev_tokens), _ptr(temperature), _ptr(seeds),
+            _ptr(gumbel), _ptr(state_idx), float(output_multiplier), float(soft_cap),
+            rows, steps, vocab, rank,
+            int(mode) | (MARKOV_BASE_F32 if base_logits.dtype == torch.float32 else 0)
+            | (MARKOV_CACHE_F32 if cache.dtype == torch.float32 else 0),
+            _ptr(draft_tokens), draft_tokens.stride(0),
+            _ptr(cache), cache.shape[0], cache.stride(0), cache.stride(1))
+    if workspace is None:
+        _check(load().markov_chain_sample_noalloc(*args, _stream(stream)))
+    else:
+        _check(load().markov_chain_sample(*args, _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
-def markov_status(workspace: torch.Tensor, stream=None) -> None:
-    """Synchronise the stream and raise if the kernel reported an error."""
-    _need(workspace, torch.uint8, "workspace")
+def markov_chain_sample_noalloc(base_logits: torch.Tensor, head: torch.Tensor, embed: torch.Tensor,
+                                prev_tokens: torch.Tensor, temperature: torch.Tensor,
+                                draft_tokens: torch.Tensor, cache: torch.Tensor, **kw) -> None:
+    """markov_chain_sample without a workspace: the library's static scratch
+    holds the exchange state and no device memory is allocated."""
+    markov_chain_sample(base_logits, head, embed, prev_tokens, temperature, draft_tokens, cache,
+                        None, **kw)
+
+
+def markov_status(workspace: torch.Tensor | None, stream=None) -> None:
+    """Synchronise the stream and raise if the kernel reported an error
+    (workspace None: the scratch of markov_chain_sample_noalloc on the
+    current device)."""
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace")
     _check(load().markov_status(_ptr(workspace), _stream(stream)))
 
 

@@ -397,6 +397,23 @@ __global__ __launch_bounds__(256) void noise_fill_kernel(float* __restrict__ gum
   *dst = make_float4(out[0], out[1], out[2], out[3]);
 }
 
+// ==================================================== allocation-free scratch ==
+// markov_chain_sample_noalloc keeps the chain's workspace in this array
+// instead of a caller's buffer: 8 MiB, enough for every shape whose
+// markov_workspace_bytes is at most that (each device the library runs on
+// holds its own copy until the process ends).  Host code never uses the name
+// itself as an address: it takes the array's device address per device with
+// hipGetSymbolAddress and passes that pointer.
+constexpr size_t kScratchBytes = MARKOV_NOALLOC_MAX_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Zeroes n16 16-byte words (a fill kernel rather than a memset, so that a
+// call captured in a graph records a kernel node).
+__global__ __launch_bounds__(256) void zero_kernel(uint4* __restrict__ p, size_t n16) {
+  for (size_t k = (size_t)blockIdx.x * 256 + threadIdx.x; k < n16; k += (size_t)gridDim.x * 256)
+    p[k] = make_uint4(0, 0, 0, 0);
+}
+
 // ============================================================ chain kernel ==
 
 struct ChainParams {
@@ -421,6 +438,7 @@ struct ChainParams {
   long long cache_states;
   unsigned char* ws;
   unsigned long long ws_half;  // bytes per parity half
+  unsigned long long clear_bytes;  // bytes of the other half each call clears (<= ws_half)
   unsigned long long wait_ticks;  // bound of every cross-workgroup wait (s_memrealtime ticks)
 };
 
@@ -764,7 +782,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   {
     // Clear the other half for the next call (nobody reads it in this one).
     uint4* other = reinterpret_cast<uint4*>(p.ws + kHeader + (parity ^ 1u) * p.ws_half);
-    const size_t n16 = p.ws_half / 16;
+    const size_t n16 = p.clear_bytes / 16;
     for (size_t k = (size_t)wg * kThreads + tid; k < n16; k += (size_t)G * kThreads)
       other[k] = make_uint4(0, 0, 0, 0);
   }
@@ -1879,7 +1897,60 @@ int pick_grid(int rows, int rank, int mode, const Shape& sh, int* grid, bool* re
   return MARKOV_OK;
 }
 
-// The chain entry point's argument checks and launches.
+// The allocation-free entry point's per-device state: the scratch array's
+// device address (from hipGetSymbolAddress, with that device current) and the
+// largest workspace half any call on the device has needed so far.  Every
+// byte of a half beyond that mark is still zero (the array is zeroed once,
+// by the first call, and no call writes beyond its own need), so a call
+// clears only that much of the other half for the next call.
+constexpr int kMaxDevices = 64;
+struct ScratchState {
+  unsigned char* ptr = nullptr;
+  size_t high_water = 0;
+};
+std::mutex g_scratch_mu;
+ScratchState g_scratch[kMaxDevices];
+
+int launch_zero(void* p, size_t bytes, void* stream) {
+  const size_t n16 = bytes / 16;
+  const unsigned blocks = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                     reinterpret_cast<uint4*>(p), n16);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MARKOV_E_HIP, "scratch clearing launch: %s", hipGetErrorString(e));
+  return MARKOV_OK;
+}
+
+// The current device's scratch for a call needing need_half bytes per half:
+// its address, and how much of the other half the call must clear.  The
+// first call on a device looks the address up and enqueues the zeroing of
+// the whole array on `stream`, ahead of its chain kernel.
+int static_scratch(size_t need_half, void* stream, void** ws, size_t* clear_bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MARKOV_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MARKOV_E_UNSUPPORTED, "device %d (max %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchState& st = g_scratch[dev];
+  if (!st.ptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(MARKOV_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    const int rc = launch_zero(ptr, kScratchBytes, stream);
+    if (rc != MARKOV_OK) return rc;
+    st.ptr = static_cast<unsigned char*>(ptr);
+  }
+  if (need_half > st.high_water) st.high_water = need_half;
+  *ws = st.ptr;
+  *clear_bytes = st.high_water;
+  return MARKOV_OK;
+}
+
+// Both chain entry points.  no_alloc: the workspace is the library's static
+// scratch (workspace_bytes is its size; there is no caller's buffer to
+// check), and each call clears the scratch's high-water mark of the other
+// half instead of the whole half.
 int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_step_stride,
                  const uint16_t* head, const uint16_t* embed, const int64_t* prev_tokens,
                  const float* temperature, const int64_t* seeds, const float* gumbel,
@@ -1887,7 +1958,7 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
                  int steps, int vocab, int rank, int mode, int64_t* draft_tokens,
                  int64_t tokens_row_stride, void* cache, int64_t cache_states,
                  int64_t cache_state_stride, int64_t cache_step_stride, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 size_t workspace_bytes, void* stream, bool no_alloc) {
   const int base_f32 = (mode & MARKOV_BASE_F32) != 0, cache_f32 = (mode & MARKOV_CACHE_F32) != 0;
   const int noise_inline = (mode & MARKOV_NOISE_INLINE) != 0;
   mode &= ~kModeFlags;
@@ -1898,7 +1969,7 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
     return fail(MARKOV_E_INVAL, "MARKOV_NOISE_INLINE applies to MARKOV_MODE_GUMBEL only");
   if (noise_inline && !seeds) return fail(MARKOV_E_INVAL, "MARKOV_NOISE_INLINE needs seeds");
   if (!base_logits || !head || !embed || !prev_tokens || !temperature || !draft_tokens || !cache ||
-      !workspace)
+      (!no_alloc && !workspace))
     return fail(MARKOV_E_INVAL, "a required pointer is null");
   if (mode == MARKOV_MODE_GUMBEL && !noise_inline && !gumbel)
     return fail(MARKOV_E_INVAL, "mode 0 needs gumbel noise (or MARKOV_NOISE_INLINE)");
@@ -1906,7 +1977,8 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
   if (!aligned16(base_logits) || !aligned16(head) || !aligned16(embed) || !aligned16(cache) ||
       (gumbel && !aligned16(gumbel)))
     return fail(MARKOV_E_INVAL, "base_logits, head, embed, cache and gumbel must be 16-byte aligned");
-  if (((uintptr_t)workspace & 255u) != 0) return fail(MARKOV_E_INVAL, "workspace is not 256-byte aligned");
+  if (!no_alloc && ((uintptr_t)workspace & 255u) != 0)
+    return fail(MARKOV_E_INVAL, "workspace is not 256-byte aligned");
   if (base_step_stride < vocab || base_row_stride < 0 || base_step_stride % 8 || base_row_stride % 8)
     return fail(MARKOV_E_INVAL, "base strides (%lld, %lld) must be multiples of 8 with step stride >= vocab",
                 (long long)base_row_stride, (long long)base_step_stride);
@@ -1922,11 +1994,22 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
   // Calls with more rows than one launch takes run as consecutive launches
   // of at most kLaunchRows rows on the stream (each reads the head once);
   // they use the workspace one after another.
-  const size_t need = kHeader + 2 * call_half_bytes(rows, steps, sh.NC, mode);
+  const size_t need_half = call_half_bytes(rows, steps, sh.NC, mode);
+  const size_t need = kHeader + 2 * need_half;
+  if (no_alloc && need > kScratchBytes)
+    return fail(MARKOV_E_UNSUPPORTED,
+                "this call shape needs %zu bytes of workspace; the allocation-free entry point has %zu "
+                "(use markov_chain_sample with a workspace of markov_workspace_bytes)",
+                need, (size_t)kScratchBytes);
   if (workspace_bytes < need)
     return fail(MARKOV_E_INVAL, "workspace_bytes=%zu < %zu needed", workspace_bytes, need);
   rc = prepare_kernels();
   if (rc != MARKOV_OK) return rc;
+  size_t clear_bytes = ((workspace_bytes - kHeader) / 2) & ~(size_t)255;
+  if (no_alloc) {
+    rc = static_scratch(need_half, stream, &workspace, &clear_bytes);
+    if (rc != MARKOV_OK) return rc;
+  }
   const size_t besz = base_f32 ? 4 : 2;
   for (int r0 = 0; r0 < rows; r0 += kLaunchRows) {
     const int nr = rows - r0 < kLaunchRows ? rows - r0 : kLaunchRows;
@@ -1967,6 +2050,7 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
     p.cache_states = cache_states;
     p.ws = (unsigned char*)workspace;
     p.ws_half = ((workspace_bytes - kHeader) / 2) & ~(size_t)255;
+    p.clear_bytes = clear_bytes;
     p.wait_ticks = g_wait_ticks.load();
 
     void* args[] = {&p};
@@ -2027,20 +2111,53 @@ int markov_chain_sample(const void* base_logits, int64_t base_row_stride, int64_
   return chain_sample(base_logits, base_row_stride, base_step_stride, head, embed, prev_tokens,
                       temperature, seeds, gumbel, state_idx, output_multiplier, soft_cap, rows, steps,
                       vocab, rank, mode, draft_tokens, tokens_row_stride, cache, cache_states,
-                      cache_state_stride, cache_step_stride, workspace, workspace_bytes, stream);
+                      cache_state_stride, cache_step_stride, workspace, workspace_bytes, stream, false);
+}
+
+int markov_chain_sample_noalloc(const void* base_logits, int64_t base_row_stride,
+                                int64_t base_step_stride, const uint16_t* head, const uint16_t* embed,
+                                const int64_t* prev_tokens, const float* temperature,
+                                const int64_t* seeds, const float* gumbel, const int64_t* state_idx,
+                                float output_multiplier, float soft_cap, int rows, int steps,
+                                int vocab, int rank, int mode, int64_t* draft_tokens,
+                                int64_t tokens_row_stride, void* cache, int64_t cache_states,
+                                int64_t cache_state_stride, int64_t cache_step_stride, void* stream) {
+  g_last_error.clear();
+  return chain_sample(base_logits, base_row_stride, base_step_stride, head, embed, prev_tokens,
+                      temperature, seeds, gumbel, state_idx, output_multiplier, soft_cap, rows, steps,
+                      vocab, rank, mode, draft_tokens, tokens_row_stride, cache, cache_states,
+                      cache_state_stride, cache_step_stride, nullptr, kScratchBytes, stream, true);
 }
 
 int markov_status(void* workspace, void* stream) {
   g_last_error.clear();
-  if (!workspace) return fail(MARKOV_E_INVAL, "null workspace");
+  const bool no_alloc = workspace == nullptr;
+  if (no_alloc) {
+    // the allocation-free entry point's scratch on the current device
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MARKOV_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(MARKOV_E_UNSUPPORTED, "device %d (max %d)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    workspace = g_scratch[dev].ptr;
+    if (!workspace) return MARKOV_OK;  // no allocation-free call has run on this device
+  }
   uint32_t hdr[2] = {0, 0};
   hipError_t e = hipMemcpyAsync(hdr, workspace, sizeof hdr, hipMemcpyDeviceToHost, (hipStream_t)stream);
   if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return fail(MARKOV_E_HIP, "status read: %s", hipGetErrorString(e));
   if (hdr[1] == 0) return MARKOV_OK;
-  static const uint32_t zero = 0;
-  e = hipMemcpyAsync((char*)workspace + 4, &zero, 4, hipMemcpyHostToDevice, (hipStream_t)stream);
-  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (no_alloc && (hdr[1] & MARKOV_DEVERR_TIMEOUT)) {
+    // A wait gave up: the scratch may hold a half-used exchange.  Zero all
+    // of it (the caller cannot), error word included.
+    const int rc = launch_zero(workspace, kScratchBytes, stream);
+    if (rc != MARKOV_OK) return rc;
+    e = hipStreamSynchronize((hipStream_t)stream);
+  } else {
+    static const uint32_t zero = 0;
+    e = hipMemcpyAsync((char*)workspace + 4, &zero, 4, hipMemcpyHostToDevice, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  }
   if (e != hipSuccess) return fail(MARKOV_E_HIP, "status clear: %s", hipGetErrorString(e));
   return fail(MARKOV_E_DEVICE, "device error bits 0x%x:%s%s%s", hdr[1],
               (hdr[1] & MARKOV_DEVERR_BAD_TOKEN) ? " previous token outside [0, V);" : "",

@@ -158,3 +158,23 @@ def test_binding_refuses_other_element_types():
     base = torch.zeros(1, 1, 16, dtype=torch.float16)
     with pytest.raises(TypeError):
         lm.markov_chain_sample(base, base, base, base, base, base, base, base)
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch():
+    """markov_chain_sample_noalloc takes the shapes whose workspace fits its
+    static scratch and refuses larger ones on the host (fake, never
+    dereferenced pointers; no HIP call is made before the refusal)."""
+    lib = lm.load()
+    P = 1 << 20
+    rows, steps, vocab = 64, 256, 129280
+    assert lm.markov_workspace_bytes(rows, steps, vocab, 256, 0) > 8 << 20
+    rc = lib.markov_chain_sample_noalloc(
+        P, steps * vocab, vocab, P, P, P, P, P, P, None, 1.0, 0.0, rows, steps, vocab, 256,
+        lm.MARKOV_NOISE_INLINE, P, steps, P, rows, steps * vocab, vocab, None)
+    assert rc == lm.MARKOV_E_UNSUPPORTED
+    assert "workspace" in lm.markov_last_error()
+    # the argument checks are those of markov_chain_sample
+    rc = lib.markov_chain_sample_noalloc(
+        None, 8 * 1024, 1024, P, P, P, P, P, P, None, 1.0, 0.0, 1, 8, 1024, 256, 0, P, 8, P, 1,
+        8 * 1024, 1024, None)
+    assert rc == lm.MARKOV_E_INVAL
