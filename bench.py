@@ -235,6 +235,10 @@ def main() -> int:
                     help="mode 0: noise drawn inside the chain kernel, or by the noise fill "
                          "kernel on a side stream; auto: inline up to 8 rows (the chain's idle "
                          "waves draw it), side stream beyond")
+    ap.add_argument("--batch-path", choices=("auto", "persistent", "step"), default="auto",
+                    help="mode 0 with the noise in memory: persistent launches of at most 64 rows, "
+                         "or one step-kernel launch per position over all rows; auto: step kernels "
+                         "beyond 64 rows")
     ap.add_argument("--cold", type=int, default=50, help="cold calls timed after the main loop")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -344,6 +348,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
+    binding.markov_set_batch_path({"auto": 0, "persistent": 1, "step": 2}[args.batch_path])
     w = synth.workload(args.workload)
     noise = args.noise if args.noise != "auto" else ("inline" if w.real_rows <= 8 else "side")
     inline = noise == "inline" and w.mode == 0
@@ -375,6 +380,7 @@ def main() -> int:
                    "mode": "gumbel" if w.mode == 0 else "invcdf",
                    "grid": binding.markov_grid(w.rows, w.N, w.V, w.r, w.mode),
                    "noise": "inline" if inline else ("side stream" if w.mode == 0 else "none"),
+                   "batch_path": args.batch_path,
                    "step": ("chain kernel drawing its noise inline (one launch)" if inline
                             else "chain kernel (one launch)" if w.mode == 1
                             else "noise fill on a side stream + chain kernel") + ", " + m["issue"]},

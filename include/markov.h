@@ -278,6 +278,21 @@ const char* markov_last_error(void);
 int markov_set_grid(int g);
 
 /*
+ * markov_set_batch_path: tuning and testing knob for MARKOV_MODE_GUMBEL calls
+ * with the noise in memory.  0 (the default): batches of at most 64 rows run
+ * as one persistent launch, larger batches as one step-kernel launch per
+ * draft position over all rows (fused_markov page, FusedMarkovSampler: the
+ * fused loop that serves batches beyond the persistent chain; muse_spark
+ * markov page, MarkovSampler: per-row arrival counters whose last block
+ * picks the winner).  1: always persistent launches of at most 64 rows, one
+ * after another.  2: always step kernels (the workspace must then hold
+ * that path's layout, which for at most 64 rows markov_workspace_bytes does
+ * not promise).  Outputs do not depend on it.  Process-wide; returns the
+ * previous value.
+ */
+int markov_set_batch_path(int path);
+
+/*
  * markov_set_wait_limit: testing and debugging knob.  Sets the bound, in
  * microseconds, of every cross-workgroup wait of later markov_chain_sample
  * calls (sharded_markov page, DSparkShardedMarkovSampler: timeout_ms bounds

@@ -40,6 +40,7 @@ EXPORTS = (
     "markov_status",
     "markov_last_error",
     "markov_set_grid",
+    "markov_set_batch_path",
     "markov_set_wait_limit",
     "markov_grid",
 )
@@ -84,6 +85,8 @@ def load():
         lib.markov_last_error.argtypes = []
         lib.markov_set_grid.restype = i32
         lib.markov_set_grid.argtypes = [i32]
+        lib.markov_set_batch_path.restype = i32
+        lib.markov_set_batch_path.argtypes = [i32]
         lib.markov_set_wait_limit.restype = ctypes.c_longlong
         lib.markov_set_wait_limit.argtypes = [ctypes.c_longlong]
         lib.markov_grid.restype = i32
@@ -237,6 +240,12 @@ def markov_last_error() -> str:
 
 def markov_set_grid(g: int) -> int:
     return int(load().markov_set_grid(int(g)))
+
+
+def markov_set_batch_path(path: int) -> int:
+    """0 auto, 1 persistent launches, 2 step kernels (mode 0, noise in
+    memory).  Returns the previous value."""
+    return int(load().markov_set_batch_path(int(path)))
 
 
 def markov_set_wait_limit(us: int) -> int:

@@ -484,15 +484,21 @@ __host__ __device__ inline size_t half_bytes_needed(int rows, int N, int NC, int
   return (b + 255) & ~(size_t)255;
 }
 
-// A call of more than kLaunchRows rows runs as launches of kLaunchRows rows
-// and one of the rest, one after another in the same workspace: its half
-// must hold the larger of their layouts.
-__host__ inline size_t call_half_bytes(int rows, int N, int NC, int mode) {
+// A call of more than kLaunchRows rows runs either as persistent launches of
+// kLaunchRows rows and one of the rest, one after another in the same
+// workspace, or (mode 0) as one step-kernel launch per position over all its
+// rows: its half must hold the larger of those layouts.
+__host__ size_t step_half_bytes_host(int rows, int rank);
+__host__ inline size_t call_half_bytes(int rows, int N, int NC, int mode, int rank) {
   const int full = rows < kLaunchRows ? rows : kLaunchRows;
   size_t b = half_bytes_needed(full, N, NC, mode);
   const int tail = rows % kLaunchRows;
   if (rows > kLaunchRows && tail != 0) {
     const size_t t = half_bytes_needed(tail, N, NC, mode);
+    if (t > b) b = t;
+  }
+  if (rows > kLaunchRows && mode == 0) {
+    const size_t t = step_half_bytes_host(rows, rank);
     if (t > b) b = t;
   }
   return b;
@@ -1771,11 +1777,338 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   if (wg == 0 && tid == 0 && !s_abort) st_agent32(header, parity ^ 1u);
 }
 
+// ============================================================= step kernel ==
+// Batches beyond one persistent launch (more than kLaunchRows rows, mode 0):
+// one launch per draft position, as the pages' fused loop for large batches
+// (fused_markov page, FusedMarkovSampler: the bias GEMM plus the sampling
+// work, launched per position; muse_spark markov page, MarkovSampler: the
+// blocks of a row count their arrivals and the last one picks the winner).
+// Here the bias GEMM is fused into the step kernel (the bias never goes to
+// memory):
+//  * workgroup c owns chunk c (8 groups of 16384 / r vocab ids, one per
+//    wave); each wave loads its group's head into VGPRs once per step and
+//    reuses it for every request row (v_mfma_f32_16x16x32_bf16 passes of 16
+//    rows, embeddings from LDS);
+//  * the epilogue (bias -> bf16, + base, transform, cache store, score)
+//    runs in batches of 8 rows with 16-byte vectors, the next two batches'
+//    base logits and noise in flight;
+//  * each workgroup folds its best key of every row into the row's slot
+//    with an agent-scope atomic max (fire and forget), then counts itself on
+//    the step's arrival counter; the workgroup that arrives last writes the
+//    step's tokens and gathers the winners' embeddings for the next step.
+// No workgroup ever waits for another, so the launch needs no co-residency.
+//
+// Workspace half layout of this path (the parity protocol of the persistent
+// kernel: a call uses half P and its step-0 launch clears the other half
+// for the next call; the last launch flips P):
+//   arrive[2] u32 (256 bytes)          arrival counters, by step parity
+//   best[2][rows][kBestStride] u64     each row's best key, by step parity
+//                                      (one 128-byte line per row)
+//   emb[2][rows][R] bf16               the current tokens' embeddings
+// The last workgroup of step i zeroes arrive[i & 1] and best[i & 1] after
+// reading them, so step i + 2 finds them zero.
+
+constexpr int kBestStride = 16;  // u64 words per row's best key (a 128-byte line)
+constexpr int kPrefetch = 3;     // epilogue batches whose inputs are in flight
+
+__host__ __device__ inline size_t step_half_bytes(int rows, int R) {
+  const size_t b = 256 + (size_t)2 * rows * kBestStride * 8 + (size_t)2 * rows * R * 2;
+  return (b + 255) & ~(size_t)255;
+}
+
+template <int R, bool FL>
+__global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int step) {
+  constexpr int RPG = 16384 / R;
+  constexpr int KSEG = R / 8;
+  constexpr int ES = emb_stride<R>();
+  constexpr int BS = bias_stride<R>();
+  constexpr int IPL = RPG / kLanesPerRow;
+  constexpr int kBlock = kLaunchRows;  // rows whose embeddings sit in LDS at once
+  const bool base_f32 = FL && p.base_f32;
+  const bool cache_f32 = FL && p.cache_f32;
+
+  __shared__ int s_state[kBlock];
+  __shared__ int s_active[kBlock];
+  __shared__ float s_T[kBlock];
+  __shared__ double s_rT[kBlock];
+  __shared__ uint64_t s_key[kWaves][kBlock];
+  __shared__ float s_bias[kWaves][kRowPass * BS];
+  __shared__ int s_last;
+  __shared__ uint32_t s_parity;
+  extern __shared__ uint4 s_e[];  // [kBlock][ES]; the last workgroup reuses it for tokens
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = blockIdx.x;
+  const int rows = p.rows, V = p.V, NG = p.NG, G = p.G;
+  uint32_t* header = reinterpret_cast<uint32_t*>(p.ws);
+  const int rr = lane >> 3, q = lane & 7;
+  const int g = c * kWaves + wave;  // this wave's group
+  const int v0 = g * RPG + q * IPL; // this lane's first vocab id in the batch layout
+
+  // The head of this wave's group, in flight while the rows are set up.
+  uint4 h[kSlots];
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) h[s] = load_head_tile_clamped<R>(p.head, g < NG ? g : NG - 1, s, lane, V);
+  if (tid == 0) s_parity = ld_agent32(header);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  const uint32_t parity = s_parity & 1u;
+  unsigned char* half = p.ws + kHeader + parity * p.ws_half;
+  uint32_t* arrive = reinterpret_cast<uint32_t*>(half);
+  uint64_t* best = reinterpret_cast<uint64_t*>(half + 256);
+  uint16_t* emb = reinterpret_cast<uint16_t*>(half + 256 + (size_t)2 * rows * kBestStride * 8);
+  uint64_t* best_i = best + (size_t)(step & 1) * rows * kBestStride;
+  if (step == 0) {
+    // Clear the other half for the next call (nobody reads it in this one).
+    uint4* other = reinterpret_cast<uint4*>(p.ws + kHeader + (parity ^ 1u) * p.ws_half);
+    const size_t n16 = p.clear_bytes / 16;
+    for (size_t k = (size_t)c * kThreads + tid; k < n16; k += (size_t)G * kThreads) other[k] = make_uint4(0, 0, 0, 0);
+  }
+  float* sb = s_bias[wave];
+
+  struct In {
+    uint32_t bw[IPL];
+    float nz[IPL];
+  };
+  // Batch inputs of rows b0 .. b0 + 7 of the current block (row rr of the
+  // batch in this lane), for active rows with valid ids only.
+  auto load_in = [&](int rb, int b0, In& in) {
+#pragma unroll
+    for (int e = 0; e < IPL; ++e) in.bw[e] = 0, in.nz[e] = 0.0f;
+    const int bl = b0 + rr;
+    int b = rb + bl;
+    asm volatile("" : "+v"(b));
+    if (bl < kBlock && b < rows && g < NG && v0 < V && s_active[bl]) {
+      const long long at = (long long)b * p.base_rs + (long long)step * p.base_ss + v0;
+      if (base_f32) {
+        const uint4* brow = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.base) + at);
+#pragma unroll
+        for (int e4 = 0; e4 < IPL / 4; ++e4) {
+          const uint4 t = brow[e4];
+          in.bw[4 * e4] = t.x, in.bw[4 * e4 + 1] = t.y, in.bw[4 * e4 + 2] = t.z, in.bw[4 * e4 + 3] = t.w;
+        }
+      } else {
+        const uint16_t* brow = reinterpret_cast<const uint16_t*>(p.base) + at;
+        if constexpr (IPL == 8) {
+          const uint4 t = *reinterpret_cast<const uint4*>(brow);
+          in.bw[0] = t.x, in.bw[1] = t.y, in.bw[2] = t.z, in.bw[3] = t.w;
+        } else {
+          const uint2 t = *reinterpret_cast<const uint2*>(brow);
+          in.bw[0] = t.x, in.bw[1] = t.y;
+        }
+      }
+      if (s_T[bl] > 0.0f) {
+        const float4* grow = reinterpret_cast<const float4*>(p.gumbel + ((size_t)b * p.N + step) * (size_t)V + v0);
+#pragma unroll
+        for (int e4 = 0; e4 < IPL / 4; ++e4) {
+          const float4 t = grow[e4];
+          in.nz[4 * e4] = t.x, in.nz[4 * e4 + 1] = t.y, in.nz[4 * e4 + 2] = t.z, in.nz[4 * e4 + 3] = t.w;
+        }
+      }
+    }
+  };
+
+  for (int rb = 0; rb < rows; rb += kBlock) {
+    const int nbr = rows - rb < kBlock ? rows - rb : kBlock;
+    // ---- the block's rows: state, activity, temperature; embeddings.
+    if (tid < nbr) {
+      const int b = rb + tid;
+      const int64_t st = p.state_idx ? p.state_idx[b] : (int64_t)b;
+      const int64_t tok = p.prev[b];
+      const float T = p.temp[b];
+      int active = st >= 0;
+      if (active && st >= p.cache_states) {
+        active = 0;
+        if (c == 0 && step == 0)
+          __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_BAD_STATE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (active && (tok < 0 || tok >= V)) {
+        active = 0;
+        if (c == 0 && step == 0)
+          __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_BAD_TOKEN, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      s_state[tid] = (int)st;
+      s_active[tid] = active;
+      s_T[tid] = T;
+      s_rT[tid] = T > 0.0f ? 1.0 / (double)T : 0.0;
+    }
+    if (lane == 0)
+      for (int k = 0; k < kBlock; ++k) s_key[wave][k] = kNoCandidate;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    for (int k = tid; k < nbr * KSEG; k += kThreads) {
+      const int bl = k / KSEG, seg = k - bl * KSEG;
+      if (!s_active[bl]) continue;
+      const uint16_t* src = step == 0 ? p.embed + (size_t)p.prev[rb + bl] * R
+                                      : emb + ((size_t)(step & 1) * rows + rb + bl) * R;
+      s_e[bl * ES + seg] = *reinterpret_cast<const uint4*>(src + seg * 8);
+    }
+    // the first batches' inputs, then the embeddings visible to every wave
+    const int nbat = (nbr + kBatch - 1) / kBatch;
+    In in[kPrefetch];
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      if (k < nbat) load_in(rb, k * kBatch, in[k]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+    for (int t = 0; t < nbat; ++t) {
+      const int b0 = t * kBatch;
+      if ((t & 1) == 0) {
+        const int np = nbr - b0 < kRowPass ? nbr - b0 : kRowPass;
+        group_bias<R>(h, s_e, b0, np, lane, sb);
+      }
+      const In cur = in[0];
+#pragma unroll
+      for (int k = 0; k + 1 < kPrefetch; ++k) in[k] = in[k + 1];
+      if (t + kPrefetch < nbat) load_in(rb, (t + kPrefetch) * kBatch, in[kPrefetch - 1]);
+      // ---- epilogue of the batch (row rr of the batch, IPL ids from v0)
+      const int bl = b0 + rr;
+      const bool ok = bl < nbr && g < NG && v0 < V && s_active[bl];
+      const float T = s_T[bl < kBlock ? bl : 0];
+      const double rT = s_rT[bl < kBlock ? bl : 0];
+      const float* sbt = sb + (t & 1) * kBatch * BS;
+      float bsum[IPL];
+#pragma unroll
+      for (int e4 = 0; e4 < IPL / 4; ++e4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(sbt + rr * BS + q * IPL + 4 * e4);
+        bsum[4 * e4] = v4.x, bsum[4 * e4 + 1] = v4.y, bsum[4 * e4 + 2] = v4.z, bsum[4 * e4 + 3] = v4.w;
+      }
+      float x[IPL];
+#pragma unroll
+      for (int e = 0; e < IPL; ++e) {
+        const uint32_t w = cur.bw[e / 2];
+        const float base = base_f32 ? __uint_as_float(cur.bw[e])
+                                    : __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        x[e] = __fmul_rn(__fadd_rn(base, bf16_round(bsum[e])), p.mult);
+      }
+      if (p.has_cap) {
+#pragma unroll
+        for (int e = 0; e < IPL; ++e) x[e] = __fmul_rn(tanhf(__fmul_rn(x[e], p.inv_cap)), p.cap);
+      }
+      uint32_t cw[IPL / 2];
+      float z[IPL];
+#pragma unroll
+      for (int e = 0; e < IPL / 2; ++e) {
+        cw[e] = f32x2_to_bf16x2(x[2 * e], x[2 * e + 1]);
+        z[2 * e] = cache_f32 ? x[2 * e] : __uint_as_float(cw[e] << 16);
+        z[2 * e + 1] = cache_f32 ? x[2 * e + 1] : __uint_as_float(cw[e] & 0xFFFF0000u);
+      }
+      if (ok) {
+        const long long at = (long long)s_state[bl] * p.cache_rs + (long long)step * p.cache_ss + v0;
+        if (cache_f32) {
+          u32x4_t* crow = reinterpret_cast<u32x4_t*>(reinterpret_cast<float*>(p.cache) + at);
+#pragma unroll
+          for (int e4 = 0; e4 < IPL / 4; ++e4)
+            __builtin_nontemporal_store((u32x4_t){__float_as_uint(z[4 * e4]), __float_as_uint(z[4 * e4 + 1]),
+                                                  __float_as_uint(z[4 * e4 + 2]), __float_as_uint(z[4 * e4 + 3])},
+                                        crow + e4);
+        } else {
+          uint16_t* crow = reinterpret_cast<uint16_t*>(p.cache) + at;
+          if constexpr (IPL == 8)
+            __builtin_nontemporal_store((u32x4_t){cw[0], cw[1], cw[2], cw[3]}, reinterpret_cast<u32x4_t*>(crow));
+          else
+            __builtin_nontemporal_store((u32x2_t){cw[0], cw[1]}, reinterpret_cast<u32x2_t*>(crow));
+        }
+      }
+      if (T > 0.0f) {
+        if (T != 1.0f) {
+#pragma unroll
+          for (int e = 0; e < IPL; ++e) z[e] = div_by_recip(z[e], rT);
+        }
+#pragma unroll
+        for (int e = 0; e < IPL; ++e) z[e] = __fadd_rn(z[e], cur.nz[e]);
+      }
+      // this lane's first NaN, else first maximum; then the row's over its 8 lanes
+      int kbest = INT_MIN;
+      uint32_t ebest = 0, enan = IPL;
+#pragma unroll
+      for (int e = 0; e < IPL; ++e) {
+        const bool isn = isnan(z[e]);
+        enan = (isn && enan == IPL) ? e : enan;
+        const int k = isn ? INT_MIN : order_key(__fadd_rn(z[e], 0.0f));
+        ebest = k > kbest ? e : ebest;
+        kbest = k > kbest ? k : kbest;
+      }
+      if (!ok) kbest = INT_MIN, enan = IPL;
+      const int gmax = group8_imax(kbest);
+      const uint32_t gid = group8_umin(kbest != INT_MIN && kbest == gmax ? (uint32_t)v0 + ebest : 0xFFFFFFFFu);
+      const uint32_t gnan = group8_umin(enan < IPL ? (uint32_t)v0 + enan : 0xFFFFFFFFu);
+      if (q == 0 && ok) {
+        s_key[wave][bl] = gnan != 0xFFFFFFFFu ? ((0xFFFFFFFFull << 32) | (0xFFFFFFFFu - gnan))
+                          : gmax != INT_MIN ? (((uint64_t)score_ord(order_key_inv(gmax)) << 32) | (0xFFFFFFFFu - gid))
+                                            : kNoCandidate;
+      }
+    }
+    // ---- the block's keys: the workgroup's best per row into the row's slot.
+    __syncthreads();
+    if (tid < nbr && s_active[tid]) {
+      uint64_t K = kNoCandidate;
+      for (int w = 0; w < kWaves; ++w) K = umax64(K, s_key[w][tid]);
+      if (K != kNoCandidate)
+        __hip_atomic_fetch_max(best_i + (size_t)(rb + tid) * kBestStride, K, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  }
+
+  // ---- arrival; the last workgroup of the step picks every row's winner.
+  if (tid == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(arrive + (step & 1), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == (uint32_t)(G - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  int* s_tok = reinterpret_cast<int*>(s_e);  // rows <= MARKOV_MAX_ROWS tokens (16 KiB)
+  for (int b = tid; b < rows; b += kThreads) {
+    const int64_t st = p.state_idx ? p.state_idx[b] : (int64_t)b;
+    const int64_t tok0 = p.prev[b];
+    const bool active = st >= 0 && st < p.cache_states && tok0 >= 0 && tok0 < V;
+    int tok = -1;
+    if (active) {
+      const uint64_t K = ld_agent(best_i + (size_t)b * kBestStride);
+      const uint32_t win = key_id(K);
+      tok = (K > kNoCandidate && win < (uint32_t)V) ? (int)win : 0;
+      p.tokens[(long long)b * p.tok_rs + step] = tok;
+      st_agent(best_i + (size_t)b * kBestStride, 0);  // for step + 2
+    }
+    s_tok[b] = tok;
+  }
+  if (tid == 0) st_agent32(arrive + (step & 1), 0u);
+  __syncthreads();
+  if (step + 1 < p.N) {
+    // the winners' embeddings for the next step, 16 bytes per thread and load
+    uint16_t* dst = emb + (size_t)((step + 1) & 1) * rows * R;
+    for (int k = tid; k < rows * KSEG; k += kThreads) {
+      const int b = k / KSEG, seg = k - b * KSEG;
+      const int tok = s_tok[b];
+      if (tok >= 0)
+        *reinterpret_cast<uint4*>(dst + (size_t)b * R + seg * 8) =
+            *reinterpret_cast<const uint4*>(p.embed + (size_t)tok * R + seg * 8);
+    }
+  } else if (tid == 0) {
+    // every launch of the call has read the parity by now
+    st_agent32(header, parity ^ 1u);
+  }
+}
+
+__host__ size_t step_half_bytes_host(int rows, int rank) { return step_half_bytes(rows, rank); }
+
+template <bool FL>
+const void* step_kernel_for(int rank) {
+  return rank == 256 ? (const void*)step_kernel<256, FL> : (const void*)step_kernel<512, FL>;
+}
+
 // ================================================================= host ==
 
 thread_local std::string g_last_error;
 std::atomic<int> g_grid_override{0};
 std::atomic<unsigned long long> g_wait_ticks{kTimeoutTicks};
+std::atomic<int> g_batch_path{0};  // 0 auto, 1 persistent launches, 2 step kernels (mode 0)
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
@@ -1866,6 +2199,13 @@ int prepare_kernels() {
                                              kLaunchRows * (rank / 8 + 1) * 16);
           if (e != hipSuccess && err == hipSuccess) err = e;
         }
+    for (int rank : {256, 512})
+      for (int fl = 0; fl < 2; ++fl) {
+        hipError_t e = hipFuncSetAttribute(fl ? step_kernel_for<true>(rank) : step_kernel_for<false>(rank),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           kLaunchRows * (rank / 8 + 1) * 16);
+        if (e != hipSuccess && err == hipSuccess) err = e;
+      }
   });
   if (err != hipSuccess) return fail(MARKOV_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(err));
   return MARKOV_OK;
@@ -1994,7 +2334,7 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
   // Calls with more rows than one launch takes run as consecutive launches
   // of at most kLaunchRows rows on the stream (each reads the head once);
   // they use the workspace one after another.
-  const size_t need_half = call_half_bytes(rows, steps, sh.NC, mode);
+  const size_t need_half = call_half_bytes(rows, steps, sh.NC, mode, rank);
   const size_t need = kHeader + 2 * need_half;
   if (no_alloc && need > kScratchBytes)
     return fail(MARKOV_E_UNSUPPORTED,
@@ -2011,6 +2351,67 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
     if (rc != MARKOV_OK) return rc;
   }
   const size_t besz = base_f32 ? 4 : 2;
+  // Mode 0 with the noise in memory: batches beyond one persistent launch
+  // run one step kernel per position over all rows (or any batch, when the
+  // knob asks for that path).
+  const int path = g_batch_path.load();
+  const bool use_step = mode == MARKOV_MODE_GUMBEL && !noise_inline &&
+                        (path == 2 || (path == 0 && rows > kLaunchRows));
+  if (use_step) {
+    const size_t step_need = kHeader + 2 * step_half_bytes(rows, rank);
+    if (workspace_bytes < step_need)
+      return fail(MARKOV_E_INVAL, "workspace_bytes=%zu < %zu needed by the step-kernel path", workspace_bytes,
+                  step_need);
+    if (no_alloc && need_half < step_half_bytes(rows, rank)) {
+      size_t cb = 0;
+      rc = static_scratch(step_half_bytes(rows, rank), stream, &workspace, &cb);
+      if (rc != MARKOV_OK) return rc;
+      clear_bytes = cb;
+    }
+    ChainParams p = {};
+    p.base = base_logits;
+    p.base_f32 = base_f32;
+    p.base_rs = base_row_stride;
+    p.base_ss = base_step_stride;
+    p.head = head;
+    p.embed = embed;
+    p.prev = prev_tokens;
+    p.temp = temperature;
+    p.seeds = seeds;
+    p.gumbel = gumbel;
+    p.state_idx = state_idx;
+    p.mult = output_multiplier;
+    p.cap = soft_cap;
+    p.inv_cap = soft_cap > 0.0f ? 1.0f / soft_cap : 1.0f;
+    p.has_cap = soft_cap > 0.0f;
+    p.rows = rows;
+    p.row_base = 0;
+    p.N = steps;
+    p.V = vocab;
+    p.NG = sh.NG;
+    p.NC = sh.NC;
+    p.G = sh.NC;  // one workgroup per chunk
+    p.tokens = draft_tokens;
+    p.tok_rs = tokens_row_stride;
+    p.cache = cache;
+    p.cache_f32 = cache_f32;
+    p.cache_rs = cache_state_stride;
+    p.cache_ss = cache_step_stride;
+    p.cache_states = cache_states;
+    p.ws = (unsigned char*)workspace;
+    p.ws_half = ((workspace_bytes - kHeader) / 2) & ~(size_t)255;
+    p.clear_bytes = clear_bytes;
+    p.wait_ticks = 0;
+    const void* kern = (base_f32 || cache_f32) ? step_kernel_for<true>(rank) : step_kernel_for<false>(rank);
+    const size_t shmem = (size_t)kLaunchRows * (rank / 8 + 1) * 16;
+    for (int i = 0; i < steps; ++i) {
+      int step = i;
+      void* args[] = {&p, &step};
+      hipError_t e = hipLaunchKernel(kern, dim3(sh.NC), dim3(kThreads), args, (unsigned)shmem, (hipStream_t)stream);
+      if (e != hipSuccess) return fail(MARKOV_E_HIP, "step kernel launch (step %d): %s", i, hipGetErrorString(e));
+    }
+    return MARKOV_OK;
+  }
   for (int r0 = 0; r0 < rows; r0 += kLaunchRows) {
     const int nr = rows - r0 < kLaunchRows ? rows - r0 : kLaunchRows;
     int G = 0;
@@ -2078,7 +2479,7 @@ size_t markov_workspace_bytes(int rows, int steps, int vocab, int rank, int mode
   mode &= ~kModeFlags;
   Shape sh;
   if (check_shape(rows, steps, vocab, rank, mode, &sh) != MARKOV_OK) return 0;
-  return kHeader + 2 * call_half_bytes(rows, steps, sh.NC, mode);
+  return kHeader + 2 * call_half_bytes(rows, steps, sh.NC, mode, rank);
 }
 
 int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps, int vocab,
@@ -2168,6 +2569,8 @@ int markov_status(void* workspace, void* stream) {
 const char* markov_last_error(void) { return g_last_error.c_str(); }
 
 int markov_set_grid(int g) { return g_grid_override.exchange(g < 0 ? 0 : g); }
+
+int markov_set_batch_path(int path) { return g_batch_path.exchange(path < 0 || path > 2 ? 0 : path); }
 
 long long markov_set_wait_limit(long long us) {
   const unsigned long long t = us < 0 ? kTimeoutTicks : (unsigned long long)us * kTicksPerUs;
