@@ -257,6 +257,30 @@ __device__ __forceinline__ void st_agent32(uint32_t* p, uint32_t v) {
 
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
+// ---------------------------------------------------------------- tracing --
+// Built with -DMARKOV_TRACE (a separate library; off by default), the chain
+// and step kernels stamp the 100 MHz s_memrealtime clock at fixed points of
+// every step, one thread (thread 0) per workgroup, into trace_buf
+// [workgroup][step][phase]; markov_trace_read copies it to the host.  Chain
+// kernel phases: 0 step start, 1 local work done (wave 0), 2 keys published,
+// 3 reducer partials / inverse-CDF decision published, 4 winner known
+// (wave 0), 5 step end; step 0 also holds 6 kernel entry and 7 prologue
+// done.  Step kernel phases (per launch): 0 entry, 1 first block's inputs
+// issued, 2 all blocks done, 3 the last workgroup's picks done.
+constexpr int kTraceWGs = 1024, kTraceSteps = 32, kTracePhases = 8;
+#ifdef MARKOV_TRACE
+__device__ unsigned long long trace_buf[kTraceWGs * kTraceSteps * kTracePhases];
+#define TRACE_STAMP(wgi, step, ph)                                                            \
+  do {                                                                                        \
+    if (threadIdx.x == 0 && (step) < kTraceSteps && (wgi) < kTraceWGs)                        \
+      trace_buf[((size_t)(wgi) * kTraceSteps + (step)) * kTracePhases + (ph)] = now_ticks(); \
+  } while (0)
+#else
+#define TRACE_STAMP(wgi, step, ph) \
+  do {                             \
+  } while (0)
+#endif
+
 // c / T correctly rounded to fp32 (the IEEE quotient), as c times rT, the
 // fp64 reciprocal of T correctly rounded, rounded once to fp32.  For fp32 c
 // and T > 0 the fp64 product is within 2^-52 of c / T relatively, and a
@@ -704,6 +728,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   const int rows = p.rows, N = p.N, V = p.V, G = p.G, NC = p.NC, NG = p.NG;
   uint32_t* header = reinterpret_cast<uint32_t*>(p.ws);
   const uint64_t deadline = now_ticks() + p.wait_ticks;
+  TRACE_STAMP(wg, 0, 6);
   // In the epilogue lane l owns group row lr (r = 512 groups have 32 rows:
   // lanes 32..63 have none).
   const int lr = (R == 256) ? lane : (lane & 31);
@@ -1237,8 +1262,11 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     bool leader_wave = false;
     if constexpr (MODE == 1)
       for (int b = wg; b < rows; b += G) leader_wave = leader_wave || (((b / G) % kWaves) == wave && s_active[b]);
+    TRACE_STAMP(wg, 0, 7);
     for (int i = 0; i < N; ++i) {
+      TRACE_STAMP(wg, i, 0);
       local_work(i);
+      TRACE_STAMP(wg, i, 1);
       if (MODE == 1 && ahead && i + 1 < N) prefetch(i + 1);
       if (stage && !base_f32 && i + 1 < N && !leader_wave) {
         // Parked at once: the wait for the loads overlaps the wait for the
@@ -1249,6 +1277,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       if (MODE == 0) {
         __syncthreads();
         publish(i);
+        TRACE_STAMP(wg, i, 2);
         if (ahead && i + 1 < N) prefetch(i + 1);
       }
 
@@ -1388,6 +1417,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
               st_agent(L.part + (((size_t)i * rows + b) * kPartCopies + lane) * kPartStride + wg, K);
           }
         }
+        TRACE_STAMP(wg, i, 3);
         for (int b = many ? rows : wave; b < rows; b += kWaves) {
           if (!s_active[b]) continue;
           const uint64_t* slots = NR > 1 ? L.part + (((size_t)i * rows + b) * kPartCopies + wg % kPartCopies) * kPartStride
@@ -1442,6 +1472,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           }
           uint32_t win = key_id(best);
           if (win >= (uint32_t)V) win = 0;  // only after a timeout
+          TRACE_STAMP(wg, i, 4);
           if (next) {
             if (win != spec && lane < KSEG) ev = *reinterpret_cast<const uint4*>(p.embed + (size_t)win * R + lane * 8);
             if (lane < KSEG) s_e[b * ES + lane] = ev;
@@ -1607,6 +1638,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           // call with the tokens copied likewise).
           if (lane < kDecCopies) st_agent(L.dec + ((size_t)i * kDecCopies + lane) * rows + b, dec);
         }
+        TRACE_STAMP(wg, i, 3);
         if (stage && !base_f32 && i + 1 < N && leader_wave) {
           stage_load(i + 1);
           stage_park();
@@ -1736,8 +1768,10 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           }
           if (mine) s_tok[b] = (uint32_t)d < (uint32_t)V ? (int)(uint32_t)d : 0;
         }
+        TRACE_STAMP(wg, i, 4);
       }
       __syncthreads();
+      TRACE_STAMP(wg, i, 5);
       if (s_abort) break;
 
       // ---- the winners: tokens out, next embeddings in.
@@ -1844,6 +1878,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   const int rr = lane >> 3, q = lane & 7;
   const int g = c * kWaves + wave;  // this wave's group
   const int v0 = g * RPG + q * IPL; // this lane's first vocab id in the batch layout
+  TRACE_STAMP(c, step, 0);
 
   // The head of this wave's group, in flight while the rows are set up.
   uint4 h[kSlots];
@@ -1955,6 +1990,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (rb == 0) TRACE_STAMP(c, step, 1);
 
     for (int t = 0; t < nbat; ++t) {
       const int b0 = t * kBatch;
@@ -2056,6 +2092,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   }
 
   // ---- arrival; the last workgroup of the step picks every row's winner.
+  TRACE_STAMP(c, step, 2);
   if (tid == 0) {
     const uint32_t old = __hip_atomic_fetch_add(arrive + (step & 1), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     s_last = old == (uint32_t)(G - 1);
@@ -2094,6 +2131,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
     // every launch of the call has read the parity by now
     st_agent32(header, parity ^ 1u);
   }
+  __syncthreads();
+  TRACE_STAMP(c, step, 3);
 }
 
 __host__ size_t step_half_bytes_host(int rows, int rank) { return step_half_bytes(rows, rank); }
@@ -2571,6 +2610,24 @@ const char* markov_last_error(void) { return g_last_error.c_str(); }
 int markov_set_grid(int g) { return g_grid_override.exchange(g < 0 ? 0 : g); }
 
 int markov_set_batch_path(int path) { return g_batch_path.exchange(path < 0 || path > 2 ? 0 : path); }
+
+#ifdef MARKOV_TRACE
+// Trace builds only (not part of the ABI in markov.h): copies the first
+// `bytes` of trace_buf ([1024 workgroups][32 steps][8 phases] u64 ticks of
+// the 100 MHz clock) to host memory and clears it.  Synchronising.
+int markov_trace_read(void* dst, size_t bytes) {
+  const size_t all = sizeof(unsigned long long) * kTraceWGs * kTraceSteps * kTracePhases;
+  if (bytes > all) bytes = all;
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(dst, HIP_SYMBOL(trace_buf), bytes, 0, hipMemcpyDeviceToHost);
+  void* ptr = nullptr;
+  if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(trace_buf));
+  if (e == hipSuccess) e = hipMemset(ptr, 0, all);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(MARKOV_E_HIP, "trace read: %s", hipGetErrorString(e));
+  return MARKOV_OK;
+}
+#endif
 
 long long markov_set_wait_limit(long long us) {
   const unsigned long long t = us < 0 ? kTimeoutTicks : (unsigned long long)us * kTicksPerUs;

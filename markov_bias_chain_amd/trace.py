@@ -1,0 +1,139 @@
+"""Per-step time breakdown of the chain kernel, from its tracing build.
+
+    python -m markov_bias_chain_amd.build --trace     # libmarkov_trace.so
+    python -m markov_bias_chain_amd.trace --workload dsv41_single_row --noise inline
+
+The tracing build (MARKOV_TRACE) is the same kernel source with clock stamps
+at fixed points of every step, one thread per workgroup (the phases are
+listed in markov.hip next to trace_buf).  This tool runs warm (back to back)
+or cold (a 1 GiB read before each call) calls of a workload through that
+library, reads the stamps after each call and prints a markdown summary:
+per step, medians over the calls of
+
+  * local work: bias and epilogue of wave 0 (median over workgroups);
+  * last key out: the last workgroup's publication, from the step's first
+    start;
+  * winner known: when wave 0 of a workgroup knows the winner, after the last
+    publication (median and slowest workgroup);
+  * step: from the step's first start to the next step's first start.
+
+It is a measuring tool: nothing of the chain's arithmetic is here.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import os
+import statistics
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+TRACE_WGS, TRACE_STEPS, TRACE_PHASES = 1024, 32, 8
+TICK_US = 0.01  # 100 MHz
+
+
+def load_trace_library():
+    from markov_bias_chain_amd import binding, build
+
+    if not os.path.exists(build.TRACE_LIB):
+        raise RuntimeError(f"{build.TRACE_LIB} is missing: run `python -m markov_bias_chain_amd.build --trace`")
+    binding.LIB_PATH = build.TRACE_LIB
+    lib = binding.load()
+    lib.markov_trace_read.restype = ctypes.c_int
+    lib.markov_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    return binding, lib
+
+
+def read(lib, G: int, N: int) -> np.ndarray:
+    """Stamps [G, N, phases] in microseconds (int64 ticks converted)."""
+    buf = np.zeros((TRACE_WGS, TRACE_STEPS, TRACE_PHASES), dtype=np.uint64)
+    rc = lib.markov_trace_read(buf.ctypes.data, buf.nbytes)
+    if rc != 0:
+        raise RuntimeError("markov_trace_read failed")
+    return buf[:G, :N].astype(np.int64)
+
+
+def summarize(stamps: list, G: int, N: int, mode: int) -> dict:
+    """Medians over calls of the per-step quantities (microseconds)."""
+    rows = {k: [[] for _ in range(N)] for k in ("local", "pub", "win_med", "win_max", "step", "spread")}
+    kern = {"prologue_med": [], "prologue_max": [], "entry_spread": [], "total": []}
+    for t in stamps:
+        t0 = t[:, 0, 6].min()
+        kern["entry_spread"].append((t[:, 0, 6].max() - t0) * TICK_US)
+        kern["prologue_med"].append(np.median(t[:, 0, 7] - t[:, 0, 6]) * TICK_US)
+        kern["prologue_max"].append((t[:, 0, 7].max() - t0) * TICK_US)
+        kern["total"].append((t[:, N - 1, 5].max() - t0) * TICK_US)
+        for i in range(N):
+            start = t[:, i, 0].min()
+            rows["spread"][i].append((t[:, i, 0].max() - start) * TICK_US)
+            rows["local"][i].append(np.median(t[:, i, 1] - t[:, i, 0]) * TICK_US)
+            pub_phase = 2 if mode == 0 else 1
+            last_pub = t[:, i, pub_phase].max()
+            rows["pub"][i].append((last_pub - start) * TICK_US)
+            rows["win_med"][i].append(np.median(t[:, i, 4] - last_pub) * TICK_US)
+            rows["win_max"][i].append((t[:, i, 4].max() - last_pub) * TICK_US)
+            nxt = t[:, i + 1, 0].min() if i + 1 < N else t[:, i, 5].max()
+            rows["step"][i].append((nxt - start) * TICK_US)
+    med = statistics.median
+    return {"steps": {k: [med(v[i]) for i in range(N)] for k, v in rows.items()},
+            "kernel": {k: med(v) for k, v in kern.items()}}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--workload", default="dsv41_single_row")
+    ap.add_argument("--noise", choices=("inline", "side"), default="inline")
+    ap.add_argument("--calls", type=int, default=20)
+    ap.add_argument("--cold", action="store_true", help="read 1 GiB before each call (evicts L2s and MALL)")
+    args = ap.parse_args()
+
+    import torch
+
+    binding, lib = load_trace_library()
+    from markov_bias_chain_amd import synth
+    from markov_bias_chain_amd.device import DeviceChain
+
+    dev = torch.device("cuda:0")
+    w = synth.workload(args.workload)
+    inline = args.noise == "inline" and w.mode == 0
+    d = DeviceChain(w, device=dev, noise_inline=inline)
+    G = binding.markov_grid(w.rows, w.N, w.V, w.r, w.mode)
+    if w.mode == 0 and not inline:
+        d.noise()
+    for _ in range(5):
+        d.chain()
+    binding.markov_status(d.workspace)
+    read(lib, G, w.N)
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev) if args.cold else None
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    stamps = []
+    for _ in range(args.calls):
+        if scratch is not None:
+            torch.sum(scratch, dim=0, out=sink)
+        d.chain()
+        binding.markov_status(d.workspace)
+        stamps.append(read(lib, G, w.N))
+    s = summarize(stamps, G, w.N, w.mode)
+    k = s["kernel"]
+    print(f"## Per-step breakdown: {w.name}, {'inline' if inline else args.noise} noise, "
+          f"{'cold' if args.cold else 'warm'} calls, grid {G}, medians over {args.calls} calls (us)\n")
+    print(f"kernel: entry spread {k['entry_spread']:.2f}, prologue done (median workgroup) "
+          f"{k['prologue_med']:.2f}, (last) {k['prologue_max']:.2f}, first entry to last step end "
+          f"{k['total']:.2f}\n")
+    print("| step | start spread | local work (wave 0) | last key out | winner known (median / slowest WG) | step |")
+    print("|---|---|---|---|---|---|")
+    st = s["steps"]
+    for i in range(w.N):
+        print(f"| {i} | {st['spread'][i]:.2f} | {st['local'][i]:.2f} | {st['pub'][i]:.2f} | "
+              f"{st['win_med'][i]:.2f} / {st['win_max'][i]:.2f} | {st['step'][i]:.2f} |")
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
