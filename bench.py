@@ -117,8 +117,10 @@ def cpu_baseline(w, budget_s: float) -> dict:
     calls = 0
     t0 = time.perf_counter()
     while True:
-        oracle.chain(w.base, w.head, w.embed, w.prev, w.temperature, w.seeds, gumbel=g,
-                     state_idx=w.state_idx, mult=w.mult, cap=w.cap, mode=w.mode)
+        tok, _ = oracle.chain(w.base, w.head, w.embed, w.prev, w.temperature, w.seeds, gumbel=g,
+                              state_idx=w.state_idx, mult=w.mult, cap=w.cap, mode=w.mode)
+        if calls == 0:
+            cpu_baseline.tokens = tok
         calls += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -128,6 +130,94 @@ def cpu_baseline(w, budget_s: float) -> dict:
     return {"value": tokens / el, "unit": "draft tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{calls} full calls of the {w.name} workload (oracle noise included, "
                       f"{el:.1f} s, single thread on {os.cpu_count()} online cores)"}
+
+
+def cpu_mt_baseline(w, budget_s: float, ref_tokens=None) -> dict:
+    """The same chain on every host core, for a fairer CPU throughput figure
+    than the single-threaded oracle: the bias as an fp32 BLAS matrix-vector
+    product (torch CPU, all cores), the epilogue and the draw in fp32 torch
+    ops, and the noise (the SplitMix64 hash in numpy uint64 arithmetic, each
+    log in fp64 rounded once to fp32) over vocabulary slices on a thread
+    pool.  Mode 0 only.  Not the oracle and not a product path: a measured
+    baseline; `matches_oracle` says whether its tokens equal the oracle's on
+    the first call."""
+    import concurrent.futures
+
+    import numpy as np
+    import torch
+
+    # every core this process may run on, at most 16 (one GPU's share of a host)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    torch.set_num_threads(cores)
+    M64 = np.uint64(0xFFFFFFFFFFFFFFFF)
+    G64, C1, C2 = np.uint64(0x9E3779B97F4A7C15), np.uint64(0xBF58476D1CE4E5B9), np.uint64(0x94D049BB133111EB)
+
+    def sm(x):
+        z = x + G64
+        z = (z ^ (z >> np.uint64(30))) * C1
+        z = (z ^ (z >> np.uint64(27))) * C2
+        return z ^ (z >> np.uint64(31))
+
+    def sm_int(x):
+        return int(sm(np.array([x & int(M64)], dtype=np.uint64))[0])
+
+    ids = np.arange(w.V, dtype=np.uint64)
+    slices = np.array_split(np.arange(w.V), cores)
+    pool = concurrent.futures.ThreadPoolExecutor(cores)
+
+    def noise(seed, row, step):
+        h = sm_int(sm_int(sm_int(seed) ^ row) ^ step)
+        out = np.empty(w.V, dtype=np.float32)
+
+        def part(sl):
+            u = ((2 * (sm(np.uint64(h) ^ ids[sl]) >> np.uint64(41)) + 1).astype(np.float32)
+                 * np.float32(2.0**-24))
+            inner = np.log(u.astype(np.float64)).astype(np.float32)
+            out[sl] = -np.log((-inner).astype(np.float64)).astype(np.float32)
+
+        list(pool.map(part, slices))
+        return torch.from_numpy(out)
+
+    with torch.inference_mode():
+        head = torch.from_numpy(w.head[:w.V].view(np.int16)).view(torch.bfloat16).float()
+        embed = torch.from_numpy(w.embed.view(np.int16)).view(torch.bfloat16).float()
+        base = torch.from_numpy(np.ascontiguousarray(w.base).view(np.int16)).view(torch.bfloat16)
+        sidx = np.arange(w.rows) if w.state_idx is None else w.state_idx
+        mult = torch.tensor(w.mult, dtype=torch.float32)
+        inv_cap = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(w.cap, dtype=torch.float32) if w.cap > 0 else None
+
+        def call():
+            tokens = np.full((w.rows, w.N), -1, dtype=np.int64)
+            for b in range(w.rows):
+                if sidx[b] < 0:
+                    continue
+                p, T = int(w.prev[b]), float(w.temperature[b])
+                for i in range(w.N):
+                    bias = (head @ embed[p]).to(torch.bfloat16).float()
+                    x = (base[b, i].float() + bias) * mult
+                    if inv_cap is not None:
+                        x = torch.tanh(x * inv_cap) * w.cap
+                    c = x.to(torch.bfloat16).float()
+                    s = c / torch.tensor(T, dtype=torch.float32) + noise(int(w.seeds[b]), b, i) if T > 0 else c
+                    p = int(torch.argmax(s))
+                    tokens[b, i] = p
+            return tokens
+
+        first = call()
+        calls = 1
+        t0 = time.perf_counter()
+        while True:
+            call()
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    pool.shutdown()
+    tokens = (calls - 1) * w.real_rows * w.N
+    return {"value": tokens / el, "unit": "draft tokens/s", "cores": cores, "kind": "cpu_mt",
+            "matches_oracle": None if ref_tokens is None else bool(np.array_equal(first, ref_tokens)),
+            "sample": f"{calls - 1} full calls of the {w.name} workload (its own noise, {el:.1f} s, "
+                      f"{cores} threads: torch CPU matrix-vector bias and epilogue, numpy noise hash)"}
 
 
 def draft_step_figures(w, hidden: int, dev, reps: int = 50) -> dict:
@@ -424,6 +514,8 @@ def main() -> int:
         result["draft_step"] = draft_step_figures(w, args.lm_hidden, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        if w.mode == 0:
+            result["cpu_mt"] = cpu_mt_baseline(w, min(8.0, args.cpu_seconds), getattr(cpu_baseline, "tokens", None))
     print(json.dumps(result), flush=True)
     return 0
 
