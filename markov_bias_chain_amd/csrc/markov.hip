@@ -1114,19 +1114,30 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   float* sb = s_bias[wave];
   // Local work of step i: bias, epilogue, keys for every chunk of this
   // workgroup (mode 1 also publishes each chunk's partials).
+  // Streamed head: a workgroup's chunks are visited in alternating order
+  // (odd steps backwards), so every step after the first starts with the
+  // chunk the previous step ended with, whose head tiles are still in h:
+  // with k chunks per workgroup a step streams k - 1 of them.
+  const int nch = RES ? 1 : (NC - wg + G - 1) / G;  // this workgroup's chunks
   auto local_work = [&](int i) {
     if (lane == 0)
       for (int b = 0; b < rows; ++b) s_key[wave][b] = kNoCandidate;
-    for (int j = 0; wg + j * G < NC; ++j) {
+    for (int jj = 0; jj < nch; ++jj) {
+      const int j = (!RES && (i & 1)) ? nch - 1 - jj : jj;
       const int c = wg + j * G;
       const int g = c * kWaves + wave;
       LaneIn cur, nxt;
       if constexpr (!RES) {
         // Stream this group's head (all 32 tiles in flight at once), with
-        // the first batch's inputs.
+        // the first batch's inputs, unless the tiles are still here from
+        // the previous step.  (Issuing the next chunk's tiles during this
+        // chunk's epilogue instead was slower: the epilogue's noise draw
+        // then runs with h live.)
+        if (jj > 0 || i == 0) {
 #pragma unroll
-        for (int s2 = 0; s2 < kSlots; ++s2)
-          h[s2] = g < NG ? load_head_tile<R>(p.head, g, s2, lane, V) : make_uint4(0, 0, 0, 0);
+          for (int s2 = 0; s2 < kSlots; ++s2)
+            h[s2] = g < NG ? load_head_tile<R>(p.head, g, s2, lane, V) : make_uint4(0, 0, 0, 0);
+        }
       }
       if constexpr (ONE) {
         // Lane lr's vocab id v: bias, cache value and score ordinal in
