@@ -828,12 +828,14 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   uint32_t one_base = 0;
   float one_noise = 0.0f;
   // Inline noise: waves 1 .. 7 draw the next step's noise here, while wave
-  // 0 alone waits for the exchange; wave 0 draws its own inside its first
-  // poll, behind the poll's loads, except in the reducer workgroups of the
-  // two-level exchange, whose wave 0 polls twice: there wave 1 draws it
-  // (into s_nz0).  Step 0's noise every wave draws here.
+  // 0 alone waits for the exchange, and wave 1 also draws wave 0's values
+  // (into s_nz0), so the polling wave draws nothing.  (Wave 0 drawing its
+  // own inside its first poll, behind the poll's loads, kept the draw's
+  // registers live in the poll loop: 47 SGPR spills against 20, and 42.7 ->
+  // 41.6 us per call on the DeepSeek-sized row.)  Step 0's noise every wave
+  // draws here.
   const bool one_nz = MODE == 0 && ONE && nz_inline;
-  const bool w0_by_w1 = one_nz && reducers_for(G) > 1 && wg < reducers_for(G);
+  const bool w0_by_w1 = one_nz;
   auto draw_one = [&](int i) {
     if (s_active[0] && own_res && s_T[0] > 0.0f)
       gumbel_noise<1>(noise_prefix(s_seed[0], p.row_base, i), v_res, s_log, &one_noise);
@@ -1438,7 +1440,6 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           uint64_t best = kNoCandidate;
           uint32_t spec = 0xFFFFFFFFu;
           uint4 ev = make_uint4(0, 0, 0, 0);
-          bool first = true;
           for (;;) {
             bool all = true;
             uint64_t mine = kNoCandidate;
@@ -1448,10 +1449,6 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
               const int idx = lane + 64 * k;
               xs[k] = idx < n ? ld_agent(slots + idx) : kNoCandidate;
             }
-            // One row, inline noise: wave 0's next-step values, drawn while
-            // the first round's loads are in flight.
-            if (one_nz && !w0_by_w1 && first && next) draw_one(i + 1);
-            first = false;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               all = all && (xs[k] != 0);
@@ -1840,7 +1837,9 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
 //  * each workgroup folds its best key of every row into the row's slot
 //    with an agent-scope atomic max (fire and forget), then counts itself on
 //    the step's arrival counter; the workgroup that arrives last writes the
-//    step's tokens and gathers the winners' embeddings for the next step.
+//    step's tokens, also into the workspace, from where every workgroup of
+//    the next launch loads its rows' winner embeddings itself (a gather of
+//    all rows by the last workgroup cost ~5.5 us per step at 256 rows).
 // No workgroup ever waits for another, so the launch needs no co-residency.
 //
 // Workspace half layout of this path (the parity protocol of the persistent
@@ -1849,15 +1848,16 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
 //   arrive[2] u32 (256 bytes)          arrival counters, by step parity
 //   best[2][rows][kBestStride] u64     each row's best key, by step parity
 //                                      (one 128-byte line per row)
-//   emb[2][rows][R] bf16               the current tokens' embeddings
+//   tok[rows] i32                      the last step's tokens (-1: inert row)
 // The last workgroup of step i zeroes arrive[i & 1] and best[i & 1] after
 // reading them, so step i + 2 finds them zero.
 
 constexpr int kBestStride = 16;  // u64 words per row's best key (a 128-byte line)
-constexpr int kPrefetch = 3;     // epilogue batches whose inputs are in flight
+constexpr int kPrefetch = 2;     // epilogue batches whose inputs are in flight
 
 __host__ __device__ inline size_t step_half_bytes(int rows, int R) {
-  const size_t b = 256 + (size_t)2 * rows * kBestStride * 8 + (size_t)2 * rows * R * 2;
+  (void)R;
+  const size_t b = 256 + (size_t)2 * rows * kBestStride * 8 + (size_t)rows * 4;
   return (b + 255) & ~(size_t)255;
 }
 
@@ -1903,7 +1903,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   unsigned char* half = p.ws + kHeader + parity * p.ws_half;
   uint32_t* arrive = reinterpret_cast<uint32_t*>(half);
   uint64_t* best = reinterpret_cast<uint64_t*>(half + 256);
-  uint16_t* emb = reinterpret_cast<uint16_t*>(half + 256 + (size_t)2 * rows * kBestStride * 8);
+  int* tokbuf = reinterpret_cast<int*>(half + 256 + (size_t)2 * rows * kBestStride * 8);
   uint64_t* best_i = best + (size_t)(step & 1) * rows * kBestStride;
   if (step == 0) {
     // Clear the other half for the next call (nobody reads it in this one).
@@ -1955,6 +1955,33 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
     }
   };
 
+  // The embeddings of a row block, kPieces 16-byte pieces per thread, loaded
+  // into registers one block ahead: the embedding table's rows of the
+  // anchors (step 0) or of the previous step's winners.
+  constexpr int kPieces = kBlock * KSEG / kThreads;
+  static_assert(kPieces * kThreads == kBlock * KSEG, "whole pieces per thread");
+  uint4 ne[kPieces];
+  auto emb_load = [&](int rb2) {
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int k = j * kThreads + tid;
+      const int bl = k / KSEG, seg = k - bl * KSEG;
+      const int b = rb2 + bl;
+      ne[j] = make_uint4(0, 0, 0, 0);
+      if (b < rows) {
+        int64_t tok = -1;
+        if (step == 0) {
+          const int64_t st = p.state_idx ? p.state_idx[b] : (int64_t)b;
+          if (st >= 0 && st < p.cache_states) tok = p.prev[b];
+        } else {
+          tok = tokbuf[b];  // -1 for an inert row
+        }
+        if (tok >= 0 && tok < V) ne[j] = *reinterpret_cast<const uint4*>(p.embed + (size_t)tok * R + seg * 8);
+      }
+    }
+  };
+  emb_load(0);
+
   for (int rb = 0; rb < rows; rb += kBlock) {
     const int nbr = rows - rb < kBlock ? rows - rb : kBlock;
     // ---- the block's rows: state, activity, temperature; embeddings.
@@ -1984,20 +2011,21 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    for (int k = tid; k < nbr * KSEG; k += kThreads) {
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int k = j * kThreads + tid;
       const int bl = k / KSEG, seg = k - bl * KSEG;
-      if (!s_active[bl]) continue;
-      const uint16_t* src = step == 0 ? p.embed + (size_t)p.prev[rb + bl] * R
-                                      : emb + ((size_t)(step & 1) * rows + rb + bl) * R;
-      s_e[bl * ES + seg] = *reinterpret_cast<const uint4*>(src + seg * 8);
+      if (bl < nbr && s_active[bl]) s_e[bl * ES + seg] = ne[j];
     }
-    // the first batches' inputs, then the embeddings visible to every wave
+    // the first batches' inputs and the next block's embeddings, then the
+    // embeddings visible to every wave
     const int nbat = (nbr + kBatch - 1) / kBatch;
     In in[kPrefetch];
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
       if (k < nbat) load_in(rb, k * kBatch, in[k]);
     }
+    if (rb + kBlock < rows) emb_load(rb + kBlock);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -2111,7 +2139,6 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  int* s_tok = reinterpret_cast<int*>(s_e);  // rows <= MARKOV_MAX_ROWS tokens (16 KiB)
   for (int b = tid; b < rows; b += kThreads) {
     const int64_t st = p.state_idx ? p.state_idx[b] : (int64_t)b;
     const int64_t tok0 = p.prev[b];
@@ -2124,23 +2151,12 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
       p.tokens[(long long)b * p.tok_rs + step] = tok;
       st_agent(best_i + (size_t)b * kBestStride, 0);  // for step + 2
     }
-    s_tok[b] = tok;
+    tokbuf[b] = tok;
   }
-  if (tid == 0) st_agent32(arrive + (step & 1), 0u);
-  __syncthreads();
-  if (step + 1 < p.N) {
-    // the winners' embeddings for the next step, 16 bytes per thread and load
-    uint16_t* dst = emb + (size_t)((step + 1) & 1) * rows * R;
-    for (int k = tid; k < rows * KSEG; k += kThreads) {
-      const int b = k / KSEG, seg = k - b * KSEG;
-      const int tok = s_tok[b];
-      if (tok >= 0)
-        *reinterpret_cast<uint4*>(dst + (size_t)b * R + seg * 8) =
-            *reinterpret_cast<const uint4*>(p.embed + (size_t)tok * R + seg * 8);
-    }
-  } else if (tid == 0) {
+  if (tid == 0) {
+    st_agent32(arrive + (step & 1), 0u);
     // every launch of the call has read the parity by now
-    st_agent32(header, parity ^ 1u);
+    if (step + 1 == p.N) st_agent32(header, parity ^ 1u);
   }
   __syncthreads();
   TRACE_STAMP(c, step, 3);

@@ -85,12 +85,40 @@ def summarize(stamps: list, G: int, N: int, mode: int) -> dict:
             "kernel": {k: med(v) for k, v in kern.items()}}
 
 
+def summarize_step_kernels(stamps: list, G: int, N: int) -> dict:
+    """Step-kernel path (one launch per position): per launch, medians over
+    calls of the entry spread, the first row block's inputs ready (median
+    workgroup, from its entry), all blocks done (median and last workgroup,
+    from the first entry), the last workgroup's picks (after the last
+    workgroup's blocks), and the gap to the next launch's first entry."""
+    keys = ("spread", "first_block", "blocks_med", "blocks_max", "pick", "gap", "launch")
+    rows = {k: [[] for _ in range(N)] for k in keys}
+    for t in stamps:
+        for i in range(N):
+            e = t[:, i, 0]
+            start = e.min()
+            rows["spread"][i].append((e.max() - start) * TICK_US)
+            rows["first_block"][i].append(np.median(t[:, i, 1] - e) * TICK_US)
+            rows["blocks_med"][i].append((np.median(t[:, i, 2]) - start) * TICK_US)
+            rows["blocks_max"][i].append((t[:, i, 2].max() - start) * TICK_US)
+            end = t[:, i, 3].max()  # only the last workgroup stamps phase 3
+            rows["pick"][i].append((end - t[:, i, 2].max()) * TICK_US)
+            rows["launch"][i].append((end - start) * TICK_US)
+            if i + 1 < N:
+                rows["gap"][i].append((t[:, i + 1, 0].min() - end) * TICK_US)
+            else:
+                rows["gap"][i].append(0.0)
+    med = statistics.median
+    return {k: [med(v[i]) for i in range(N)] for k, v in rows.items()}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--workload", default="dsv41_single_row")
     ap.add_argument("--noise", choices=("inline", "side"), default="inline")
     ap.add_argument("--calls", type=int, default=20)
     ap.add_argument("--cold", action="store_true", help="read 1 GiB before each call (evicts L2s and MALL)")
+    ap.add_argument("--batch-path", choices=("auto", "persistent", "step"), default="auto")
     args = ap.parse_args()
 
     import torch
@@ -100,10 +128,14 @@ def main() -> int:
     from markov_bias_chain_amd.device import DeviceChain
 
     dev = torch.device("cuda:0")
+    binding.markov_set_batch_path({"auto": 0, "persistent": 1, "step": 2}[args.batch_path])
     w = synth.workload(args.workload)
     inline = args.noise == "inline" and w.mode == 0
     d = DeviceChain(w, device=dev, noise_inline=inline)
+    step_path = w.mode == 0 and not inline and (args.batch_path == "step" or (args.batch_path == "auto" and w.rows > 64))
     G = binding.markov_grid(w.rows, w.N, w.V, w.r, w.mode)
+    if step_path:  # one workgroup per chunk
+        G = -(-w.V // (8 * (16384 // w.r)))
     if w.mode == 0 and not inline:
         d.noise()
     for _ in range(5):
@@ -119,6 +151,17 @@ def main() -> int:
         d.chain()
         binding.markov_status(d.workspace)
         stamps.append(read(lib, G, w.N))
+    if step_path:
+        st = summarize_step_kernels(stamps, G, w.N)
+        print(f"## Step kernels: {w.name}, noise in memory, {'cold' if args.cold else 'warm'} calls, "
+              f"{G} workgroups per launch, medians over {args.calls} calls (us)\n")
+        print("| step | entry spread | first block ready (median WG) | blocks done (median / last WG) "
+              "| last WG's picks | launch (first entry to picks done) | gap to next launch |")
+        print("|---|---|---|---|---|---|---|")
+        for i in range(w.N):
+            print(f"| {i} | {st['spread'][i]:.2f} | {st['first_block'][i]:.2f} | {st['blocks_med'][i]:.2f} / "
+                  f"{st['blocks_max'][i]:.2f} | {st['pick'][i]:.2f} | {st['launch'][i]:.2f} | {st['gap'][i]:.2f} |")
+        return 0
     s = summarize(stamps, G, w.N, w.mode)
     k = s["kernel"]
     print(f"## Per-step breakdown: {w.name}, {'inline' if inline else args.noise} noise, "

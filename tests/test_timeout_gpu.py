@@ -37,6 +37,7 @@ def _gpu():
     lm.load()
     yield
     lm.markov_set_wait_limit(-1)
+    lm.markov_set_batch_path(0)
     torch.cuda.synchronize()
 
 
@@ -45,7 +46,7 @@ def _gpu():
     (129280, 1, 0, True),   # the same with inline noise (the bench's kernel)
     (20000, 3, 0, False),   # a batch: the all-to-all exchange
     (12288, 5, 1, False),   # inverse CDF: leader, decision and token waits
-    (8192, 100, 0, False),  # two launches of up to 64 rows
+    (8192, 100, 0, False),  # two persistent launches of up to 64 rows
 ])
 def test_wait_limit_zero_times_out_then_recovers(V, rows, mode, inline):
     w = synth.make(f"timeout_V{V}_rows{rows}", V, 256, rows, 3, seed=V + rows, weights="int",
@@ -54,6 +55,7 @@ def test_wait_limit_zero_times_out_then_recovers(V, rows, mode, inline):
     d = DeviceChain(w, noise_inline=inline)
     if g is not None:
         d.set_gumbel(g)
+    lm.markov_set_batch_path(1)  # the persistent kernels (the only ones that wait)
     say(f"  V={V} rows={rows} mode={mode} inline={inline}: wait limit 0")
     assert lm.markov_set_wait_limit(0) == 2_000_000
     t0 = time.perf_counter()
@@ -80,3 +82,20 @@ def test_wait_limit_zero_times_out_then_recovers(V, rows, mode, inline):
     lm.markov_status(d.workspace)
     t2, c2 = d.results()
     assert np.array_equal(t2, ref[0]) and np.array_equal(c2, ref[1])
+
+
+def test_step_kernels_never_wait():
+    """The step-kernel path (large batches) has no cross-workgroup wait: with
+    a zero wait limit it still completes without an error and exactly."""
+    w = synth.make("timeout_step", 8192, 256, 100, 3, seed=8292, weights="int", base_std=2.0, temperature=1.0)
+    g = oracle.noise_fill(w.seeds, w.N, w.V)
+    d = DeviceChain(w)
+    d.set_gumbel(g)
+    lm.markov_set_batch_path(2)
+    lm.markov_set_wait_limit(0)
+    d.chain()
+    lm.markov_status(d.workspace)
+    lm.markov_set_wait_limit(-1)
+    t, c = d.results()
+    ref = oracle.chain(w.base, w.head, w.embed, w.prev, w.temperature, w.seeds, gumbel=g)
+    assert np.array_equal(t, ref[0]) and np.array_equal(c, ref[1])
