@@ -86,7 +86,7 @@ def head_residency(w, inline: bool, noise: str):
     if not f or "fetch_bytes_per_launch" not in f:
         return None
     ab = algorithmic_bytes(w, inline)
-    other = ab["base"] + ab["noise"] + ab["embed"] + w.real_rows * 8
+    other = ab["reads"] - ab["head"] + w.real_rows * 8  # base, noise read, embedding rows, anchors
     head_fetched = int(f["fetch_bytes_per_launch"]) - other
     return {"head_bytes": ab["head"], "steps": w.N, "head_bytes_fetched_per_call": head_fetched,
             "head_reads_per_call": head_fetched / ab["head"],
@@ -94,16 +94,22 @@ def head_residency(w, inline: bool, noise: str):
 
 
 def algorithmic_bytes(w, inline: bool) -> dict:
-    """Bytes one chain call must move at minimum (padding rows excluded)."""
+    """The algorithmic bytes of one chain call, per unit as the scope table
+    counts them: the head once, base logits, noise (fp32, mode 0: counted
+    whether the kernel reads it or draws it inline), cache writes and the
+    embedding rows, for the real (non-padding) rows; `reads` are the bytes a
+    call actually reads (no noise when it is drawn inline), for comparing
+    with the measured fetch traffic."""
     real = w.real_rows
     head = w.V * w.r * 2
     base = real * w.N * w.V * 2
-    noise = real * w.N * w.V * 4 if w.mode == 0 and not inline else 0
+    noise = real * w.N * w.V * 4 if w.mode == 0 else 0
     cache = real * w.N * w.V * 2
     embed = real * w.N * w.r * 2
-    tokens = real * w.N * 8
-    return dict(head=head, base=base, noise=noise, cache=cache, embed=embed, tokens=tokens,
-                total=head + base + noise + cache + embed + tokens)
+    noise_read = 0 if inline else noise
+    return dict(head=head, base=base, noise=noise, cache=cache, embed=embed,
+                total=head + base + noise + cache + embed,
+                reads=head + base + noise_read + embed)
 
 
 def cpu_baseline(w, budget_s: float) -> dict:
