@@ -1088,15 +1088,17 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     const uint32_t gnan = group8_umin(enan < IPL ? (uint32_t)v0 + enan : 0xFFFFFFFFu);
     float wsum = 0.0f;
     if (MODE == 1) {
-      // The same expf as the owner's scan of the chosen chunk, so that the
-      // leader's chunk weights and the owner's in-chunk CDF are built from
-      // the same exponentials (a cruder exp here would shift draws near a
-      // chunk's upper edge onto its last id).
+      // The same exponential as the owner's scan of the chosen chunk, so
+      // that the leader's chunk weights and the owner's in-chunk CDF are
+      // built from the same function (a cruder one here than there would
+      // shift draws near a chunk's upper edge onto its last id).  Both use
+      // the hardware exp2 form: the library expf on every element cost
+      // 252.5 vs 234.0 us per call at 64 rows.
       const float m = order_key_inv(gmax);
       float s = 0.0f;
       if (ok && gmax != INT_MIN && isfinite(m)) {
 #pragma unroll
-        for (int e = 0; e < IPL; ++e) s += isnan(z[e]) ? 0.0f : expf(z[e] - m);
+        for (int e = 0; e < IPL; ++e) s += isnan(z[e]) ? 0.0f : __expf(z[e] - m);
       }
       wsum = group8_sum(s);
     }
@@ -1737,7 +1739,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           float lsum = 0.0f;
 #pragma unroll
           for (int k = 0; k < PER; ++k) {
-            w[k] = (v0 + k < V && z[k] > -INFINITY) ? expf(z[k] - m) : 0.0f;
+            w[k] = (v0 + k < V && z[k] > -INFINITY) ? __expf(z[k] - m) : 0.0f;  // as the partial sums
             lsum += w[k];
           }
           float run = wave_incl_scan(lsum) - lsum;
