@@ -164,7 +164,8 @@ def main() -> int:
         return 0
     s = summarize(stamps, G, w.N, w.mode)
     k = s["kernel"]
-    print(f"## Per-step breakdown: {w.name}, {'inline' if inline else args.noise} noise, "
+    noise = "no noise (inverse CDF)" if w.mode == 1 else f"{'inline' if inline else args.noise} noise"
+    print(f"## Per-step breakdown: {w.name}, {noise}, "
           f"{'cold' if args.cold else 'warm'} calls, grid {G}, medians over {args.calls} calls (us)\n")
     print(f"kernel: entry spread {k['entry_spread']:.2f}, prologue done (median workgroup) "
           f"{k['prologue_med']:.2f}, (last) {k['prologue_max']:.2f}, first entry to last step end "
