@@ -464,7 +464,14 @@ struct ChainParams {
   unsigned long long ws_half;  // bytes per parity half
   unsigned long long clear_bytes;  // bytes of the other half each call clears (<= ws_half)
   unsigned long long wait_ticks;  // bound of every cross-workgroup wait (s_memrealtime ticks)
+  int nres;  // streamed head: 0, or kParked<R>: chunk 1's tiles kept in LDS after step 0
 };
+
+// Streamed head: the tile slots per wave of a workgroup's chunk 1 kept in LDS
+// across steps when they fit beside the kernel's static arrays and the
+// embeddings (160 KiB of LDS: up to 13 rows at r = 512, 10 at r = 256).
+template <int R>
+constexpr int kParked = R == 512 ? 15 : 14;
 
 // Workspace half layout (slot arrays of one parity; every slot is written at
 // most once per call, and 0 means "not written yet"):
@@ -719,7 +726,9 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   __shared__ float s_nz0[64];  // one row, inline noise: wave 0's next-step noise (reducers)
   __shared__ int s_abort;
   __shared__ uint32_t s_parity;
-  extern __shared__ uint4 s_e[];  // [rows][ES] 16-byte vectors of the current embeddings
+  // Dynamic LDS: [rows][ES] 16-byte vectors of the current embeddings, then
+  // (streamed head) [kWaves][nres][64] head tiles of the workgroup's chunk 1.
+  extern __shared__ uint4 s_e[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1116,6 +1125,19 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   };
 
   float* sb = s_bias[wave];
+  // Streamed head: the first nres tiles of each wave's group in chunk 1 are
+  // written to LDS at step 0 and read from there at later steps, so those
+  // bytes are streamed from memory once per launch instead of every step.
+  constexpr int NP = kParked<R>;
+  uint4* const s_hres = s_e + rows * ES + wave * NP * 64;
+  auto park_tiles = [&](int i, int j) {
+    if constexpr (!RES) {
+      if (i == 0 && j == 1 && p.nres > 0) {
+#pragma unroll
+        for (int s2 = 0; s2 < NP; ++s2) s_hres[s2 * 64 + lane] = h[s2];
+      }
+    }
+  };
   // Local work of step i: bias, epilogue, keys for every chunk of this
   // workgroup (mode 1 also publishes each chunk's partials).
   // Streamed head: a workgroup's chunks are visited in alternating order
@@ -1138,9 +1160,17 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // chunk's epilogue instead was slower: the epilogue's noise draw
         // then runs with h live.)
         if (jj > 0 || i == 0) {
+          if (i > 0 && j == 1 && p.nres > 0) {
 #pragma unroll
-          for (int s2 = 0; s2 < kSlots; ++s2)
-            h[s2] = g < NG ? load_head_tile<R>(p.head, g, s2, lane, V) : make_uint4(0, 0, 0, 0);
+            for (int s2 = NP; s2 < kSlots; ++s2)
+              h[s2] = g < NG ? load_head_tile<R>(p.head, g, s2, lane, V) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int s2 = 0; s2 < NP; ++s2) h[s2] = s_hres[s2 * 64 + lane];
+          } else {
+#pragma unroll
+            for (int s2 = 0; s2 < kSlots; ++s2)
+              h[s2] = g < NG ? load_head_tile<R>(p.head, g, s2, lane, V) : make_uint4(0, 0, 0, 0);
+          }
         }
       }
       if constexpr (ONE) {
@@ -1150,6 +1180,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         const int v = g * RPG + lr;
         const bool own = g < NG && v < V && lane_owns;
         const float bsum = one_row_bias<R>(h, s_e, lane);
+        park_tiles(i, j);
         if (w0_by_w1 && wave == 0 && i > 0) one_noise = s_nz0[lane];
         uint32_t ord = 0;
         if (s_active[0] && own) {
@@ -1207,6 +1238,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         if ((t & 1) == 0) {
           const int np = rows - b0 < kRowPass ? rows - b0 : kRowPass;
           group_bias<R>(h, s_e, b0, np, lane, sb);
+          if (t == 0) park_tiles(i, j);
         }
         const int nb = rows - b0 < kBatch ? rows - b0 : kBatch;
         if constexpr (ahead) {
@@ -2251,32 +2283,57 @@ const void* kernel_for(int rank, int mode, int kind, bool fl, bool nz) {
   return nz ? kernel_for_fl<false, true>(rank, mode, kind) : kernel_for_fl<false, false>(rank, mode, kind);
 }
 
+// The LDS one workgroup may use on the current device, and a chain kernel's
+// static LDS (its __shared__ arrays); the rest is the kernel's dynamic LDS:
+// the embeddings and, on a streamed head, the tiles kept across steps.
+int device_lds_bytes() {
+  int dev = 0, lds = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return 0;
+  return lds;
+}
+int static_lds_bytes(const void* kern) {
+  hipFuncAttributes a;
+  if (hipFuncGetAttributes(&a, kern) != hipSuccess) return -1;
+  return (int)a.sharedSizeBytes;
+}
+
 // Dynamic LDS above the default per-launch limit is opted into once per
-// process for every chain kernel (the embeddings of kLaunchRows rows:
-// 33 KiB at r = 256, 65 KiB at r = 512).
+// process for every kernel: all the LDS a workgroup may have beside the
+// kernel's static arrays.
 int prepare_kernels() {
   static std::once_flag once;
   static hipError_t err = hipSuccess;
   std::call_once(once, [] {
+    const int lds = device_lds_bytes();
+    // (at least the embeddings of kLaunchRows rows)
+    auto allow = [&](const void* kern, int rank) {
+      const int st = static_lds_bytes(kern);
+      const int emb = kLaunchRows * (rank / 8 + 1) * 16;
+      hipError_t e = st < 0 ? hipErrorInvalidValue
+                            : hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                  lds - st > emb ? lds - st : emb);
+      if (e != hipSuccess && err == hipSuccess) err = e;
+    };
     for (int rank : {256, 512})
       for (int mode : {0, 1})
         for (int kind = 0; kind < 4; ++kind)
-          for (int flags = 0; flags < 4; ++flags) {
-          hipError_t e = hipFuncSetAttribute(kernel_for(rank, mode, kind, flags & 1, flags & 2),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             kLaunchRows * (rank / 8 + 1) * 16);
-          if (e != hipSuccess && err == hipSuccess) err = e;
-        }
+          for (int flags = 0; flags < 4; ++flags) allow(kernel_for(rank, mode, kind, flags & 1, flags & 2), rank);
     for (int rank : {256, 512})
-      for (int fl = 0; fl < 2; ++fl) {
-        hipError_t e = hipFuncSetAttribute(fl ? step_kernel_for<true>(rank) : step_kernel_for<false>(rank),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           kLaunchRows * (rank / 8 + 1) * 16);
-        if (e != hipSuccess && err == hipSuccess) err = e;
-      }
+      for (int fl = 0; fl < 2; ++fl) allow(fl ? step_kernel_for<true>(rank) : step_kernel_for<false>(rank), rank);
   });
   if (err != hipSuccess) return fail(MARKOV_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(err));
   return MARKOV_OK;
+}
+
+// Streamed head: kParked<R> when chunk 1's parked tiles fit in the LDS left
+// beside the kernel's static arrays and the embeddings, else 0.
+int parked_slots(const void* kern, int rank, size_t emb_bytes) {
+  const int np = rank == 512 ? kParked<512> : kParked<256>;
+  const int st = static_lds_bytes(kern);
+  if (st < 0) return 0;
+  const long long need = (long long)st + (long long)emb_bytes + (long long)kWaves * np * 64 * 16;
+  return need <= device_lds_bytes() ? np : 0;
 }
 
 // The grid: one workgroup per CU at most.  If the CUs cover every chunk the
@@ -2470,6 +2527,7 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
     p.ws_half = ((workspace_bytes - kHeader) / 2) & ~(size_t)255;
     p.clear_bytes = clear_bytes;
     p.wait_ticks = 0;
+    p.nres = 0;
     const void* kern = (base_f32 || cache_f32) ? step_kernel_for<true>(rank) : step_kernel_for<false>(rank);
     const size_t shmem = (size_t)kLaunchRows * (rank / 8 + 1) * 16;
     for (int i = 0; i < steps; ++i) {
@@ -2522,9 +2580,11 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
     p.clear_bytes = clear_bytes;
     p.wait_ticks = g_wait_ticks.load();
 
-    void* args[] = {&p};
-    const size_t shmem = (size_t)nr * (rank / 8 + 1) * 16;
     const void* kern = kernel_for(rank, mode, kernel_kind(nr, mode, res), base_f32 || cache_f32, noise_inline);
+    size_t shmem = (size_t)nr * (rank / 8 + 1) * 16;
+    p.nres = res ? 0 : parked_slots(kern, rank, shmem);
+    shmem += (size_t)kWaves * p.nres * 64 * 16;
+    void* args[] = {&p};
     // A regular launch: the grid is at most one workgroup per CU and the
     // kernel's resources admit only one per CU, so on an otherwise idle
     // device every workgroup is resident at once; every cross-workgroup wait
