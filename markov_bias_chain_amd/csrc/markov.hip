@@ -265,9 +265,12 @@ __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memr
 // kernel phases: 0 step start, 1 local work done (wave 0), 2 keys published,
 // 3 reducer partials / inverse-CDF decision published, 4 winner known
 // (wave 0), 5 step end; step 0 also holds 6 kernel entry and 7 prologue
-// done.  Step kernel phases (per launch): 0 entry, 1 first block's inputs
-// issued, 2 all blocks done, 3 the last workgroup's picks done.
-constexpr int kTraceWGs = 1024, kTraceSteps = 32, kTracePhases = 8;
+// done.  Inverse CDF, in addition: 8 decisions read (wave 0), and the latest
+// of any wave's 9 token published as a chunk's owner, 10 partials all seen
+// as a row's leader, 11 decision published.  Step kernel phases (per
+// launch): 0 entry, 1 first block's inputs issued, 2 all blocks done, 3 the
+// last workgroup's picks done.
+constexpr int kTraceWGs = 1024, kTraceSteps = 32, kTracePhases = 12;
 #ifdef MARKOV_TRACE
 __device__ unsigned long long trace_buf[kTraceWGs * kTraceSteps * kTracePhases];
 #define TRACE_STAMP(wgi, step, ph)                                                            \
@@ -275,9 +278,19 @@ __device__ unsigned long long trace_buf[kTraceWGs * kTraceSteps * kTracePhases];
     if (threadIdx.x == 0 && (step) < kTraceSteps && (wgi) < kTraceWGs)                        \
       trace_buf[((size_t)(wgi) * kTraceSteps + (step)) * kTracePhases + (ph)] = now_ticks(); \
   } while (0)
+// From lane 0 of the calling wave; the latest stamp of the workgroup's waves.
+#define TRACE_STAMP_MAX(wgi, step, ph)                                                              \
+  do {                                                                                              \
+    if ((threadIdx.x & 63) == 0 && (step) < kTraceSteps && (wgi) < kTraceWGs)                       \
+      __hip_atomic_fetch_max(trace_buf + ((size_t)(wgi) * kTraceSteps + (step)) * kTracePhases + (ph), \
+                             (unsigned long long)now_ticks(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); \
+  } while (0)
 #else
 #define TRACE_STAMP(wgi, step, ph) \
   do {                             \
+  } while (0)
+#define TRACE_STAMP_MAX(wgi, step, ph) \
+  do {                                 \
   } while (0)
 #endif
 
@@ -1303,19 +1316,22 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   {
     // The step loop: local work, publication, then the exchange of the
     // step (its tail overlaps the fetch of the next embedding).
-    // Inverse CDF: a wave that leads a row (H2 below) stages its next base
-    // logits after its decisions, not before: the leaders' polls would
-    // otherwise wait behind the staging loads (loads complete in order).
-    bool leader_wave = false;
+    // Inverse CDF: a workgroup that leads a row (H2 below) stages its next
+    // base logits after its decisions, in every wave: the leader's polls
+    // would otherwise queue behind its own wave's staging loads (loads
+    // complete in order) and behind the other waves' in the CU's memory
+    // pipeline (64 rows: 233.0 -> 225.3 us per call against deferring the
+    // leader wave alone).
+    bool leads = false;
     if constexpr (MODE == 1)
-      for (int b = wg; b < rows; b += G) leader_wave = leader_wave || (((b / G) % kWaves) == wave && s_active[b]);
+      for (int b = wg; b < rows; b += G) leads = leads || s_active[b];
     TRACE_STAMP(wg, 0, 7);
     for (int i = 0; i < N; ++i) {
       TRACE_STAMP(wg, i, 0);
       local_work(i);
       TRACE_STAMP(wg, i, 1);
       if (MODE == 1 && ahead && i + 1 < N) prefetch(i + 1);
-      if (stage && !base_f32 && i + 1 < N && !leader_wave) {
+      if (stage && !base_f32 && i + 1 < N && !leads) {
         // Parked at once: the wait for the loads overlaps the wait for the
         // other workgroups' partials.
         stage_load(i + 1);
@@ -1580,6 +1596,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             }
             __builtin_amdgcn_s_sleep(1);
           }
+          TRACE_STAMP_MAX(wg, i, 10);
           uint64_t K = kNoCandidate;
           for (int k = 0; k < KPL; ++k) {
             uint64_t key;
@@ -1679,9 +1696,11 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           // workgroups in H3 instead of all G (64 rows: 258 -> 241 us per
           // call with the tokens copied likewise).
           if (lane < kDecCopies) st_agent(L.dec + ((size_t)i * kDecCopies + lane) * rows + b, dec);
+          TRACE_STAMP_MAX(wg, i, 11);
         }
         TRACE_STAMP(wg, i, 3);
-        if (stage && !base_f32 && i + 1 < N && leader_wave) {
+        if (stage && !base_f32 && i + 1 < N && leads) {
+          __syncthreads();  // after this workgroup's decisions
           stage_load(i + 1);
           stage_park();
         }
@@ -1719,6 +1738,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             }
           }
         }
+        TRACE_STAMP(wg, i, 8);
         __syncthreads();
         // The chunk's owner scans it in vocabulary order (its cache values were
         // stored by this workgroup in this step).
@@ -1792,6 +1812,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           }
           if (lane == 0) s_tok[b] = tok;
           if (lane < kDecCopies) st_agent(L.tok + ((size_t)i * kDecCopies + lane) * rows + b, (1ull << 63) | (uint32_t)tok);
+          TRACE_STAMP_MAX(wg, i, 9);
         }
         // H4: rows whose chunk another workgroup owns, polled all at once.
         {
@@ -2702,7 +2723,7 @@ int markov_set_batch_path(int path) { return g_batch_path.exchange(path < 0 || p
 
 #ifdef MARKOV_TRACE
 // Trace builds only (not part of the ABI in markov.h): copies the first
-// `bytes` of trace_buf ([1024 workgroups][32 steps][8 phases] u64 ticks of
+// `bytes` of trace_buf ([1024 workgroups][32 steps][12 phases] u64 ticks of
 // the 100 MHz clock) to host memory and clears it.  Synchronising.
 int markov_trace_read(void* dst, size_t bytes) {
   const size_t all = sizeof(unsigned long long) * kTraceWGs * kTraceSteps * kTracePhases;

@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-TRACE_WGS, TRACE_STEPS, TRACE_PHASES = 1024, 32, 8
+TRACE_WGS, TRACE_STEPS, TRACE_PHASES = 1024, 32, 12
 TICK_US = 0.01  # 100 MHz
 
 
@@ -85,6 +85,37 @@ def summarize(stamps: list, G: int, N: int, mode: int) -> dict:
             "kernel": {k: med(v) for k, v in kern.items()}}
 
 
+def summarize_invcdf(stamps: list, N: int) -> dict:
+    """Inverse CDF: per step, medians over calls of when (after the last
+    workgroup's partials, i.e. its end of local work) the leaders have seen
+    every partial (last leader), published their decisions (last leader),
+    the workgroups have read the decisions (median / last), the owners have
+    published the tokens (last owner), the workgroups know every token
+    (median / last), and the next step starts."""
+    keys = ("seen", "dec", "h3_med", "h3_max", "own", "tok_med", "tok_max", "next")
+    rows = {k: [[] for _ in range(N)] for k in keys}
+
+    def last(a):
+        a = a[a > 0]
+        return a.max() if a.size else np.nan
+
+    for t in stamps:
+        for i in range(N):
+            p1 = t[:, i, 1].max()
+            us = lambda x: (x - p1) * TICK_US
+            rows["seen"][i].append(us(last(t[:, i, 10])))
+            rows["dec"][i].append(us(last(t[:, i, 11])))
+            rows["h3_med"][i].append(us(np.median(t[:, i, 8])))
+            rows["h3_max"][i].append(us(t[:, i, 8].max()))
+            rows["own"][i].append(us(last(t[:, i, 9])))
+            rows["tok_med"][i].append(us(np.median(t[:, i, 4])))
+            rows["tok_max"][i].append(us(t[:, i, 4].max()))
+            nxt = t[:, i + 1, 0].min() if i + 1 < N else t[:, i, 5].max()
+            rows["next"][i].append(us(nxt))
+    med = statistics.median
+    return {k: [med(v[i]) for i in range(N)] for k, v in rows.items()}
+
+
 def summarize_step_kernels(stamps: list, G: int, N: int) -> dict:
     """Step-kernel path (one launch per position): per launch, medians over
     calls of the entry spread, the first row block's inputs ready (median
@@ -119,6 +150,7 @@ def main() -> int:
     ap.add_argument("--calls", type=int, default=20)
     ap.add_argument("--cold", action="store_true", help="read 1 GiB before each call (evicts L2s and MALL)")
     ap.add_argument("--batch-path", choices=("auto", "persistent", "step"), default="auto")
+    ap.add_argument("--dump", help="also save the raw stamps [calls, workgroups, steps, phases] (ticks) to this .npy")
     args = ap.parse_args()
 
     import torch
@@ -151,6 +183,8 @@ def main() -> int:
         d.chain()
         binding.markov_status(d.workspace)
         stamps.append(read(lib, G, w.N))
+    if args.dump:
+        np.save(args.dump, np.stack(stamps))
     if step_path:
         st = summarize_step_kernels(stamps, G, w.N)
         print(f"## Step kernels: {w.name}, noise in memory, {'cold' if args.cold else 'warm'} calls, "
@@ -176,6 +210,16 @@ def main() -> int:
     for i in range(w.N):
         print(f"| {i} | {st['spread'][i]:.2f} | {st['local'][i]:.2f} | {st['pub'][i]:.2f} | "
               f"{st['win_med'][i]:.2f} / {st['win_max'][i]:.2f} | {st['step'][i]:.2f} |")
+    if w.mode == 1:
+        c = summarize_invcdf(stamps, w.N)
+        print("\nInverse CDF, after the last workgroup's partials (us): leaders have seen every partial, "
+              "decisions out, decisions read (median / last workgroup), owners' tokens out, tokens known "
+              "(median / last workgroup), next step's first start\n")
+        print("| step | partials seen | decisions out | decisions read | tokens out | tokens known | next step |")
+        print("|---|---|---|---|---|---|---|")
+        for i in range(w.N):
+            print(f"| {i} | {c['seen'][i]:.2f} | {c['dec'][i]:.2f} | {c['h3_med'][i]:.2f} / {c['h3_max'][i]:.2f} | "
+                  f"{c['own'][i]:.2f} | {c['tok_med'][i]:.2f} / {c['tok_max'][i]:.2f} | {c['next'][i]:.2f} |")
     return 0
 
 
