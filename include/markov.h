@@ -59,7 +59,7 @@ typedef enum {
 #define MARKOV_NOISE_INLINE 0x40
 
 /* Limits of this build. */
-#define MARKOV_MAX_ROWS 4096 /* one launch takes 64; more run as consecutive launches */
+#define MARKOV_MAX_ROWS 4096 /* one persistent launch takes 64; more run per position */
 #define MARKOV_MAX_STEPS 256
 #define MARKOV_MAX_VOCAB (1 << 24)
 
@@ -115,9 +115,17 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
                       int vocab, void* stream);
 
 /*
- * markov_chain_sample: the whole N-position chain for `rows` request rows in
- * one persistent launch (sharded_markov page, module docstring: one kernel
- * runs the whole chain and keeps the head in registers, so it is read once).
+ * markov_chain_sample: the whole N-position chain for `rows` request rows.
+ * Up to 64 rows run in one persistent launch (sharded_markov page, module
+ * docstring: one kernel runs the whole chain and keeps the head in
+ * registers, so it is read once).  Larger batches run per position over all
+ * rows (fused_markov page, FusedMarkovSampler: the fused loop that serves
+ * batches beyond the chain's rows): one step-kernel launch per position
+ * (MARKOV_MODE_GUMBEL with the noise in memory), or a step kernel and a
+ * pick kernel per position (MARKOV_MODE_INVCDF); inline-noise calls of more
+ * than 64 rows run as consecutive persistent launches of at most 64 rows.
+ * The step and pick kernels never wait for one another's workgroups, so the
+ * co-residency condition below applies to the persistent launches only.
  *
  * Launch and co-residency: the launch is a regular one (not a cooperative
  * launch) of at most one 512-thread workgroup per compute unit, and the
@@ -175,10 +183,9 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
  *                   marks a padding row.  Distinct non-negative entries.
  *   output_multiplier  fp32 multiplier (1.0f: none); finite.
  *   soft_cap        fp32 soft cap (0: none); finite, >= 0.
- *   rows in [1, MARKOV_MAX_ROWS] (more than 64 rows run as consecutive
- *   launches of at most 64 rows on `stream`, each reading the head once;
- *   row indices in the mode-1 hash and the identity state map stay the
- *   call's); steps in [1, MARKOV_MAX_STEPS]; vocab a
+ *   rows in [1, MARKOV_MAX_ROWS] (more than 64 rows run as described above,
+ *   in order on `stream`; row indices in the mode-1 hash and the identity
+ *   state map stay the call's); steps in [1, MARKOV_MAX_STEPS]; vocab a
  *   positive multiple of 16 up to MARKOV_MAX_VOCAB; rank 256 or 512;
  *   mode MARKOV_MODE_GUMBEL or MARKOV_MODE_INVCDF, with the element-type
  *   flags above and, for MARKOV_MODE_GUMBEL, MARKOV_NOISE_INLINE
@@ -278,17 +285,16 @@ const char* markov_last_error(void);
 int markov_set_grid(int g);
 
 /*
- * markov_set_batch_path: tuning and testing knob for MARKOV_MODE_GUMBEL calls
- * with the noise in memory.  0 (the default): batches of at most 64 rows run
- * as one persistent launch, larger batches as one step-kernel launch per
- * draft position over all rows (fused_markov page, FusedMarkovSampler: the
- * fused loop that serves batches beyond the persistent chain; muse_spark
- * markov page, MarkovSampler: per-row arrival counters whose last block
- * picks the winner).  1: always persistent launches of at most 64 rows, one
- * after another.  2: always step kernels (the workspace must then hold
- * that path's layout, which for at most 64 rows markov_workspace_bytes does
- * not promise).  Outputs do not depend on it.  Process-wide; returns the
- * previous value.
+ * markov_set_batch_path: tuning and testing knob for MARKOV_MODE_INVCDF calls
+ * and MARKOV_MODE_GUMBEL calls with the noise in memory.  0 (the default):
+ * batches of at most 64 rows run as one persistent launch, larger batches
+ * per draft position over all rows (fused_markov page, FusedMarkovSampler:
+ * the fused loop that serves batches beyond the persistent chain, the bias
+ * GEMM plus two kernels a position; muse_spark markov page, MarkovSampler:
+ * per-row arrival counters whose last block picks the winner).  1: always
+ * persistent launches of at most 64 rows, one after another.  2: always the
+ * per-position kernels.  markov_workspace_bytes covers every path.  Outputs
+ * do not depend on it.  Process-wide; returns the previous value.
  */
 int markov_set_batch_path(int path);
 

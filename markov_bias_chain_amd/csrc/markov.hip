@@ -269,7 +269,8 @@ __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memr
 // of any wave's 9 token published as a chunk's owner, 10 partials all seen
 // as a row's leader, 11 decision published.  Step kernel phases (per
 // launch): 0 entry, 1 first block's inputs issued, 2 all blocks done, 3 the
-// last workgroup's picks done.
+// last workgroup's picks done (mode 1: in workgroup 0's entry, the latest
+// pick-kernel wave done).
 constexpr int kTraceWGs = 1024, kTraceSteps = 32, kTracePhases = 12;
 #ifdef MARKOV_TRACE
 __device__ unsigned long long trace_buf[kTraceWGs * kTraceSteps * kTracePhases];
@@ -530,9 +531,10 @@ __host__ __device__ inline size_t half_bytes_needed(int rows, int N, int NC, int
 
 // A call of more than kLaunchRows rows runs either as persistent launches of
 // kLaunchRows rows and one of the rest, one after another in the same
-// workspace, or (mode 0) as one step-kernel launch per position over all its
-// rows: its half must hold the larger of those layouts.
-__host__ size_t step_half_bytes_host(int rows, int rank);
+// workspace, or as step-kernel launches per position over all its rows (any
+// call, when the path knob asks for them): its half holds the larger of
+// those layouts.
+__host__ size_t step_half_bytes_host(int rows, int rank, int mode, int NC);
 __host__ inline size_t call_half_bytes(int rows, int N, int NC, int mode, int rank) {
   const int full = rows < kLaunchRows ? rows : kLaunchRows;
   size_t b = half_bytes_needed(full, N, NC, mode);
@@ -541,10 +543,8 @@ __host__ inline size_t call_half_bytes(int rows, int N, int NC, int mode, int ra
     const size_t t = half_bytes_needed(tail, N, NC, mode);
     if (t > b) b = t;
   }
-  if (rows > kLaunchRows && mode == 0) {
-    const size_t t = step_half_bytes_host(rows, rank);
-    if (t > b) b = t;
-  }
+  const size_t t = step_half_bytes_host(rows, rank, mode, NC);
+  if (t > b) b = t;
   return b;
 }
 
@@ -1875,10 +1875,11 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
 }
 
 // ============================================================= step kernel ==
-// Batches beyond one persistent launch (more than kLaunchRows rows, mode 0):
-// one launch per draft position, as the pages' fused loop for large batches
-// (fused_markov page, FusedMarkovSampler: the bias GEMM plus the sampling
-// work, launched per position; muse_spark markov page, MarkovSampler: the
+// Batches beyond one persistent launch (more than kLaunchRows rows): per
+// draft position one step-kernel launch (mode 0), or a step kernel and a
+// pick kernel (mode 1), as the pages' fused loop for large batches
+// (fused_markov page, FusedMarkovSampler: the bias GEMM plus two kernels a
+// step, drawing by inverse CDF; muse_spark markov page, MarkovSampler: the
 // blocks of a row count their arrivals and the last one picks the winner).
 // Here the bias GEMM is fused into the step kernel (the bias never goes to
 // memory):
@@ -1889,34 +1890,50 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
 //  * the epilogue (bias -> bf16, + base, transform, cache store, score)
 //    runs in batches of 8 rows with 16-byte vectors, the next two batches'
 //    base logits and noise in flight;
-//  * each workgroup folds its best key of every row into the row's slot
-//    with an agent-scope atomic max (fire and forget), then counts itself on
-//    the step's arrival counter; the workgroup that arrives last writes the
-//    step's tokens, also into the workspace, from where every workgroup of
-//    the next launch loads its rows' winner embeddings itself (a gather of
-//    all rows by the last workgroup cost ~5.5 us per step at 256 rows).
-// No workgroup ever waits for another, so the launch needs no co-residency.
+//  * mode 0: each workgroup folds its best key of every row into the row's
+//    slot with an agent-scope atomic max (fire and forget), then counts
+//    itself on the step's arrival counter; the workgroup that arrives last
+//    writes the step's tokens, also into the workspace, from where every
+//    workgroup of the next launch loads its rows' winner embeddings itself
+//    (a gather of all rows by the last workgroup cost ~5.5 us per step at
+//    256 rows);
+//  * mode 1: each workgroup writes its chunk's partials of every row (the
+//    best key and the sum of exp(z - chunk max), as the persistent kernel's
+//    chunks publish them); the pick kernel that follows (one wave per row)
+//    combines them in chunk order, draws the row's uniform, finds the chunk
+//    holding u * S and scans that chunk's cache values in vocabulary order,
+//    with the persistent kernel's arithmetic (so both paths draw the same
+//    tokens), and writes the token.
+// No workgroup ever waits for another, so the launches need no
+// co-residency.
 //
 // Workspace half layout of this path (the parity protocol of the persistent
 // kernel: a call uses half P and its step-0 launch clears the other half
 // for the next call; the last launch flips P):
 //   arrive[2] u32 (256 bytes)          arrival counters, by step parity
-//   best[2][rows][kBestStride] u64     each row's best key, by step parity
-//                                      (one 128-byte line per row)
+//   mode 0: best[2][rows][kBestStride] u64   each row's best key, by step
+//                                      parity (one 128-byte line per row)
+//   mode 1: keys[rows][NC] u64, sums[rows][NC] u32   the chunks' partials
+//                                      (written, then read by the pick
+//                                      kernel that follows)
 //   tok[rows] i32                      the last step's tokens (-1: inert row)
-// The last workgroup of step i zeroes arrive[i & 1] and best[i & 1] after
-// reading them, so step i + 2 finds them zero.
+// Mode 0: the last workgroup of step i zeroes arrive[i & 1] and best[i & 1]
+// after reading them, so step i + 2 finds them zero.  Mode 1: the last
+// wave of the last pick launch to arrive zeroes arrive[0] and flips P.
 
 constexpr int kBestStride = 16;  // u64 words per row's best key (a 128-byte line)
 constexpr int kPrefetch = 2;     // epilogue batches whose inputs are in flight
 
-__host__ __device__ inline size_t step_half_bytes(int rows, int R) {
+__host__ __device__ inline size_t step_slots_bytes(int rows, int mode, int NC) {
+  return mode == 0 ? (size_t)2 * rows * kBestStride * 8 : (size_t)rows * NC * 12;
+}
+__host__ __device__ inline size_t step_half_bytes(int rows, int R, int mode, int NC) {
   (void)R;
-  const size_t b = 256 + (size_t)2 * rows * kBestStride * 8 + (size_t)rows * 4;
+  const size_t b = 256 + step_slots_bytes(rows, mode, NC) + (size_t)rows * 4;
   return (b + 255) & ~(size_t)255;
 }
 
-template <int R, bool FL>
+template <int R, bool FL, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int step) {
   constexpr int RPG = 16384 / R;
   constexpr int KSEG = R / 8;
@@ -1932,6 +1949,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   __shared__ float s_T[kBlock];
   __shared__ double s_rT[kBlock];
   __shared__ uint64_t s_key[kWaves][kBlock];
+  __shared__ float s_wsum[kWaves][MODE == 1 ? kBlock : 1];
   __shared__ float s_bias[kWaves][kRowPass * BS];
   __shared__ int s_last;
   __shared__ uint32_t s_parity;
@@ -1958,8 +1976,9 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   unsigned char* half = p.ws + kHeader + parity * p.ws_half;
   uint32_t* arrive = reinterpret_cast<uint32_t*>(half);
   uint64_t* best = reinterpret_cast<uint64_t*>(half + 256);
-  int* tokbuf = reinterpret_cast<int*>(half + 256 + (size_t)2 * rows * kBestStride * 8);
+  int* tokbuf = reinterpret_cast<int*>(half + 256 + step_slots_bytes(rows, MODE, p.NC));
   uint64_t* best_i = best + (size_t)(step & 1) * rows * kBestStride;
+  uint32_t* sums = reinterpret_cast<uint32_t*>(best + (size_t)rows * p.NC);  // mode 1
   if (step == 0) {
     // Clear the other half for the next call (nobody reads it in this one).
     uint4* other = reinterpret_cast<uint4*>(p.ws + kHeader + (parity ^ 1u) * p.ws_half);
@@ -1999,7 +2018,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
           in.bw[0] = t.x, in.bw[1] = t.y;
         }
       }
-      if (s_T[bl] > 0.0f) {
+      if (MODE == 0 && s_T[bl] > 0.0f) {
         const float4* grow = reinterpret_cast<const float4*>(p.gumbel + ((size_t)b * p.N + step) * (size_t)V + v0);
 #pragma unroll
         for (int e4 = 0; e4 < IPL / 4; ++e4) {
@@ -2150,8 +2169,10 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
 #pragma unroll
           for (int e = 0; e < IPL; ++e) z[e] = div_by_recip(z[e], rT);
         }
+        if (MODE == 0) {
 #pragma unroll
-        for (int e = 0; e < IPL; ++e) z[e] = __fadd_rn(z[e], cur.nz[e]);
+          for (int e = 0; e < IPL; ++e) z[e] = __fadd_rn(z[e], cur.nz[e]);
+        }
       }
       // this lane's first NaN, else first maximum; then the row's over its 8 lanes
       int kbest = INT_MIN;
@@ -2168,21 +2189,55 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
       const int gmax = group8_imax(kbest);
       const uint32_t gid = group8_umin(kbest != INT_MIN && kbest == gmax ? (uint32_t)v0 + ebest : 0xFFFFFFFFu);
       const uint32_t gnan = group8_umin(enan < IPL ? (uint32_t)v0 + enan : 0xFFFFFFFFu);
+      float wsum = 0.0f;
+      if (MODE == 1) {
+        // the group's sum of exp(z - max), as the persistent kernel forms it
+        const float m = order_key_inv(gmax);
+        float sm = 0.0f;
+        if (ok && gmax != INT_MIN && isfinite(m)) {
+#pragma unroll
+          for (int e = 0; e < IPL; ++e) sm += isnan(z[e]) ? 0.0f : __expf(z[e] - m);
+        }
+        wsum = group8_sum(sm);
+      }
       if (q == 0 && ok) {
         s_key[wave][bl] = gnan != 0xFFFFFFFFu ? ((0xFFFFFFFFull << 32) | (0xFFFFFFFFu - gnan))
                           : gmax != INT_MIN ? (((uint64_t)score_ord(order_key_inv(gmax)) << 32) | (0xFFFFFFFFu - gid))
                                             : kNoCandidate;
+        if (MODE == 1) s_wsum[wave][bl] = wsum;
       }
     }
-    // ---- the block's keys: the workgroup's best per row into the row's slot.
+    // ---- the block's keys: the workgroup's best per row into the row's
+    // slot (mode 0), or the chunk's partials of every row (mode 1: the 8
+    // waves' partials combined in wave order, as the persistent kernel does).
     __syncthreads();
     if (tid < nbr && s_active[tid]) {
       uint64_t K = kNoCandidate;
       for (int w = 0; w < kWaves; ++w) K = umax64(K, s_key[w][tid]);
-      if (K != kNoCandidate)
-        __hip_atomic_fetch_max(best_i + (size_t)(rb + tid) * kBestStride, K, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (MODE == 0) {
+        if (K != kNoCandidate)
+          __hip_atomic_fetch_max(best_i + (size_t)(rb + tid) * kBestStride, K, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        float S = 0.0f;
+        const float M = ord_score((uint32_t)(K >> 32));
+        if (K != kNoCandidate && isfinite(M)) {
+          for (int w = 0; w < kWaves; ++w) {
+            const uint64_t kw = s_key[w][tid];
+            const float mw = ord_score((uint32_t)(kw >> 32));
+            if (kw != kNoCandidate && isfinite(mw)) S += s_wsum[w][tid] * expf(mw - M);
+          }
+        }
+        const size_t slot = (size_t)(rb + tid) * p.NC + c;
+        best[slot] = K;
+        sums[slot] = __float_as_uint(S);
+      }
     }
     __syncthreads();
+  }
+  if (MODE == 1) {
+    TRACE_STAMP(c, step, 2);
+    return;  // the pick kernel follows
   }
 
   // ---- arrival; the last workgroup of the step picks every row's winner.
@@ -2217,11 +2272,191 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   TRACE_STAMP(c, step, 3);
 }
 
-__host__ size_t step_half_bytes_host(int rows, int rank) { return step_half_bytes(rows, rank); }
+// Mode 1, after the step kernel of each position: one wave per request row
+// draws the row's token from the chunks' partials.  The arithmetic is the
+// persistent kernel's, in the same order (its leader's combination of the
+// chunks and search, its owner's scan of the chosen chunk), so both paths
+// draw the same tokens.
+template <int R, bool FL>
+__global__ __launch_bounds__(64) void pick_kernel(ChainParams p, int step) {
+  constexpr int RPG = 16384 / R;
+  constexpr int CHUNK = kWaves * RPG;  // vocab ids per chunk
+  constexpr int PER = CHUNK / 64;      // ids per lane in the chunk scan
+  static_assert(PER == 8 || PER == 4, "chunk slice");
+  const bool cache_f32 = FL && p.cache_f32;
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x;
+  const int rows = p.rows, V = p.V, NC = p.NC;
+  uint32_t* header = reinterpret_cast<uint32_t*>(p.ws);
+  const uint32_t parity = ld_agent32(header) & 1u;
+  unsigned char* half = p.ws + kHeader + parity * p.ws_half;
+  uint32_t* arrive = reinterpret_cast<uint32_t*>(half);
+  const uint64_t* keys = reinterpret_cast<const uint64_t*>(half + 256) + (size_t)b * NC;
+  const uint32_t* sums = reinterpret_cast<const uint32_t*>(half + 256 + (size_t)rows * NC * 8) + (size_t)b * NC;
+  int* tokbuf = reinterpret_cast<int*>(half + 256 + step_slots_bytes(rows, 1, NC));
+  const int64_t st = p.state_idx ? p.state_idx[b] : (int64_t)b;
+  const int64_t tok0 = p.prev[b];
+  const bool active = st >= 0 && st < p.cache_states && tok0 >= 0 && tok0 < V;
+  int tok = -1;
+  if (active) {
+    const float T = p.temp[b];
+    const int KPL = (NC + 63) / 64;  // contiguous chunks per lane
+    uint64_t K = kNoCandidate;
+    for (int k = 0; k < KPL; ++k) {
+      const int c = lane * KPL + k;
+      if (c < NC) K = umax64(K, keys[c]);
+    }
+    K = wave_max_u64(K);
+    const float M = ord_score((uint32_t)(K >> 32));
+    if (!(T > 0.0f) || !isfinite(M)) {
+      const uint32_t tk = key_id(K);  // argmax: the lowest NaN id, or of the maximum
+      tok = tk < (uint32_t)V ? (int)tk : 0;
+    } else {
+      const float u = hash_uniform(noise_prefix(p.seeds[b], b, step));
+      // Chunk c's weight: its sum rescaled by exp(m_c - M); the lanes'
+      // totals scanned in chunk order.
+      auto weight = [&](int k, float& e) -> float {
+        e = 0.0f;
+        const int c = lane * KPL + k;
+        if (c >= NC) return 0.0f;
+        const uint64_t key = keys[c];
+        const float mc = ord_score((uint32_t)(key >> 32));
+        if (key == kNoCandidate || !isfinite(mc)) return 0.0f;
+        e = expf(mc - M);
+        return __uint_as_float(sums[c] & 0x7FFFFFFFu) * e;
+      };
+      float lsum = 0.0f;
+      for (int k = 0; k < KPL; ++k) {
+        float e;
+        lsum += weight(k, e);
+      }
+      const float incl = wave_incl_scan(lsum);
+      const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(incl), 63));
+      const float t = u * total;
+      // the first chunk with weight whose inclusive prefix exceeds t, else
+      // the last chunk with weight
+      int found = -1, last_pos = -1;
+      float before = 0.0f, wfound = 0.0f, last_before = 0.0f, last_w = 0.0f;
+      float run = incl - lsum;
+      for (int k = 0; k < KPL; ++k) {
+        float e;
+        const float w = weight(k, e);
+        const int c = lane * KPL + k;
+        if (found < 0 && w > 0.0f && run + w > t) {
+          found = c;
+          before = run;
+          wfound = e;
+        }
+        if (w > 0.0f) {
+          last_pos = c;
+          last_before = run;
+          last_w = e;
+        }
+        run += w;
+      }
+      const uint64_t hit = __ballot(found >= 0);
+      int o;
+      float tl;
+      if (hit) {
+        const int src = __builtin_ctzll(hit);
+        o = __shfl(found, src);
+        tl = (t - __shfl(before, src)) / __shfl(wfound, src);
+      } else {
+        const uint64_t any = __ballot(last_pos >= 0);
+        const int src = 63 - __builtin_clzll(any);
+        o = __shfl(last_pos, src);
+        tl = (t - __shfl(last_before, src)) / __shfl(last_w, src);
+      }
+      if (!(tl >= 0.0f)) tl = 0.0f;
+      if ((unsigned)o >= (unsigned)NC) o = NC - 1;
+      // The chosen chunk's cache values in vocabulary order, PER per lane.
+      const double rT = 1.0 / (double)T;
+      const int v0 = o * CHUNK + lane * PER;
+      const long long at = st * p.cache_rs + (long long)step * p.cache_ss + v0;
+      uint32_t cw[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) cw[k] = 0;
+      if (v0 < V) {
+        if (cache_f32) {
+          const uint4* crow = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.cache) + at);
+#pragma unroll
+          for (int k4 = 0; k4 < PER / 4; ++k4) {
+            const uint4 t4 = crow[k4];
+            cw[4 * k4] = t4.x, cw[4 * k4 + 1] = t4.y, cw[4 * k4 + 2] = t4.z, cw[4 * k4 + 3] = t4.w;
+          }
+        } else {
+          const uint16_t* crow = reinterpret_cast<const uint16_t*>(p.cache) + at;
+          uint32_t pk[PER / 2];
+          if constexpr (PER == 8) {
+            const uint4 t4 = *reinterpret_cast<const uint4*>(crow);
+            pk[0] = t4.x, pk[1] = t4.y, pk[2] = t4.z, pk[3] = t4.w;
+          } else {
+            const uint2 t2 = *reinterpret_cast<const uint2*>(crow);
+            pk[0] = t2.x, pk[1] = t2.y;
+          }
+#pragma unroll
+          for (int k = 0; k < PER; ++k) cw[k] = (k & 1) ? (pk[k / 2] & 0xFFFF0000u) : (pk[k / 2] << 16);
+        }
+      }
+      float z[PER];
+      float m = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const float cv = __uint_as_float(cw[k]);
+        z[k] = v0 < V ? (T != 1.0f ? div_by_recip(cv, rT) : cv) : -INFINITY;
+        m = fmaxf(m, z[k]);
+      }
+      m = order_key_inv(wave_imax(order_key(m)));  // the chunk's maximum (no NaN here)
+      float w[PER];
+      float csum = 0.0f;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        w[k] = (v0 + k < V && z[k] > -INFINITY) ? __expf(z[k] - m) : 0.0f;
+        csum += w[k];
+      }
+      float crun = wave_incl_scan(csum) - csum;
+      int fv = -1, lastv = -1;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        if (fv < 0 && w[k] > 0.0f && crun + w[k] > tl) fv = v0 + k;
+        if (w[k] > 0.0f) lastv = v0 + k;
+        crun += w[k];
+      }
+      const uint64_t chit = __ballot(fv >= 0);
+      if (chit) {
+        tok = __shfl(fv, __builtin_ctzll(chit));
+      } else {
+        const uint64_t any = __ballot(lastv >= 0);
+        tok = any ? __shfl(lastv, 63 - __builtin_clzll(any)) : o * CHUNK;
+      }
+    }
+    if (lane == 0) p.tokens[(long long)b * p.tok_rs + step] = tok;
+  }
+  if (lane == 0) tokbuf[b] = tok;
+  TRACE_STAMP_MAX(0, step, 3);  // the latest pick of the position
+  // The last step: the last wave to arrive flips the call parity (every
+  // pick wave of the call has read it by then, every step launch is done).
+  if (step + 1 == p.N && lane == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (uint32_t)(rows - 1)) {
+      st_agent32(arrive, 0u);
+      st_agent32(header, parity ^ 1u);
+    }
+  }
+}
+
+__host__ size_t step_half_bytes_host(int rows, int rank, int mode, int NC) {
+  return step_half_bytes(rows, rank, mode, NC);
+}
 
 template <bool FL>
-const void* step_kernel_for(int rank) {
-  return rank == 256 ? (const void*)step_kernel<256, FL> : (const void*)step_kernel<512, FL>;
+const void* step_kernel_for(int rank, int mode) {
+  if (mode == 1) return rank == 256 ? (const void*)step_kernel<256, FL, 1> : (const void*)step_kernel<512, FL, 1>;
+  return rank == 256 ? (const void*)step_kernel<256, FL, 0> : (const void*)step_kernel<512, FL, 0>;
+}
+template <bool FL>
+const void* pick_kernel_for(int rank) {
+  return rank == 256 ? (const void*)pick_kernel<256, FL> : (const void*)pick_kernel<512, FL>;
 }
 
 // ================================================================= host ==
@@ -2341,7 +2576,8 @@ int prepare_kernels() {
         for (int kind = 0; kind < 4; ++kind)
           for (int flags = 0; flags < 4; ++flags) allow(kernel_for(rank, mode, kind, flags & 1, flags & 2), rank);
     for (int rank : {256, 512})
-      for (int fl = 0; fl < 2; ++fl) allow(fl ? step_kernel_for<true>(rank) : step_kernel_for<false>(rank), rank);
+      for (int fl = 0; fl < 2; ++fl)
+        for (int mode : {0, 1}) allow(fl ? step_kernel_for<true>(rank, mode) : step_kernel_for<false>(rank, mode), rank);
   });
   if (err != hipSuccess) return fail(MARKOV_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(err));
   return MARKOV_OK;
@@ -2497,20 +2733,26 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
     if (rc != MARKOV_OK) return rc;
   }
   const size_t besz = base_f32 ? 4 : 2;
-  // Mode 0 with the noise in memory: batches beyond one persistent launch
-  // run one step kernel per position over all rows (or any batch, when the
-  // knob asks for that path).
+  // Batches beyond one persistent launch run per position over all rows: a
+  // step kernel (mode 0, the noise in memory), or a step kernel and a pick
+  // kernel (mode 1); also any batch, when the knob asks for that path.
   const int path = g_batch_path.load();
-  const bool use_step = mode == MARKOV_MODE_GUMBEL && !noise_inline &&
+  const bool use_step = (mode == MARKOV_MODE_INVCDF || !noise_inline) &&
                         (path == 2 || (path == 0 && rows > kLaunchRows));
   if (use_step) {
-    const size_t step_need = kHeader + 2 * step_half_bytes(rows, rank);
-    if (workspace_bytes < step_need)
+    const size_t step_half = step_half_bytes(rows, rank, mode, sh.NC);
+    const size_t step_need = kHeader + 2 * step_half;
+    if (no_alloc && step_need > kScratchBytes)
+      return fail(MARKOV_E_UNSUPPORTED,
+                  "this call shape needs %zu bytes of workspace; the allocation-free entry point has %zu "
+                  "(use markov_chain_sample with a workspace of markov_workspace_bytes)",
+                  step_need, (size_t)kScratchBytes);
+    if (!no_alloc && workspace_bytes < step_need)
       return fail(MARKOV_E_INVAL, "workspace_bytes=%zu < %zu needed by the step-kernel path", workspace_bytes,
                   step_need);
-    if (no_alloc && need_half < step_half_bytes(rows, rank)) {
+    if (no_alloc && need_half < step_half) {
       size_t cb = 0;
-      rc = static_scratch(step_half_bytes(rows, rank), stream, &workspace, &cb);
+      rc = static_scratch(step_half, stream, &workspace, &cb);
       if (rc != MARKOV_OK) return rc;
       clear_bytes = cb;
     }
@@ -2549,13 +2791,19 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
     p.clear_bytes = clear_bytes;
     p.wait_ticks = 0;
     p.nres = 0;
-    const void* kern = (base_f32 || cache_f32) ? step_kernel_for<true>(rank) : step_kernel_for<false>(rank);
+    const bool fl = base_f32 || cache_f32;
+    const void* kern = fl ? step_kernel_for<true>(rank, mode) : step_kernel_for<false>(rank, mode);
+    const void* pick = fl ? pick_kernel_for<true>(rank) : pick_kernel_for<false>(rank);
     const size_t shmem = (size_t)kLaunchRows * (rank / 8 + 1) * 16;
     for (int i = 0; i < steps; ++i) {
       int step = i;
       void* args[] = {&p, &step};
       hipError_t e = hipLaunchKernel(kern, dim3(sh.NC), dim3(kThreads), args, (unsigned)shmem, (hipStream_t)stream);
       if (e != hipSuccess) return fail(MARKOV_E_HIP, "step kernel launch (step %d): %s", i, hipGetErrorString(e));
+      if (mode == MARKOV_MODE_INVCDF) {
+        e = hipLaunchKernel(pick, dim3(rows), dim3(64), args, 0, (hipStream_t)stream);
+        if (e != hipSuccess) return fail(MARKOV_E_HIP, "pick kernel launch (step %d): %s", i, hipGetErrorString(e));
+      }
     }
     return MARKOV_OK;
   }

@@ -174,12 +174,12 @@ def large_vocab_stress() -> Workload:
     return w
 
 
-def dsv41_batch(rows: int) -> Workload:
+def dsv41_batch(rows: int, mode: int = 0) -> Workload:
     """Beyond the five named workloads: a DeepSeek-sized batch of `rows`
-    Gumbel rows (N=8, T=1, base as the 1-row case), for the > 64-row path
-    (consecutive launches of 64 rows)."""
-    return make(f"dsv41_V129280_r256_rows{rows}_N8", 129280, 256, rows, 8,
-                seed=MASTER_SEED + 6 + rows, peaks=32, temperature=1.0)
+    rows (N=8, T=1, base as the 1-row case), Gumbel or inverse CDF, for the
+    > 64-row path (per-position step kernels)."""
+    return make(f"dsv41_V129280_r256_rows{rows}_N8" + ("_invcdf" if mode == 1 else ""), 129280, 256, rows, 8,
+                seed=MASTER_SEED + 6 + rows, peaks=32, temperature=1.0, mode=mode)
 
 
 WORKLOADS = {
@@ -190,6 +190,7 @@ WORKLOADS = {
     "large_vocab_stress": large_vocab_stress,
     "dsv41_64rows": functools.partial(dsv41_batch, 64),
     "dsv41_256rows": functools.partial(dsv41_batch, 256),
+    "dsv41_invcdf_256rows": functools.partial(dsv41_batch, 256, 1),
 }
 
 

@@ -164,7 +164,7 @@ def main() -> int:
     w = synth.workload(args.workload)
     inline = args.noise == "inline" and w.mode == 0
     d = DeviceChain(w, device=dev, noise_inline=inline)
-    step_path = w.mode == 0 and not inline and (args.batch_path == "step" or (args.batch_path == "auto" and w.rows > 64))
+    step_path = (w.mode == 1 or not inline) and (args.batch_path == "step" or (args.batch_path == "auto" and w.rows > 64))
     G = binding.markov_grid(w.rows, w.N, w.V, w.r, w.mode)
     if step_path:  # one workgroup per chunk
         G = -(-w.V // (8 * (16384 // w.r)))
@@ -187,7 +187,8 @@ def main() -> int:
         np.save(args.dump, np.stack(stamps))
     if step_path:
         st = summarize_step_kernels(stamps, G, w.N)
-        print(f"## Step kernels: {w.name}, noise in memory, {'cold' if args.cold else 'warm'} calls, "
+        kind = "inverse CDF, step and pick kernels" if w.mode == 1 else "noise in memory"
+        print(f"## Step kernels: {w.name}, {kind}, {'cold' if args.cold else 'warm'} calls, "
               f"{G} workgroups per launch, medians over {args.calls} calls (us)\n")
         print("| step | entry spread | first block ready (median WG) | blocks done (median / last WG) "
               "| last WG's picks | launch (first entry to picks done) | gap to next launch |")

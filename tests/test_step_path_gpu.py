@@ -1,16 +1,20 @@
-"""The step-kernel path for large batches (one launch per draft position over
-all rows; the last workgroup to arrive picks the winners).
+"""The step-kernel path for large batches: per draft position one step
+kernel over all rows (mode 0: the last workgroup to arrive picks the
+winners) or a step kernel and a pick kernel (mode 1: one wave per row draws
+by inverse CDF from the chunks' partials).
 
 It must give exactly the outputs of the persistent path (both compute the
-bias with the same MFMA passes, so even random weights agree bit for bit),
-and sampled rows must equal the CPU oracle (bit for bit on integer-valued
-weights, within the derived tolerances on random ones).  Covered: padding
-rows, permuted state indices, greedy rows, the output transform, fp32 base
-logits and cache, r = 512, ragged vocabularies, the largest row count,
-repeated calls on one workspace shared with persistent calls, and the
-DeepSeek-sized 256-row batch.
+bias with the same MFMA passes and, in mode 1, combine the partials and
+scan the chosen chunk with the same arithmetic, so even random weights
+agree bit for bit), and sampled rows must equal the CPU oracle (bit for bit
+on integer-valued weights, within the derived tolerances on random ones).
+Covered, in both modes: padding rows, permuted state indices, greedy rows,
+the output transform, fp32 base logits and cache, r = 512, ragged
+vocabularies, the largest row count, repeated calls on one workspace shared
+with persistent calls, and the DeepSeek-sized 256-row batch.
 """
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -42,15 +46,17 @@ def _gpu():
     torch.cuda.synchronize()
 
 
+def noise_for(w):
+    return oracle.noise_fill(w.seeds, w.N, w.V) if w.mode == 0 else None
+
+
 def run_path(w, g, path, d=None):
-    """(tokens, cache) of one call on the given path (1 persistent, 2 step)."""
+    """(tokens, cache) of one call on the given path (1 persistent, 2 step);
+    the documented workspace size covers both paths."""
     if d is None:
         d = DeviceChain(w)
-        # room for either path's layout
-        need = max(lm.markov_workspace_bytes(w.rows, w.N, w.V, w.r, w.mode),
-                   256 + 2 * (256 + 2 * w.rows * 128 + 2 * w.rows * w.r * 2 + 255) // 256 * 256)
-        d.workspace = torch.zeros(need, dtype=torch.uint8, device="cuda")
-        d.set_gumbel(g)
+        if g is not None:
+            d.set_gumbel(g)
     lm.markov_set_batch_path(path)
     say(f"  path {path}: {w.name} V={w.V} r={w.r} rows={w.rows} N={w.N}")
     d.tokens.fill_(-7)
@@ -65,13 +71,13 @@ def oracle_rows(w, g, rows, c_dev):
     mask[rows] = 1
     tokens = np.full((w.rows, w.N), -7, dtype=np.int64)
     return oracle.chain(w.base, w.head, w.embed, w.prev, w.temperature, w.seeds, gumbel=g,
-                        state_idx=w.state_idx, mult=w.mult, cap=w.cap, mode=0, row_mask=mask,
+                        state_idx=w.state_idx, mult=w.mult, cap=w.cap, mode=w.mode, row_mask=mask,
                         tokens=tokens, cache=c_dev.copy(), cache_f32=w.cache_f32)
 
 
 def check_exact(w, rows):
     rows = [b for b in rows if b < w.rows]
-    g = oracle.noise_fill(w.seeds, w.N, w.V)
+    g = noise_for(w)
     (t2, c2), _ = run_path(w, g, 2)
     (t1, c1), _ = run_path(w, g, 1)
     assert np.array_equal(t1, t2), "step path tokens differ from the persistent path's"
@@ -86,38 +92,57 @@ def check_exact(w, rows):
         assert np.array_equal(c2[sidx[b]], ref_c[sidx[b]]), f"row {b}: cache differs from the oracle"
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("V,r,rows,N", [
     (4096 + 16, 256, 200, 3),   # ragged vocabulary, four row blocks (the last partial)
     (2048 + 32, 512, 130, 4),   # r = 512
     (16, 256, 65, 2),           # the smallest vocabulary, one row past a block
 ])
-def test_step_path_exact_integer_weights(V, r, rows, N):
+def test_step_path_exact_integer_weights(V, r, rows, N, mode):
     rng = np.random.default_rng(V + rows)
     sidx = rng.permutation(rows + 7)[:rows].astype(np.int64)
     sidx[[1, rows // 2, rows - 1]] = -1
     temps = np.array([1.0, 0.7, 0.0, 1.5, 0.6], dtype=np.float32)[np.arange(rows) % 5]
-    w = synth.make(f"step_V{V}_r{r}", V, r, rows, N, seed=V + r + rows, weights="int", base_std=2.0,
-                   temperature=temps, state_idx=sidx)
+    w = synth.make(f"step_V{V}_r{r}_m{mode}", V, r, rows, N, seed=V + r + rows, weights="int", base_std=2.0,
+                   temperature=temps, state_idx=sidx, mode=mode)
     check_exact(w, sorted({0, 1, 2, 63, 64, 65, rows // 2, rows - 2, rows - 1}))
 
 
+@pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("base_f32,cache_f32", [(True, False), (False, True), (True, True)])
-def test_step_path_fp32_types(base_f32, cache_f32):
+def test_step_path_fp32_types(base_f32, cache_f32, mode):
     rows = 96
-    w = synth.make("step_fl", 3000 - 8, 256, rows, 3, seed=91, weights="int", base_std=2.0,
+    w = synth.make(f"step_fl_m{mode}", 3000 - 8, 256, rows, 3, seed=91, weights="int", base_std=2.0,
                    temperature=np.array([1.0, 0.0, 1.3] * 32, dtype=np.float32), mult=0.5,
-                   base_f32=base_f32, cache_f32=cache_f32)
+                   base_f32=base_f32, cache_f32=cache_f32, mode=mode)
     check_exact(w, [0, 1, 2, 64, 95])
 
 
-def test_step_path_soft_cap():
+def test_step_path_invcdf_nan_inf_and_ties():
+    """Inverse CDF on the step path: rows whose logits hold NaN or +inf take
+    the argmax rule, exact ties keep the lowest id, and the last chunk and
+    ids past V are never drawn."""
+    rows = 70
+    w = synth.make("step_cdf_edges", 4096 + 48, 256, rows, 3, seed=97, weights="int", base_std=2.0,
+                   temperature=np.array([1.0, 0.8, 0.0, 2.5, 1.0] * 14, dtype=np.float32), mode=1)
+    base = w.base.copy()
+    base[3, 1, [17, 4000]] = 0x7FC0   # NaN: argmax rule, lowest NaN id
+    base[66, 0, [100, 2000]] = 0x7F80  # +inf: argmax rule, lowest id of the maximum
+    base[10, 2, [5, 700, 3000]] = 0x4220  # an exact tie at 40.0
+    base[69, :, -48:] = 0x42C8          # 100.0 on the ragged tail's ids
+    w = dataclasses.replace(w, base=base)
+    check_exact(w, [0, 3, 10, 64, 66, 69])
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_step_path_soft_cap(mode):
     """With the soft cap the two libraries' tanhf may differ in the last fp32
     bit, so the oracle comparison uses the tolerance walk; the two paths
     still agree bit for bit."""
     rows = 80
-    w = synth.make("step_cap", 8192, 256, rows, 3, seed=96, peaks=8, temperature=np.array(
-        [1.0, 0.0, 0.6, 1.5] * 20, dtype=np.float32), mult=0.5, cap=30.0)
-    g = oracle.noise_fill(w.seeds, w.N, w.V)
+    w = synth.make(f"step_cap_m{mode}", 8192, 256, rows, 3, seed=96, peaks=8, temperature=np.array(
+        [1.0, 0.0, 0.6, 1.5] * 20, dtype=np.float32), mult=0.5, cap=30.0, mode=mode)
+    g = noise_for(w)
     (t2, c2), _ = run_path(w, g, 2)
     (t1, c1), _ = run_path(w, g, 1)
     assert np.array_equal(t1, t2) and np.array_equal(c1, c2)
@@ -126,20 +151,23 @@ def test_step_path_soft_cap():
     assert st.token_match >= st.pairs - 1
 
 
-def test_step_path_forced_for_small_batches():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_step_path_forced_for_small_batches(mode):
     """The knob runs 1, 3 and 64 rows through the step kernels too; outputs
-    equal the persistent kernels' (one row, small batch and inverse-free
-    64-row variants)."""
+    equal the persistent kernels' (one row, small batch and 64-row
+    variants)."""
     for rows in (1, 3, 64):
-        w = synth.make(f"step_small{rows}", 20000, 256, rows, 4, seed=92 + rows, weights="int",
-                       base_std=2.0, temperature=0.9)
+        w = synth.make(f"step_small{rows}_m{mode}", 20000, 256, rows, 4, seed=92 + rows, weights="int",
+                       base_std=2.0, temperature=0.9, mode=mode)
         check_exact(w, list(range(min(rows, 4))))
 
 
-def test_step_path_most_rows():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_step_path_most_rows(mode):
     rows = lm.MARKOV_MAX_ROWS
-    w = synth.make("step_max", 1024, 256, rows, 2, seed=93, weights="int", base_std=2.0, temperature=1.0)
-    g = oracle.noise_fill(w.seeds, w.N, w.V)
+    w = synth.make(f"step_max_m{mode}", 1024, 256, rows, 2, seed=93, weights="int", base_std=2.0,
+                   temperature=1.0, mode=mode)
+    g = noise_for(w)
     (t, c), _ = run_path(w, g, 0)  # the default path for this size
     sample = [0, 63, 64, 1000, 2048, 4095]
     ref_t, ref_c = oracle_rows(w, g, sample, c)
@@ -148,18 +176,22 @@ def test_step_path_most_rows():
 
 
 def test_step_path_repeat_calls_share_a_workspace_with_persistent_calls():
-    """Step-path calls and persistent calls alternate on one workspace (both
-    use its parity halves); every result equals the first of its kind."""
+    """Step-path calls of both modes and persistent calls take turns on one
+    workspace (all use its parity halves); every result equals the first of
+    its kind."""
     big = synth.make("rep_big", 8192, 256, 100, 3, seed=94, temperature=0.8)
+    bigc = synth.make("rep_big_cdf", 8192, 256, 90, 3, seed=98, temperature=1.0, mode=1)
     small = synth.make("rep_small", 8192, 256, 5, 3, seed=95, temperature=1.1)
     gb, gs = oracle.noise_fill(big.seeds, big.N, big.V), oracle.noise_fill(small.seeds, small.N, small.V)
-    db, ds = DeviceChain(big), DeviceChain(small)
-    ds.workspace = db.workspace
+    db, dc, ds = DeviceChain(big), DeviceChain(bigc), DeviceChain(small)
+    ws = max((d.workspace for d in (db, dc, ds)), key=lambda t: t.numel())
+    for d in (db, dc, ds):
+        d.workspace = ws
     db.set_gumbel(gb)
     ds.set_gumbel(gs)
     ref = {}
-    for k in range(24):
-        d = db if k % 3 != 2 else ds
+    for k in range(30):
+        d = (db, dc, ds)[k % 3]
         d.tokens.fill_(-7)
         d.chain()
         out = d.results()
@@ -168,21 +200,25 @@ def test_step_path_repeat_calls_share_a_workspace_with_persistent_calls():
             assert np.array_equal(out[0], ref[name][0]) and np.array_equal(out[1], ref[name][1]), (k, name)
         else:
             ref[name] = (out[0].copy(), out[1].copy())
-    lm.markov_status(db.workspace)
+    lm.markov_status(ws)
     chain_check.walk(big, ref["rep_big"][0], ref["rep_big"][1], gb, rows=[0, 50, 99])
+    chain_check.walk(bigc, ref["rep_big_cdf"][0], ref["rep_big_cdf"][1], None, rows=[0, 45, 89])
     chain_check.walk(small, ref["rep_small"][0], ref["rep_small"][1], gs)
 
 
-def test_step_path_dsv41_256_rows():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_step_path_dsv41_256_rows(mode):
     """The DeepSeek-sized 256-row batch on random weights: the step path
     equals the persistent path bit for bit, and sampled rows pass the
     oracle walk."""
     w = synth.workload("dsv41_256rows")
-    g = oracle.noise_fill(w.seeds, w.N, w.V)
+    if mode == 1:
+        w = dataclasses.replace(w, name=w.name + "_invcdf", mode=1)
+    g = noise_for(w)
     (t2, c2), _ = run_path(w, g, 2)
     (t1, c1), _ = run_path(w, g, 1)
     assert np.array_equal(t1, t2) and np.array_equal(c1, c2)
     st = chain_check.walk(w, t2, c2, g, rows=[0, 1, 63, 64, 127, 128, 200, 255])
     say("  " + st.summary())
-    chain_check.record("step_path_dsv41_256rows_sampled", st)
+    chain_check.record(f"step_path_dsv41_256rows{'_invcdf' if mode else ''}_sampled", st)
     assert st.token_match >= 0.999 * st.pairs
