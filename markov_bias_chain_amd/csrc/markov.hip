@@ -310,55 +310,51 @@ __device__ __forceinline__ float div_by_recip(float c, double rT) { return (floa
 __device__ __noinline__ float log_f32_rn(float x) { return (float)log((double)x); }
 
 // A faster route to the same correctly rounded fp32 log of a positive
-// normal fp32 x.  x = m 2^e with m in [0.707, 1.414); with the bucket centre
-// m_j = 1 + j/128 nearest m, c_j an fp32 value near 1/m_j and
-// r = m c_j - 1 (exact in fp64: 24-bit times 24-bit), |r| < 2^-7.5,
+// normal fp32 x.  x = m 2^e with m in [sqrt(1/2), sqrt(2)) (from the bit
+// pattern: e = (bits(x) - bits(sqrt(1/2))) >> 23); with the bucket centre
+// m_j = 1 + j/128 nearest m, c_j an fp32 value near 1/m_j and r = m c_j - 1
+// (exact in fp64: 24-bit times 24-bit), |r| < 2^-7.49,
 //   ln x = e ln2 - ln c_j + ln(1 + r),
-//   ln(1 + r) = r - r^2/2 + r^3/3 + r^4 (-1/4 + r/5 - r^2/6) + O(r^7),
-// with the first three terms in fp64 and the r^4 tail (at most 2^-24.5 |r|)
-// in fp32.  The bucket of 1 has c = 1 and ln c = 0, so results near 0 keep
-// their relative accuracy; elsewhere |ln m| <= ln2/2 cannot cancel e ln2.
-// The fp64 result y is within about 2^-45 of ln x relatively (under 2^8 of
-// its ulps; an exhaustive host check over the noise's inputs saw at most 27),
-// so when the 29 bits of y below fp32 precision are more than 2^12 ulps away
-// from the rounding midpoint, rounding y gives the correctly rounded log;
-// otherwise (about 2^-16 of the inputs) the fp64 library log decides.
-// The buckets j = -38 .. 53: g_log_c[j + 38] = c_j, g_log_nlc[j + 38] =
-// -ln(c_j) correctly rounded to fp64 (written by gen_log_table.py).
+//   ln(1 + r) = r + r^2 (-1/2 + r (1/3 + r (-1/4 + r (1/5 - r/6)))) + O(r^7)
+// in fp64 (Horner).  The bucket index j + 38 is the integer that the fp32
+// rounding of m 128 + 1.5 2^23 - 90 leaves in its low bits (ties to even,
+// as a rounding of 128 (m - 1) would), and one 16-byte table entry holds
+// c_j and -ln c_j.  The bucket of 1 has c = 1 and ln c = 0, so results near
+// 0 keep their relative accuracy; elsewhere |ln m| <= ln2/2 cannot cancel
+// e ln2.  The truncated series is within r^6/7 < 2^-47.7 of ln(1 + r)
+// relatively, so the fp64 result y is within a few of its ulps of ln x (an
+// exhaustive host check over the noise's inputs saw at most 5); when the 29
+// bits of y below fp32 precision are more than 2^12 ulps away from the
+// rounding midpoint, rounding y gives the correctly rounded log; otherwise
+// (about 2^-16 of the inputs) the fp64 library log decides.
+// The buckets j = -38 .. 53: g_log_tab[j + 38] = {c_j, -ln(c_j) correctly
+// rounded to fp64} (written by gen_log_table.py).
 #include "log_table.inc"
 struct LogTable {
-  float c[kLogTable];
-  double nlc[kLogTable];
+  LogEntry e[kLogTable];
 };
 // The fast part: sets ok = false (and returns garbage) when the library
 // log must decide.
 __device__ __forceinline__ float log_f32_try(float x, const LogTable& t, bool& ok) {
   const uint32_t b = __float_as_uint(x);
-  int e = (int)(b >> 23) - 127;
-  float m = __uint_as_float((b & 0x7FFFFFu) | 0x3F800000u);  // [1, 2)
-  if (m >= 1.4140625f) {
-    m *= 0.5f;
-    e += 1;
-  }
-  const int k = (int)rintf(__fmaf_rn(m, 128.0f, -128.0f)) + kLogTableBias;  // (m - 1) * 128, exact
-  const double r = fma((double)m, (double)t.c[k], -1.0);
-  const float rf = (float)r;
-  float q = __fmaf_rn(-1.0f / 6.0f, rf, 0.2f);
-  q = __fmaf_rn(q, rf, -0.25f);
-  const float r2 = __fmul_rn(rf, rf);
-  const float tail = __fmul_rn(__fmul_rn(q, r2), r2);
-  const double lp = fma(r * r, fma(r, 1.0 / 3.0, -0.5), r) + (double)tail;  // ln(1 + r)
-  const double y = fma((double)e, 0x1.62e42fefa39efp-1, t.nlc[k] + lp);     // + e ln2
+  const int e = (int)(b - 0x3F3504F3u) >> 23;
+  const float m = __uint_as_float(b - ((uint32_t)e << 23));
+  const float f = __fmaf_rn(m, 128.0f, 12582822.0f);  // 1.5 2^23 + 128 (m - 1) + 38
+  const int k = __float_as_int(f) - 0x4B400000;
+  const double c = t.e[k].c, nlc = t.e[k].nlc;  // (as scalars: a struct copy lands on the stack)
+  const double r = fma((double)m, c, -1.0);
+  double q = fma(r, -1.0 / 6.0, 0.2);
+  q = fma(r, q, -0.25);
+  q = fma(r, q, 1.0 / 3.0);
+  q = fma(r, q, -0.5);
+  const double lp = fma(r * r, q, r);                                   // ln(1 + r)
+  const double y = fma((double)e, 0x1.62e42fefa39efp-1, nlc + lp);  // + e ln2
   const uint32_t low = (uint32_t)__double_as_longlong(y) & 0x1FFFFFFFu;
-  const int d = (int)low - (1 << 28);
-  ok = (d < 0 ? -d : d) > (1 << 12);
+  ok = low - ((1u << 28) - (1u << 12)) > (1u << 13);  // more than 2^12 from the midpoint 2^28
   return (float)y;
 }
 __device__ __forceinline__ void log_table_load(LogTable& t, int tid, int nthreads) {
-  for (int k = tid; k < kLogTable; k += nthreads) {
-    t.c[k] = g_log_c[k];
-    t.nlc[k] = g_log_nlc[k];
-  }
+  for (int k = tid; k < kLogTable; k += nthreads) t.e[k] = g_log_tab[k];
 }
 
 // The uniforms of M consecutive vocabulary ids v0 .. v0 + M - 1 of one
@@ -366,7 +362,7 @@ __device__ __forceinline__ void log_table_load(LogTable& t, int tid, int nthread
 template <int M>
 __device__ __forceinline__ void noise_uniforms(uint64_t prefix, int v0, float* u) {
 #pragma unroll
-  for (int j = 0; j < M; ++j) u[j] = hash_uniform(splitmix64(prefix ^ (uint64_t)(v0 + j)));
+  for (int j = 0; j < M; ++j) u[j] = hash_uniform(splitmix64(prefix ^ (uint64_t)(uint32_t)(v0 + j)));
 }
 
 // Gumbel noise -log(-log u) of M uniforms, both logs correctly rounded.  The
@@ -772,12 +768,11 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   const float r_T = p.temp[b_ld];
   const int64_t r_seed = (MODE == 1 || nz_inline) ? p.seeds[b_ld] : 0;
   const bool tab_thread = MODE == 0 && nz_inline && tid < kLogTable;
-  float t_c = 0.0f;
-  double t_nlc = 0.0;
+  double t_c = 0.0, t_nlc = 0.0;  // (scalars: a struct here lands on the stack)
   if (MODE == 0 && nz_inline) {
     const int k = tid < kLogTable ? tid : 0;
-    t_c = g_log_c[k];
-    t_nlc = g_log_nlc[k];
+    t_c = g_log_tab[k].c;
+    t_nlc = g_log_tab[k].nlc;
   }
   const uint32_t par = ld_agent32(header);
   // One row: the step-0 base logit (bf16 bits) of this lane's vocabulary id;
@@ -801,8 +796,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     s_abort = 0;
   }
   if (tab_thread) {
-    s_log.c[tid] = t_c;
-    s_log.nlc[tid] = t_nlc;
+    s_log.e[tid].c = t_c;
+    s_log.e[tid].nlc = t_nlc;
   }
   if (row_thread) {
     const int b = b_row;

@@ -16,28 +16,30 @@ static float ref_log(float x) { return (float)std::log((double)x); }
 static long fallbacks = 0;
 static bool list_fallbacks = false;  // print the inputs the fast path leaves to the library
 
-// Same operations, same order, as the kernel: bucket, r = m c - 1 in fp64,
-// the r^4 tail of ln(1 + r) in fp32, r - r^2/2 + r^3/3 in fp64, + e ln2 -
-// ln c, and the test of the 29 bits below fp32 precision against the
-// rounding midpoint, with the library log when it fails.
+static int asi(float f) { int b; std::memcpy(&b, &f, 4); return b; }
+
+// Same operations, same order, as the kernel: x = m 2^e from the bit pattern,
+// the bucket from the fp32 rounding of m 128 + 1.5 2^23 - 90, r = m c - 1 in
+// fp64, ln(1 + r) by Horner in fp64, + e ln2 - ln c, and the test of the 29
+// bits below fp32 precision against the rounding midpoint, with the library
+// log when it fails.
 static float fast_log(float x) {
   const uint32_t b = asu(x);
-  int e = (int)(b >> 23) - 127;
-  float m = asf((b & 0x7FFFFFu) | 0x3F800000u);
-  if (m >= 1.4140625f) { m *= 0.5f; e += 1; }
-  const int k = (int)std::rint(std::fmaf(m, 128.0f, -128.0f)) + kLogTableBias;
-  const double r = std::fma((double)m, (double)g_log_c[k], -1.0);
-  const float rf = (float)r;
-  float q = std::fmaf(-1.0f / 6.0f, rf, 0.2f);
-  q = std::fmaf(q, rf, -0.25f);
-  const float r2 = rf * rf;
-  const float tail = (q * r2) * r2;
-  const double lp = std::fma(r * r, std::fma(r, 1.0 / 3.0, -0.5), r) + (double)tail;
-  const double y = std::fma((double)e, 0x1.62e42fefa39efp-1, g_log_nlc[k] + lp);
+  const int e = (int)(b - 0x3F3504F3u) >> 23;
+  const float m = asf(b - ((uint32_t)e << 23));
+  const float f = std::fmaf(m, 128.0f, 12582822.0f);
+  const LogEntry te = g_log_tab[asi(f) - 0x4B400000];
+  const double r = std::fma((double)m, te.c, -1.0);
+  double q = std::fma(r, -1.0 / 6.0, 0.2);
+  q = std::fma(r, q, -0.25);
+  q = std::fma(r, q, 1.0 / 3.0);
+  q = std::fma(r, q, -0.5);
+  const double lp = std::fma(r * r, q, r);
+  const double y = std::fma((double)e, 0x1.62e42fefa39efp-1, te.nlc + lp);
   uint64_t yb;
   std::memcpy(&yb, &y, 8);
-  const int d = (int)((uint32_t)yb & 0x1FFFFFFFu) - (1 << 28);
-  if ((d < 0 ? -d : d) > (1 << 12)) return (float)y;
+  const uint32_t low = (uint32_t)yb & 0x1FFFFFFFu;
+  if (low - ((1u << 28) - (1u << 12)) > (1u << 13)) return (float)y;
   ++fallbacks;
   if (list_fallbacks) std::printf("%08x\n", b);
   return ref_log(x);

@@ -6,6 +6,8 @@ import math
 import os
 import re
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "markov_bias_chain_amd", "csrc")
 
@@ -18,10 +20,9 @@ def _gen():
 
 
 def _arrays(text):
-    def grab(name):
-        body = re.search(name + r"\[kLogTable\] = \{(.*?)\};", text, re.S).group(1)
-        return [float.fromhex(t.strip().rstrip("f")) for t in body.split(",") if t.strip()]
-    return grab("g_log_c"), grab("g_log_nlc")
+    body = re.search(r"g_log_tab\[kLogTable\] = \{(.*?)\n\};", text, re.S).group(1)
+    pairs = re.findall(r"\{([^,{}]+), ([^,{}]+)\}", body)
+    return [float.fromhex(c) for c, _ in pairs], [float.fromhex(v) for _, v in pairs]
 
 
 def test_committed_table_matches_generator():
@@ -34,7 +35,8 @@ def test_table_entries():
     assert len(c) == len(nlc) == 92
     for k, (cj, v) in enumerate(zip(c, nlc)):
         j = k - 38
-        # c_j is the fp32 value nearest 1 / (1 + j/128)
+        # c_j is the fp32 value nearest 1 / (1 + j/128), held exactly
+        assert float(np.float32(cj)) == cj
         assert abs(cj * (1 + j / 128) - 1) <= 2 ** -24
         # nlc_j = -ln(c_j) to within an ulp of fp64 (libm's log is not exact)
         assert abs(v + math.log(cj)) <= 2 ** -52 * max(abs(v), 2 ** -60)
