@@ -120,12 +120,15 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
  * docstring: one kernel runs the whole chain and keeps the head in
  * registers, so it is read once).  Larger batches run per position over all
  * rows (fused_markov page, FusedMarkovSampler: the fused loop that serves
- * batches beyond the chain's rows): one step-kernel launch per position
- * (MARKOV_MODE_GUMBEL with the noise in memory), or a step kernel and a
- * pick kernel per position (MARKOV_MODE_INVCDF); inline-noise calls of more
- * than 64 rows run as consecutive persistent launches of at most 64 rows.
- * The step and pick kernels never wait for one another's workgroups, so the
- * co-residency condition below applies to the persistent launches only.
+ * batches beyond the chain's rows): MARKOV_MODE_GUMBEL with the noise in
+ * memory runs one persistent step kernel for all positions (one workgroup
+ * per chunk of 8 * 16384 / rank vocabulary ids, when they fit on the compute
+ * units at once and the workspace holds its layout; otherwise one step
+ * kernel launch per position), MARKOV_MODE_INVCDF a step kernel and a pick
+ * kernel per position; inline-noise calls of more than 64 rows run as
+ * consecutive persistent launches of at most 64 rows.  The per-position
+ * launches never wait for one another's workgroups; the persistent kernels
+ * (chain and step kernel) are subject to the co-residency condition below.
  *
  * Launch and co-residency: the launch is a regular one (not a cooperative
  * launch) of at most one 512-thread workgroup per compute unit, and the
@@ -287,14 +290,17 @@ int markov_set_grid(int g);
 /*
  * markov_set_batch_path: tuning and testing knob for MARKOV_MODE_INVCDF calls
  * and MARKOV_MODE_GUMBEL calls with the noise in memory.  0 (the default):
- * batches of at most 64 rows run as one persistent launch, larger batches
- * per draft position over all rows (fused_markov page, FusedMarkovSampler:
- * the fused loop that serves batches beyond the persistent chain, the bias
- * GEMM plus two kernels a position; muse_spark markov page, MarkovSampler:
- * per-row arrival counters whose last block picks the winner).  1: always
- * persistent launches of at most 64 rows, one after another.  2: always the
- * per-position kernels.  markov_workspace_bytes covers every path.  Outputs
- * do not depend on it.  Process-wide; returns the previous value.
+ * batches of at most 64 rows run as one persistent chain launch, larger
+ * batches over all rows per draft position (fused_markov page,
+ * FusedMarkovSampler: the fused loop that serves batches beyond the
+ * persistent chain, the bias GEMM plus two kernels a position; muse_spark
+ * markov page, MarkovSampler: per-row arrival counters whose last block
+ * picks the winner), in MARKOV_MODE_GUMBEL by the persistent step kernel
+ * where it fits.  1: always persistent chain launches of at most 64 rows,
+ * one after another.  2: always one launch per position.  3: the
+ * persistent step kernel where it fits (MARKOV_MODE_GUMBEL; otherwise as 2).
+ * markov_workspace_bytes covers every path.  Outputs do not depend on it.
+ * Process-wide; returns the previous value.
  */
 int markov_set_batch_path(int path);
 

@@ -1922,14 +1922,28 @@ constexpr int kPrefetch = 2;     // epilogue batches whose inputs are in flight
 __host__ __device__ inline size_t step_slots_bytes(int rows, int mode, int NC) {
   return mode == 0 ? (size_t)2 * rows * kBestStride * 8 : (size_t)rows * NC * 12;
 }
+// The persistent mode-0 variant: best[N][rows][kBestStride] u64, then the
+// tokens as tagged words tags[rows] u64.
+__host__ __device__ inline size_t pers_half_bytes(int rows, int N) {
+  const size_t b = 256 + (size_t)N * rows * kBestStride * 8 + (size_t)rows * 8;
+  return (b + 255) & ~(size_t)255;
+}
 __host__ __device__ inline size_t step_half_bytes(int rows, int R, int mode, int NC) {
   (void)R;
   const size_t b = 256 + step_slots_bytes(rows, mode, NC) + (size_t)rows * 4;
   return (b + 255) & ~(size_t)255;
 }
 
-template <int R, bool FL, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int step) {
+// PERS (mode 0): one persistent launch runs every position, the head staying
+// in registers; the last workgroup of each position writes the tokens as
+// tagged words ((position + 1) << 32 | token), and each workgroup's
+// embedding loads of the next position wait (bounded) for the tags of the
+// rows they need.  The grid must then be co-resident (one workgroup per CU
+// at most); best keys and arrival counters are kept per position, so
+// nothing is reset within a call.
+template <int R, bool FL, int MODE, bool PERS>
+__global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int step_arg) {
+  static_assert(!PERS || MODE == 0, "the persistent variant is mode 0");
   constexpr int RPG = 16384 / R;
   constexpr int KSEG = R / 8;
   constexpr int ES = emb_stride<R>();
@@ -1948,15 +1962,19 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   __shared__ float s_bias[kWaves][kRowPass * BS];
   __shared__ int s_last;
   __shared__ uint32_t s_parity;
-  extern __shared__ uint4 s_e[];  // [kBlock][ES]; the last workgroup reuses it for tokens
+  __shared__ int s_toks[PERS ? MARKOV_MAX_ROWS : 1];  // PERS: the previous position's tokens
+  extern __shared__ uint4 s_e[];  // [kBlock][ES]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tid = threadIdx.x;  // (PERS: made opaque at every position, see below)
+  const int lane = tid & 63, wave = tid >> 6;
   const int c = blockIdx.x;
   const int rows = p.rows, V = p.V, NG = p.NG, G = p.G;
   uint32_t* header = reinterpret_cast<uint32_t*>(p.ws);
   const int rr = lane >> 3, q = lane & 7;
   const int g = c * kWaves + wave;  // this wave's group
-  const int v0 = g * RPG + q * IPL; // this lane's first vocab id in the batch layout
+  int v0 = g * RPG + q * IPL;  // this lane's first vocab id in the batch layout
+  int step = PERS ? 0 : step_arg;
+  const uint64_t deadline = now_ticks() + p.wait_ticks;  // (PERS: the token waits)
   TRACE_STAMP(c, step, 0);
 
   // The head of this wave's group, in flight while the rows are set up.
@@ -1972,7 +1990,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   uint32_t* arrive = reinterpret_cast<uint32_t*>(half);
   uint64_t* best = reinterpret_cast<uint64_t*>(half + 256);
   int* tokbuf = reinterpret_cast<int*>(half + 256 + step_slots_bytes(rows, MODE, p.NC));
-  uint64_t* best_i = best + (size_t)(step & 1) * rows * kBestStride;
+  uint64_t* tags = reinterpret_cast<uint64_t*>(half + 256 + (size_t)p.N * rows * kBestStride * 8);  // PERS
   uint32_t* sums = reinterpret_cast<uint32_t*>(best + (size_t)rows * p.NC);  // mode 1
   if (step == 0) {
     // Clear the other half for the next call (nobody reads it in this one).
@@ -2037,18 +2055,47 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
       const int bl = k / KSEG, seg = k - bl * KSEG;
       const int b = rb2 + bl;
       ne[j] = make_uint4(0, 0, 0, 0);
+      int64_t tok = -1;
       if (b < rows) {
-        int64_t tok = -1;
-        if (step == 0) {
+        if (PERS && step > 0) {
+          tok = s_toks[b];  // -1 for an inert row
+        } else if (step == 0) {
           const int64_t st = p.state_idx ? p.state_idx[b] : (int64_t)b;
           if (st >= 0 && st < p.cache_states) tok = p.prev[b];
         } else {
           tok = tokbuf[b];  // -1 for an inert row
         }
-        if (tok >= 0 && tok < V) ne[j] = *reinterpret_cast<const uint4*>(p.embed + (size_t)tok * R + seg * 8);
       }
+      if (b < rows && tok >= 0 && tok < V) ne[j] = *reinterpret_cast<const uint4*>(p.embed + (size_t)tok * R + seg * 8);
     }
   };
+  for (;; ++step) {
+  if constexpr (PERS) {
+    // Opaque at every position: the per-lane addresses derived from them
+    // are then formed inside the loop instead of being hoisted out of it
+    // and spilled (the head holds 128 registers for the whole launch).
+    asm volatile("" : "+v"(v0), "+v"(tid));
+  }
+  if (PERS && step > 0) {
+    TRACE_STAMP(c, step, 0);
+    // Every row's token of the previous position: thread t waits (bounded)
+    // for the tags of rows t, t + 512, ...; the tokens go to LDS.
+    for (int b = tid; b < rows; b += kThreads) {
+      uint64_t t = ld_agent(tags + b);
+      while ((uint32_t)(t >> 32) != (uint32_t)step) {
+        if (now_ticks() > deadline) {
+          __hip_atomic_fetch_or(header + 1, MARKOV_DEVERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          t = 0;  // token 0: the launch runs to its end
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        t = ld_agent(tags + b);
+      }
+      s_toks[b] = (int)(uint32_t)t;
+    }
+    __syncthreads();
+  }
+  uint64_t* best_i = best + (size_t)(PERS ? step : (step & 1)) * rows * kBestStride;
   emb_load(0);
 
   for (int rb = 0; rb < rows; rb += kBlock) {
@@ -2238,33 +2285,40 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   // ---- arrival; the last workgroup of the step picks every row's winner.
   TRACE_STAMP(c, step, 2);
   if (tid == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(arrive + (step & 1), 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(arrive + (PERS ? step : (step & 1)), 1u, __ATOMIC_ACQ_REL,
+                                                __HIP_MEMORY_SCOPE_AGENT);
     s_last = old == (uint32_t)(G - 1);
   }
   __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int b = tid; b < rows; b += kThreads) {
-    const int64_t st = p.state_idx ? p.state_idx[b] : (int64_t)b;
-    const int64_t tok0 = p.prev[b];
-    const bool active = st >= 0 && st < p.cache_states && tok0 >= 0 && tok0 < V;
-    int tok = -1;
-    if (active) {
-      const uint64_t K = ld_agent(best_i + (size_t)b * kBestStride);
-      const uint32_t win = key_id(K);
-      tok = (K > kNoCandidate && win < (uint32_t)V) ? (int)win : 0;
-      p.tokens[(long long)b * p.tok_rs + step] = tok;
-      st_agent(best_i + (size_t)b * kBestStride, 0);  // for step + 2
+  if (s_last) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    for (int b = tid; b < rows; b += kThreads) {
+      const int64_t st = p.state_idx ? p.state_idx[b] : (int64_t)b;
+      const int64_t tok0 = p.prev[b];
+      const bool active = st >= 0 && st < p.cache_states && tok0 >= 0 && tok0 < V;
+      int tok = -1;
+      if (active) {
+        const uint64_t K = ld_agent(best_i + (size_t)b * kBestStride);
+        const uint32_t win = key_id(K);
+        tok = (K > kNoCandidate && win < (uint32_t)V) ? (int)win : 0;
+        p.tokens[(long long)b * p.tok_rs + step] = tok;
+        if (!PERS) st_agent(best_i + (size_t)b * kBestStride, 0);  // for step + 2
+      }
+      if (PERS)
+        st_agent(tags + b, ((uint64_t)(step + 1) << 32) | (uint32_t)tok);
+      else
+        tokbuf[b] = tok;
     }
-    tokbuf[b] = tok;
+    if (tid == 0) {
+      if (!PERS) st_agent32(arrive + (step & 1), 0u);
+      // every workgroup of the call has read the parity by now
+      if (step + 1 == p.N) st_agent32(header, parity ^ 1u);
+    }
+    __syncthreads();
+    TRACE_STAMP(c, step, 3);
   }
-  if (tid == 0) {
-    st_agent32(arrive + (step & 1), 0u);
-    // every launch of the call has read the parity by now
-    if (step + 1 == p.N) st_agent32(header, parity ^ 1u);
+  if (!PERS || step + 1 == p.N) return;
   }
-  __syncthreads();
-  TRACE_STAMP(c, step, 3);
 }
 
 // Mode 1, after the step kernel of each position: one wave per request row
@@ -2445,9 +2499,11 @@ __host__ size_t step_half_bytes_host(int rows, int rank, int mode, int NC) {
 }
 
 template <bool FL>
-const void* step_kernel_for(int rank, int mode) {
-  if (mode == 1) return rank == 256 ? (const void*)step_kernel<256, FL, 1> : (const void*)step_kernel<512, FL, 1>;
-  return rank == 256 ? (const void*)step_kernel<256, FL, 0> : (const void*)step_kernel<512, FL, 0>;
+const void* step_kernel_for(int rank, int mode, bool pers = false) {
+  if (mode == 1)
+    return rank == 256 ? (const void*)step_kernel<256, FL, 1, false> : (const void*)step_kernel<512, FL, 1, false>;
+  if (pers) return rank == 256 ? (const void*)step_kernel<256, FL, 0, true> : (const void*)step_kernel<512, FL, 0, true>;
+  return rank == 256 ? (const void*)step_kernel<256, FL, 0, false> : (const void*)step_kernel<512, FL, 0, false>;
 }
 template <bool FL>
 const void* pick_kernel_for(int rank) {
@@ -2572,7 +2628,8 @@ int prepare_kernels() {
           for (int flags = 0; flags < 4; ++flags) allow(kernel_for(rank, mode, kind, flags & 1, flags & 2), rank);
     for (int rank : {256, 512})
       for (int fl = 0; fl < 2; ++fl)
-        for (int mode : {0, 1}) allow(fl ? step_kernel_for<true>(rank, mode) : step_kernel_for<false>(rank, mode), rank);
+        for (int k = 0; k < 3; ++k)
+          allow(fl ? step_kernel_for<true>(rank, k == 1, k == 2) : step_kernel_for<false>(rank, k == 1, k == 2), rank);
   });
   if (err != hipSuccess) return fail(MARKOV_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(err));
   return MARKOV_OK;
@@ -2733,9 +2790,25 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
   // kernel (mode 1); also any batch, when the knob asks for that path.
   const int path = g_batch_path.load();
   const bool use_step = (mode == MARKOV_MODE_INVCDF || !noise_inline) &&
-                        (path == 2 || (path == 0 && rows > kLaunchRows));
+                        (path >= 2 || (path == 0 && rows > kLaunchRows));
   if (use_step) {
-    const size_t step_half = step_half_bytes(rows, rank, mode, sh.NC);
+    // Mode 0: one persistent step kernel for all positions when its grid
+    // (one workgroup per chunk) fits on the compute units at once and the
+    // workspace holds its layout; otherwise one launch per position.
+    bool pers = false;
+    if (mode == MARKOV_MODE_GUMBEL && path != 2) {
+      int dev = 0, cus = 0, per_cu = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, (base_f32 || cache_f32) ? step_kernel_for<true>(rank, 0, true) : step_kernel_for<false>(rank, 0, true),
+            kThreads, (size_t)kLaunchRows * (rank / 8 + 1) * 16);
+      if (e != hipSuccess) return fail(MARKOV_E_HIP, "step kernel occupancy query: %s", hipGetErrorString(e));
+      const size_t avail = no_alloc ? (kScratchBytes - kHeader) / 2 : ((workspace_bytes - kHeader) / 2) & ~(size_t)255;
+      pers = per_cu >= 1 && sh.NC <= cus && pers_half_bytes(rows, steps) <= avail;
+    }
+    const size_t step_half = pers ? pers_half_bytes(rows, steps) : step_half_bytes(rows, rank, mode, sh.NC);
     const size_t step_need = kHeader + 2 * step_half;
     if (no_alloc && step_need > kScratchBytes)
       return fail(MARKOV_E_UNSUPPORTED,
@@ -2784,12 +2857,22 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
     p.ws = (unsigned char*)workspace;
     p.ws_half = ((workspace_bytes - kHeader) / 2) & ~(size_t)255;
     p.clear_bytes = clear_bytes;
-    p.wait_ticks = 0;
+    p.wait_ticks = pers ? g_wait_ticks.load() : 0;  // (only the persistent variant waits)
     p.nres = 0;
     const bool fl = base_f32 || cache_f32;
-    const void* kern = fl ? step_kernel_for<true>(rank, mode) : step_kernel_for<false>(rank, mode);
+    const void* kern = fl ? step_kernel_for<true>(rank, mode, pers) : step_kernel_for<false>(rank, mode, pers);
     const void* pick = fl ? pick_kernel_for<true>(rank) : pick_kernel_for<false>(rank);
     const size_t shmem = (size_t)kLaunchRows * (rank / 8 + 1) * 16;
+    if (pers) {
+      // A regular launch of at most one workgroup per CU (checked above):
+      // on an otherwise idle device every workgroup is resident at once;
+      // the token waits are bounded (MARKOV_DEVERR_TIMEOUT otherwise).
+      int step = 0;
+      void* args[] = {&p, &step};
+      hipError_t e = hipLaunchKernel(kern, dim3(sh.NC), dim3(kThreads), args, (unsigned)shmem, (hipStream_t)stream);
+      if (e != hipSuccess) return fail(MARKOV_E_HIP, "persistent step kernel launch: %s", hipGetErrorString(e));
+      return MARKOV_OK;
+    }
     for (int i = 0; i < steps; ++i) {
       int step = i;
       void* args[] = {&p, &step};
@@ -2871,7 +2954,9 @@ size_t markov_workspace_bytes(int rows, int steps, int vocab, int rank, int mode
   mode &= ~kModeFlags;
   Shape sh;
   if (check_shape(rows, steps, vocab, rank, mode, &sh) != MARKOV_OK) return 0;
-  return kHeader + 2 * call_half_bytes(rows, steps, sh.NC, mode, rank);
+  size_t half = call_half_bytes(rows, steps, sh.NC, mode, rank);
+  if (mode == MARKOV_MODE_GUMBEL && pers_half_bytes(rows, steps) > half) half = pers_half_bytes(rows, steps);
+  return kHeader + 2 * half;
 }
 
 int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps, int vocab,
@@ -2962,7 +3047,7 @@ const char* markov_last_error(void) { return g_last_error.c_str(); }
 
 int markov_set_grid(int g) { return g_grid_override.exchange(g < 0 ? 0 : g); }
 
-int markov_set_batch_path(int path) { return g_batch_path.exchange(path < 0 || path > 2 ? 0 : path); }
+int markov_set_batch_path(int path) { return g_batch_path.exchange(path < 0 || path > 3 ? 0 : path); }
 
 #ifdef MARKOV_TRACE
 // Trace builds only (not part of the ABI in markov.h): copies the first

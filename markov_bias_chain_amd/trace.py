@@ -149,7 +149,7 @@ def main() -> int:
     ap.add_argument("--noise", choices=("inline", "side"), default="inline")
     ap.add_argument("--calls", type=int, default=20)
     ap.add_argument("--cold", action="store_true", help="read 1 GiB before each call (evicts L2s and MALL)")
-    ap.add_argument("--batch-path", choices=("auto", "persistent", "step"), default="auto")
+    ap.add_argument("--batch-path", choices=("auto", "persistent", "step", "persistent-step"), default="auto")
     ap.add_argument("--dump", help="also save the raw stamps [calls, workgroups, steps, phases] (ticks) to this .npy")
     args = ap.parse_args()
 
@@ -160,11 +160,12 @@ def main() -> int:
     from markov_bias_chain_amd.device import DeviceChain
 
     dev = torch.device("cuda:0")
-    binding.markov_set_batch_path({"auto": 0, "persistent": 1, "step": 2}[args.batch_path])
+    binding.markov_set_batch_path({"auto": 0, "persistent": 1, "step": 2, "persistent-step": 3}[args.batch_path])
     w = synth.workload(args.workload)
     inline = args.noise == "inline" and w.mode == 0
     d = DeviceChain(w, device=dev, noise_inline=inline)
-    step_path = (w.mode == 1 or not inline) and (args.batch_path == "step" or (args.batch_path == "auto" and w.rows > 64))
+    step_path = (w.mode == 1 or not inline) and (args.batch_path in ("step", "persistent-step")
+                                                  or (args.batch_path == "auto" and w.rows > 64))
     G = binding.markov_grid(w.rows, w.N, w.V, w.r, w.mode)
     if step_path:  # one workgroup per chunk
         G = -(-w.V // (8 * (16384 // w.r)))

@@ -29,27 +29,47 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def _round256(x):
+    return -(-x // 256) * 256
+
+
+def _step_halves(rows, N, chunks, mode):
+    """The per-position paths' halves: mode 0 keeps each row's best key on a
+    128-byte line for two positions and 4-byte tokens, or (the persistent
+    step kernel) a line per position and 8-byte tagged tokens; mode 1 keeps
+    an 8-byte key and a 4-byte sum per (row, chunk) and 4-byte tokens."""
+    if mode == 0:
+        return max(_round256(256 + 2 * rows * 128 + rows * 4), _round256(256 + N * rows * 128 + rows * 8))
+    return _round256(256 + rows * chunks * 12 + rows * 4)
+
+
 def test_workspace_bytes():
-    # header + two halves; mode 0: an 8-byte key per (step, row, chunk) and an
+    # header + two halves, each the largest layout a call may use.  The
+    # persistent kernel, mode 0: an 8-byte key per (step, row, chunk) and an
     # 8-byte reducer partial per (step, row, 64 chunks) (512-id chunks at
     # r=256); up to 8 rows keep 16 copies of each step's partials, 512 bytes apart
     chunks = -(-129280 // 512)
     red = -(-chunks // 64)
-    half = -(-(8 * 1 * chunks * 8 + 8 * 16 * 64 * 8) // 256) * 256
+    half = max(_round256(8 * 1 * chunks * 8 + 8 * 16 * 64 * 8), _step_halves(1, 8, chunks, 0))
     assert lm.markov_workspace_bytes(1, 8, 129280, 256, 0) == 256 + 2 * half
     # one row without reducers (at most 64 chunks): one partial word per step, no copies
-    assert lm.markov_workspace_bytes(1, 8, 4096, 256, 0) == 256 + 2 * (-(-(8 * 8 * 8 + 8 * 8) // 256) * 256)
+    assert lm.markov_workspace_bytes(1, 8, 4096, 256, 0) == 256 + 2 * max(
+        _round256(8 * 8 * 8 + 8 * 8), _step_halves(1, 8, 8, 0))
     # more than 64 rows: launches of 64 rows and of the rest share the workspace
-    assert lm.markov_workspace_bytes(65, 8, 129280, 256, 0) == lm.markov_workspace_bytes(64, 8, 129280, 256, 0)
-    half9 = -(-(8 * 9 * chunks * 8 + 8 * 9 * red * 8) // 256) * 256
+    assert lm.markov_workspace_bytes(65, 8, 129280, 256, 0) == 256 + 2 * max(
+        _round256(8 * 64 * chunks * 8 + 8 * 64 * red * 8), _step_halves(65, 8, chunks, 0))
+    half9 = max(_round256(8 * 9 * chunks * 8 + 8 * 9 * red * 8), _step_halves(9, 8, chunks, 0))
     assert lm.markov_workspace_bytes(9, 8, 129280, 256, 0) == 256 + 2 * half9
     # mode 1 adds 4-byte sums and two 8-byte words per (step, row), each in
     # 16 copies, no partials
-    half1 = -(-(8 * 64 * chunks * 12 + 8 * 16 * 64 * 16) // 256) * 256
+    half1 = max(_round256(8 * 64 * chunks * 12 + 8 * 16 * 64 * 16), _step_halves(64, 8, chunks, 1))
     assert lm.markov_workspace_bytes(64, 8, 129280, 256, 1) == 256 + 2 * half1
+    # 256 rows: the per-position layouts are the larger
+    assert lm.markov_workspace_bytes(256, 8, 129280, 256, 1) == 256 + 2 * max(
+        half1, _step_halves(256, 8, chunks, 1))
     # r=512 chunks hold 256 ids
     c5 = 262144 // 256
-    half5 = -(-(16 * 8 * c5 * 8 + 16 * 8 * 16 * 64 * 8) // 256) * 256  # <= 8 rows: partial copies
+    half5 = max(_round256(16 * 8 * c5 * 8 + 16 * 8 * 16 * 64 * 8), _step_halves(8, 16, c5, 0))  # <= 8 rows: partial copies
     assert lm.markov_workspace_bytes(8, 16, 262144, 512, 0) == 256 + 2 * half5
 
 

@@ -51,8 +51,9 @@ def noise_for(w):
 
 
 def run_path(w, g, path, d=None):
-    """(tokens, cache) of one call on the given path (1 persistent, 2 step);
-    the documented workspace size covers both paths."""
+    """(tokens, cache) of one call on the given path (1 persistent chain
+    launches, 2 per-position launches, 3 the persistent step kernel); the
+    documented workspace size covers every path."""
     if d is None:
         d = DeviceChain(w)
         if g is not None:
@@ -82,6 +83,10 @@ def check_exact(w, rows):
     (t1, c1), _ = run_path(w, g, 1)
     assert np.array_equal(t1, t2), "step path tokens differ from the persistent path's"
     assert np.array_equal(c1, c2), "step path cache differs from the persistent path's"
+    if w.mode == 0:
+        (t3, c3), _ = run_path(w, g, 3)
+        assert np.array_equal(t3, t2), "persistent step kernel tokens differ from the per-position launches'"
+        assert np.array_equal(c3, c2), "persistent step kernel cache differs from the per-position launches'"
     ref_t, ref_c = oracle_rows(w, g, rows, c2)
     sidx = np.arange(w.rows) if w.state_idx is None else w.state_idx
     for b in rows:
@@ -146,6 +151,9 @@ def test_step_path_soft_cap(mode):
     (t2, c2), _ = run_path(w, g, 2)
     (t1, c1), _ = run_path(w, g, 1)
     assert np.array_equal(t1, t2) and np.array_equal(c1, c2)
+    if mode == 0:
+        (t3, c3), _ = run_path(w, g, 3)
+        assert np.array_equal(t3, t2) and np.array_equal(c3, c2)
     st = chain_check.walk(w, t2, c2, g, rows=[0, 1, 2, 3, 64, 79])
     say("  " + st.summary())
     assert st.token_match >= st.pairs - 1
@@ -218,6 +226,9 @@ def test_step_path_dsv41_256_rows(mode):
     (t2, c2), _ = run_path(w, g, 2)
     (t1, c1), _ = run_path(w, g, 1)
     assert np.array_equal(t1, t2) and np.array_equal(c1, c2)
+    if mode == 0:
+        (t3, c3), _ = run_path(w, g, 3)
+        assert np.array_equal(t3, t2) and np.array_equal(c3, c2)
     st = chain_check.walk(w, t2, c2, g, rows=[0, 1, 63, 64, 127, 128, 200, 255])
     say("  " + st.summary())
     chain_check.record(f"step_path_dsv41_256rows{'_invcdf' if mode else ''}_sampled", st)

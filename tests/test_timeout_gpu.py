@@ -84,9 +84,38 @@ def test_wait_limit_zero_times_out_then_recovers(V, rows, mode, inline):
     assert np.array_equal(t2, ref[0]) and np.array_equal(c2, ref[1])
 
 
+def test_persistent_step_kernel_times_out_then_recovers():
+    """The persistent step kernel (mode 0, large batches) waits for each
+    position's tokens: with a zero wait limit the workgroups that arrive
+    before the last one give up at once (every wait is bounded, every
+    workgroup runs to its end), MARKOV_DEVERR_TIMEOUT is reported, and after
+    the workspace is zeroed again the next call is exact."""
+    w = synth.make("timeout_pers", 8192, 256, 100, 3, seed=8293, weights="int", base_std=2.0, temperature=1.0)
+    g = oracle.noise_fill(w.seeds, w.N, w.V)
+    d = DeviceChain(w)
+    d.set_gumbel(g)
+    lm.markov_set_batch_path(3)
+    say("  persistent step kernel, rows=100: wait limit 0")
+    lm.markov_set_wait_limit(0)
+    d.chain()
+    torch.cuda.synchronize()
+    lm.markov_set_wait_limit(-1)
+    with pytest.raises(lm.MarkovError) as err:
+        lm.markov_status(d.workspace)
+    assert err.value.code == lm.MARKOV_E_DEVICE and "timed out" in str(err.value)
+    d.workspace.zero_()
+    d.tokens.fill_(-7)
+    d.chain()
+    lm.markov_status(d.workspace)
+    t, c = d.results()
+    ref = oracle.chain(w.base, w.head, w.embed, w.prev, w.temperature, w.seeds, gumbel=g)
+    assert np.array_equal(t, ref[0]) and np.array_equal(c, ref[1])
+
+
 def test_step_kernels_never_wait():
-    """The step-kernel path (large batches) has no cross-workgroup wait: with
-    a zero wait limit it still completes without an error and exactly."""
+    """The per-position launches (large batches) have no cross-workgroup
+    wait: with a zero wait limit they still complete without an error and
+    exactly."""
     w = synth.make("timeout_step", 8192, 256, 100, 3, seed=8292, weights="int", base_std=2.0, temperature=1.0)
     g = oracle.noise_fill(w.seeds, w.N, w.V)
     d = DeviceChain(w)
