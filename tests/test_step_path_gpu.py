@@ -123,6 +123,17 @@ def test_step_path_fp32_types(base_f32, cache_f32, mode):
     check_exact(w, [0, 1, 2, 64, 95])
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_step_path_more_chunks_than_compute_units(mode):
+    """513 chunks (V = 262160 at r = 256): more workgroups than CUs, so the
+    persistent step kernel does not apply and mode 0 runs one launch per
+    position on every path; sampled rows equal the oracle."""
+    rows = 70
+    w = synth.make(f"step_wide_m{mode}", 262144 + 16, 256, rows, 2, seed=99 + mode, weights="int", base_std=2.0,
+                   temperature=np.array([1.0, 0.0, 0.7, 1.5, 0.6] * 14, dtype=np.float32), mode=mode)
+    check_exact(w, [0, 1, 69])
+
+
 def test_step_path_invcdf_nan_inf_and_ties():
     """Inverse CDF on the step path: rows whose logits hold NaN or +inf take
     the argmax rule, exact ties keep the lowest id, and the last chunk and
