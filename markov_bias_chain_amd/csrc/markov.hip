@@ -1922,10 +1922,12 @@ constexpr int kPrefetch = 2;     // epilogue batches whose inputs are in flight
 __host__ __device__ inline size_t step_slots_bytes(int rows, int mode, int NC) {
   return mode == 0 ? (size_t)2 * rows * kBestStride * 8 : (size_t)rows * NC * 12;
 }
-// The persistent mode-0 variant: best[N][rows][kBestStride] u64, then the
-// tokens as tagged words tags[rows] u64.
+// The persistent mode-0 variant: an arrival counter per position u32,
+// best[N][rows][kBestStride] u64, then the tokens as tagged words
+// tags[rows] u64.
+__host__ __device__ inline size_t pers_arrive_bytes(int N) { return ((size_t)N * 4 + 255) & ~(size_t)255; }
 __host__ __device__ inline size_t pers_half_bytes(int rows, int N) {
-  const size_t b = 256 + (size_t)N * rows * kBestStride * 8 + (size_t)rows * 8;
+  const size_t b = pers_arrive_bytes(N) + (size_t)N * rows * kBestStride * 8 + (size_t)rows * 8;
   return (b + 255) & ~(size_t)255;
 }
 __host__ __device__ inline size_t step_half_bytes(int rows, int R, int mode, int NC) {
@@ -1988,9 +1990,10 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   const uint32_t parity = s_parity & 1u;
   unsigned char* half = p.ws + kHeader + parity * p.ws_half;
   uint32_t* arrive = reinterpret_cast<uint32_t*>(half);
-  uint64_t* best = reinterpret_cast<uint64_t*>(half + 256);
+  const size_t arrive_bytes = PERS ? pers_arrive_bytes(p.N) : 256;
+  uint64_t* best = reinterpret_cast<uint64_t*>(half + arrive_bytes);
   int* tokbuf = reinterpret_cast<int*>(half + 256 + step_slots_bytes(rows, MODE, p.NC));
-  uint64_t* tags = reinterpret_cast<uint64_t*>(half + 256 + (size_t)p.N * rows * kBestStride * 8);  // PERS
+  uint64_t* tags = reinterpret_cast<uint64_t*>(half + arrive_bytes + (size_t)p.N * rows * kBestStride * 8);  // PERS
   uint32_t* sums = reinterpret_cast<uint32_t*>(best + (size_t)rows * p.NC);  // mode 1
   if (step == 0) {
     // Clear the other half for the next call (nobody reads it in this one).
@@ -2005,15 +2008,19 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
     float nz[IPL];
   };
   // Batch inputs of rows b0 .. b0 + 7 of the current block (row rr of the
-  // batch in this lane), for active rows with valid ids only.
+  // batch in this lane).  Every lane loads, so that no branch skips the
+  // loads and the waits for a batch's inputs can count the loads issued
+  // after them; a lane whose row is inactive or whose ids lie past the
+  // vocabulary reads the arrays' first elements instead (the epilogue
+  // ignores its values), as does a lane of a zero-temperature row for the
+  // noise.
   auto load_in = [&](int rb, int b0, In& in) {
-#pragma unroll
-    for (int e = 0; e < IPL; ++e) in.bw[e] = 0, in.nz[e] = 0.0f;
     const int bl = b0 + rr;
     int b = rb + bl;
     asm volatile("" : "+v"(b));
-    if (bl < kBlock && b < rows && g < NG && v0 < V && s_active[bl]) {
-      const long long at = (long long)b * p.base_rs + (long long)step * p.base_ss + v0;
+    const bool lok = bl < kBlock && b < rows && g < NG && v0 < V && s_active[bl];
+    {
+      const long long at = lok ? (long long)b * p.base_rs + (long long)step * p.base_ss + v0 : 0;
       if (base_f32) {
         const uint4* brow = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.base) + at);
 #pragma unroll
@@ -2031,8 +2038,10 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
           in.bw[0] = t.x, in.bw[1] = t.y;
         }
       }
-      if (MODE == 0 && s_T[bl] > 0.0f) {
-        const float4* grow = reinterpret_cast<const float4*>(p.gumbel + ((size_t)b * p.N + step) * (size_t)V + v0);
+      if (MODE == 0) {
+        const bool nok = lok && s_T[bl] > 0.0f;
+        const float4* grow =
+            reinterpret_cast<const float4*>(p.gumbel + (nok ? ((size_t)b * p.N + step) * (size_t)V + v0 : 0));
 #pragma unroll
         for (int e4 = 0; e4 < IPL / 4; ++e4) {
           const float4 t = grow[e4];
@@ -2136,27 +2145,37 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
     // the first batches' inputs and the next block's embeddings, then the
     // embeddings visible to every wave
     const int nbat = (nbr + kBatch - 1) / kBatch;
-    In in[kPrefetch];
+    // kPrefetch + 1 input sets in a fixed rotation: batch t reads set
+    // t mod kSets and, before its epilogue, loads batch t + kPrefetch into
+    // the set batch t - 1 has finished with.  The batch loop is unrolled by
+    // kSets so that every set keeps its registers across iterations: a
+    // register copy at the loop's back edge would wait for the loads still
+    // in flight and leave a single batch of epilogue to hide them.
+    // Batches past the block's end load the dummy inputs too: with the same
+    // loads on every path, the wait for a batch's inputs is not forced down
+    // to the most recent load by a path that skipped the later ones.
+    constexpr int kSets = kPrefetch + 1;
+    In in[kSets];
 #pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) {
-      if (k < nbat) load_in(rb, k * kBatch, in[k]);
-    }
+    for (int k = 0; k < kPrefetch; ++k) load_in(rb, k * kBatch, in[k]);
     if (rb + kBlock < rows) emb_load(rb + kBlock);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     if (rb == 0) TRACE_STAMP(c, step, 1);
 
-    for (int t = 0; t < nbat; ++t) {
+    for (int t0 = 0; t0 < nbat; t0 += kSets) {
+#pragma unroll
+    for (int u = 0; u < kSets; ++u) {
+      const int t = t0 + u;
+      if (t >= nbat) break;
       const int b0 = t * kBatch;
       if ((t & 1) == 0) {
         const int np = nbr - b0 < kRowPass ? nbr - b0 : kRowPass;
         group_bias<R>(h, s_e, b0, np, lane, sb);
       }
-      const In cur = in[0];
-#pragma unroll
-      for (int k = 0; k + 1 < kPrefetch; ++k) in[k] = in[k + 1];
-      if (t + kPrefetch < nbat) load_in(rb, (t + kPrefetch) * kBatch, in[kPrefetch - 1]);
+      const In& cur = in[u];
+      load_in(rb, (t + kPrefetch) * kBatch, in[(u + kPrefetch) % kSets]);
       // ---- epilogue of the batch (row rr of the batch, IPL ids from v0)
       const int bl = b0 + rr;
       const bool ok = bl < nbr && g < NG && v0 < V && s_active[bl];
@@ -2248,6 +2267,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
                                             : kNoCandidate;
         if (MODE == 1) s_wsum[wave][bl] = wsum;
       }
+    }
     }
     // ---- the block's keys: the workgroup's best per row into the row's
     // slot (mode 0), or the chunk's partials of every row (mode 1: the 8

@@ -36,10 +36,12 @@ def _round256(x):
 def _step_halves(rows, N, chunks, mode):
     """The per-position paths' halves: mode 0 keeps each row's best key on a
     128-byte line for two positions and 4-byte tokens, or (the persistent
-    step kernel) a line per position and 8-byte tagged tokens; mode 1 keeps
-    an 8-byte key and a 4-byte sum per (row, chunk) and 4-byte tokens."""
+    step kernel) a 4-byte arrival counter per position, a line per
+    (position, row) and 8-byte tagged tokens; mode 1 keeps an 8-byte key and
+    a 4-byte sum per (row, chunk) and 4-byte tokens."""
     if mode == 0:
-        return max(_round256(256 + 2 * rows * 128 + rows * 4), _round256(256 + N * rows * 128 + rows * 8))
+        arrive = _round256(N * 4)
+        return max(_round256(256 + 2 * rows * 128 + rows * 4), _round256(arrive + N * rows * 128 + rows * 8))
     return _round256(256 + rows * chunks * 12 + rows * 4)
 
 
@@ -67,6 +69,10 @@ def test_workspace_bytes():
     # 256 rows: the per-position layouts are the larger
     assert lm.markov_workspace_bytes(256, 8, 129280, 256, 1) == 256 + 2 * max(
         half1, _step_halves(256, 8, chunks, 1))
+    # the persistent step kernel's arrival counters outgrow 256 bytes at
+    # more than 64 positions
+    assert lm.markov_workspace_bytes(65, 256, 4096, 256, 0) >= 256 + 2 * _step_halves(65, 256, 16, 0)
+    assert _step_halves(65, 256, 16, 0) == _round256(_round256(256 * 4) + 256 * 65 * 128 + 65 * 8)
     # r=512 chunks hold 256 ids
     c5 = 262144 // 256
     half5 = max(_round256(16 * 8 * c5 * 8 + 16 * 8 * 16 * 64 * 8), _step_halves(8, 16, c5, 0))  # <= 8 rows: partial copies

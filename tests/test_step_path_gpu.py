@@ -123,6 +123,17 @@ def test_step_path_fp32_types(base_f32, cache_f32, mode):
     check_exact(w, [0, 1, 2, 64, 95])
 
 
+def test_persistent_step_kernel_many_positions():
+    """72 positions of 130 rows (three row blocks, the last of two rows):
+    the persistent step kernel keeps an arrival counter per position, more
+    than fit in the 256 bytes before its best keys; all paths agree and
+    sampled rows equal the oracle."""
+    rows = 130
+    w = synth.make("step_many_positions", 4096 + 16, 256, rows, 72, seed=101, weights="int", base_std=2.0,
+                   temperature=np.array([1.0, 0.0, 0.7, 1.5, 0.6] * 26, dtype=np.float32))
+    check_exact(w, [0, 64, 128, 129])
+
+
 @pytest.mark.parametrize("mode", [0, 1])
 def test_step_path_more_chunks_than_compute_units(mode):
     """513 chunks (V = 262160 at r = 256): more workgroups than CUs, so the
