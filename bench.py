@@ -112,6 +112,30 @@ def algorithmic_bytes(w, inline: bool) -> dict:
                 reads=head + base + noise_read + embed)
 
 
+def launch_kind(w, inline: bool, batch_path: str):
+    """(dominant kernel, description) of the launches a call makes, by the
+    library's documented dispatch: step kernels per position for mode 1 or
+    noise in memory beyond 64 rows (or when the path knob asks), the
+    persistent step kernel for mode 0 when its grid of one workgroup per
+    chunk fits on the CUs at once, else persistent chain launches of at most
+    64 rows."""
+    import torch
+
+    step = (w.mode == 1 or not inline) and (batch_path in ("step", "persistent-step")
+                                            or (batch_path == "auto" and w.rows > 64))
+    if not step:
+        n = -(-w.rows // 64)
+        what = "chain kernel drawing its noise inline" if inline else "chain kernel"
+        return "chain_kernel", f"{what} ({n} launch{'es' if n > 1 else ''})"
+    chunks = -(-w.V // (8 * (16384 // w.r)))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if w.mode == 0 and batch_path != "step" and chunks <= cus:
+        return "step_kernel", "persistent step kernel (one launch)"
+    if w.mode == 1:
+        return "step_kernel", f"step kernel + pick kernel per position ({2 * w.N} launches)"
+    return "step_kernel", f"step kernel per position ({w.N} launches)"
+
+
 def cpu_baseline(w, budget_s: float) -> dict:
     """The oracle as it stands (single-threaded C), timed on whole calls of
     the same workload, with its own noise, for about budget_s seconds."""
@@ -331,10 +355,12 @@ def main() -> int:
                     help="mode 0: noise drawn inside the chain kernel, or by the noise fill "
                          "kernel on a side stream; auto: inline up to 8 rows (the chain's idle "
                          "waves draw it), side stream beyond")
-    ap.add_argument("--batch-path", choices=("auto", "persistent", "step"), default="auto",
-                    help="mode 0 with the noise in memory: persistent launches of at most 64 rows, "
-                         "or one step-kernel launch per position over all rows; auto: step kernels "
-                         "beyond 64 rows")
+    ap.add_argument("--batch-path", choices=("auto", "persistent", "step", "persistent-step"), default="auto",
+                    help="mode 1, and mode 0 with the noise in memory: persistent chain launches of "
+                         "at most 64 rows; step kernels per position over all rows (mode 1: with a "
+                         "pick kernel); or (mode 0) one persistent step kernel for all positions; "
+                         "auto: beyond 64 rows the persistent step kernel when its grid fits on "
+                         "the CUs at once (mode 0), else the step kernels")
     ap.add_argument("--cold", type=int, default=50, help="cold calls timed after the main loop")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -444,7 +470,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    binding.markov_set_batch_path({"auto": 0, "persistent": 1, "step": 2}[args.batch_path])
+    binding.markov_set_batch_path({"auto": 0, "persistent": 1, "step": 2, "persistent-step": 3}[args.batch_path])
     w = synth.workload(args.workload)
     noise = args.noise if args.noise != "auto" else ("inline" if w.real_rows <= 8 else "side")
     inline = noise == "inline" and w.mode == 0
@@ -457,6 +483,7 @@ def main() -> int:
     chain_us_med = statistics.median(chain_ms) * 1e3
     cold_us_med = statistics.median(cold_ms) * 1e3 if cold_ms else None
     achieved = ab["total"] / (chain_us * 1e-6) / 1e9
+    kernel, chain_desc = launch_kind(w, inline, args.batch_path)
     result = {
         "metric": "µs/call & draft tokens/s, V=129280 r=256 N=8 rows=1/8; head GB/s vs HBM peak",
         "value": tok_per_step / (ms_per_step * 1e-3),
@@ -477,9 +504,8 @@ def main() -> int:
                    "grid": binding.markov_grid(w.rows, w.N, w.V, w.r, w.mode),
                    "noise": "inline" if inline else ("side stream" if w.mode == 0 else "none"),
                    "batch_path": args.batch_path,
-                   "step": ("chain kernel drawing its noise inline (one launch)" if inline
-                            else "chain kernel (one launch)" if w.mode == 1
-                            else "noise fill on a side stream + chain kernel") + ", " + m["issue"]},
+                   "step": ("noise fill on a side stream + " if (w.mode == 0 and not inline) else "")
+                           + chain_desc + ", " + m["issue"]},
         "chain_us_per_call": {"back_to_back_mean": chain_us,
                               "warm_event_mean": statistics.mean(chain_ms) * 1e3,
                               "warm_median": chain_us_med,
@@ -491,7 +517,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(noise) if args.workload == "dsv41_single_row" else None,
-                     "kernel": "chain_kernel", "bytes_per_launch": ab["total"]},
+                     "kernel": kernel, "bytes_per_launch": ab["total"]},
     }
     if args.workload == "dsv41_single_row":
         result["head_residency"] = head_residency(w, inline, noise)

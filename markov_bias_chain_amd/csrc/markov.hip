@@ -2010,11 +2010,18 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   // Batch inputs of rows b0 .. b0 + 7 of the current block (row rr of the
   // batch in this lane).  Every lane loads, so that no branch skips the
   // loads and the waits for a batch's inputs can count the loads issued
-  // after them; a lane whose row is inactive or whose ids lie past the
-  // vocabulary reads the arrays' first elements instead (the epilogue
-  // ignores its values), as does a lane of a zero-temperature row for the
-  // noise.
+  // after them.  A lane whose row is inactive (this includes every row of a
+  // batch past the block's end) or whose ids lie past the vocabulary reads
+  // the arrays' first elements instead, as does a lane of a
+  // zero-temperature row for the noise; the epilogue ignores these values.
+  // The persistent variant instead reloads the block's last batch for a
+  // batch past the block's end (lines still in the L2s): measured faster
+  // there, and slower for the per-position launches.
   auto load_in = [&](int rb, int b0, In& in) {
+    if constexpr (PERS) {
+      const int nbr_in = rows - rb < kBlock ? rows - rb : kBlock;
+      if (b0 >= nbr_in) b0 = (nbr_in - 1) / kBatch * kBatch;
+    }
     const int bl = b0 + rr;
     int b = rb + bl;
     asm volatile("" : "+v"(b));
