@@ -114,26 +114,25 @@ def algorithmic_bytes(w, inline: bool) -> dict:
 
 def launch_kind(w, inline: bool, batch_path: str):
     """(dominant kernel, description) of the launches a call makes, by the
-    library's documented dispatch: step kernels per position for mode 1 or
-    noise in memory beyond 64 rows (or when the path knob asks), the
-    persistent step kernel for mode 0 when its grid of one workgroup per
-    chunk fits on the CUs at once, else persistent chain launches of at most
-    64 rows."""
+    library's documented dispatch: beyond 64 rows (or when the path knob
+    asks) step kernels, in mode 0 the persistent step kernel when its grid of
+    one workgroup per chunk fits on the CUs at once, else one launch per
+    position (mode 1: with a pick kernel); otherwise persistent chain
+    launches of at most 64 rows."""
     import torch
 
-    step = (w.mode == 1 or not inline) and (batch_path in ("step", "persistent-step")
-                                            or (batch_path == "auto" and w.rows > 64))
+    drawing = " drawing its noise inline" if inline else ""
+    step = batch_path in ("step", "persistent-step") or (batch_path == "auto" and w.rows > 64)
     if not step:
         n = -(-w.rows // 64)
-        what = "chain kernel drawing its noise inline" if inline else "chain kernel"
-        return "chain_kernel", f"{what} ({n} launch{'es' if n > 1 else ''})"
+        return "chain_kernel", f"chain kernel{drawing} ({n} launch{'es' if n > 1 else ''})"
     chunks = -(-w.V // (8 * (16384 // w.r)))
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if w.mode == 0 and batch_path != "step" and chunks <= cus:
-        return "step_kernel", "persistent step kernel (one launch)"
+        return "step_kernel", f"persistent step kernel{drawing} (one launch)"
     if w.mode == 1:
         return "step_kernel", f"step kernel + pick kernel per position ({2 * w.N} launches)"
-    return "step_kernel", f"step kernel per position ({w.N} launches)"
+    return "step_kernel", f"step kernel{drawing} per position ({w.N} launches)"
 
 
 def cpu_baseline(w, budget_s: float) -> dict:

@@ -52,8 +52,9 @@ typedef enum {
 
 /* Noise placement, OR-ed into MARKOV_MODE_GUMBEL (sharded_markov page,
  * fork_noise; fused_markov page, module docstring: Gumbel-max costs a hash
- * and two logs per logit).  With MARKOV_NOISE_INLINE the chain kernel draws
- * gumbel[b][i][v] itself, from seeds, bit-identical to what
+ * and two logs per logit).  With MARKOV_NOISE_INLINE the chain's kernels
+ * (the persistent chain kernel and the step kernels) draw gumbel[b][i][v]
+ * themselves, from seeds, bit-identical to what
  * markov_noise_fill writes; `gumbel` is then not read and may be NULL, and
  * `seeds` is required.  Without it the noise is read from `gumbel`. */
 #define MARKOV_NOISE_INLINE 0x40
@@ -120,15 +121,15 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps,
  * docstring: one kernel runs the whole chain and keeps the head in
  * registers, so it is read once).  Larger batches run per position over all
  * rows (fused_markov page, FusedMarkovSampler: the fused loop that serves
- * batches beyond the chain's rows): MARKOV_MODE_GUMBEL with the noise in
- * memory runs one persistent step kernel for all positions (one workgroup
- * per chunk of 8 * 16384 / rank vocabulary ids, when they fit on the compute
- * units at once and the workspace holds its layout; otherwise one step
- * kernel launch per position), MARKOV_MODE_INVCDF a step kernel and a pick
- * kernel per position; inline-noise calls of more than 64 rows run as
- * consecutive persistent launches of at most 64 rows.  The per-position
- * launches never wait for one another's workgroups; the persistent kernels
- * (chain and step kernel) are subject to the co-residency condition below.
+ * batches beyond the chain's rows): MARKOV_MODE_GUMBEL runs one persistent
+ * step kernel for all positions (one workgroup per chunk of 8 * 16384 / rank
+ * vocabulary ids, when they fit on the compute units at once and the
+ * workspace holds its layout; otherwise one step kernel launch per
+ * position), with the noise read from memory or, with MARKOV_NOISE_INLINE,
+ * drawn by the step kernel itself (the same values); MARKOV_MODE_INVCDF runs
+ * a step kernel and a pick kernel per position.  The per-position launches
+ * never wait for one another's workgroups; the persistent kernels (chain and
+ * step kernel) are subject to the co-residency condition below.
  *
  * Launch and co-residency: the launch is a regular one (not a cooperative
  * launch) of at most one 512-thread workgroup per compute unit, and the
@@ -288,8 +289,8 @@ const char* markov_last_error(void);
 int markov_set_grid(int g);
 
 /*
- * markov_set_batch_path: tuning and testing knob for MARKOV_MODE_INVCDF calls
- * and MARKOV_MODE_GUMBEL calls with the noise in memory.  0 (the default):
+ * markov_set_batch_path: tuning and testing knob for markov_chain_sample's
+ * choice of kernels.  0 (the default):
  * batches of at most 64 rows run as one persistent chain launch, larger
  * batches over all rows per draft position (fused_markov page,
  * FusedMarkovSampler: the fused loop that serves batches beyond the

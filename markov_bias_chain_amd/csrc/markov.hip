@@ -1943,9 +1943,13 @@ __host__ __device__ inline size_t step_half_bytes(int rows, int R, int mode, int
 // rows they need.  The grid must then be co-resident (one workgroup per CU
 // at most); best keys and arrival counters are kept per position, so
 // nothing is reset within a call.
-template <int R, bool FL, int MODE, bool PERS>
+// NZ (mode 0): the kernel draws the Gumbel noise of each element itself, in
+// the epilogue, with the noise fill kernel's function (bit-identical
+// values), instead of reading it from memory.
+template <int R, bool FL, int MODE, bool PERS, bool NZ>
 __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int step_arg) {
   static_assert(!PERS || MODE == 0, "the persistent variant is mode 0");
+  static_assert(!NZ || MODE == 0, "inline noise is mode 0's");
   constexpr int RPG = 16384 / R;
   constexpr int KSEG = R / 8;
   constexpr int ES = emb_stride<R>();
@@ -1965,6 +1969,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   __shared__ int s_last;
   __shared__ uint32_t s_parity;
   __shared__ int s_toks[PERS ? MARKOV_MAX_ROWS : 1];  // PERS: the previous position's tokens
+  __shared__ int64_t s_seed[NZ ? kBlock : 1];          // NZ: the block's rows' noise seeds
+  __shared__ LogTable s_log;                           // NZ: the noise's log table
   extern __shared__ uint4 s_e[];  // [kBlock][ES]
 
   int tid = threadIdx.x;  // (PERS: made opaque at every position, see below)
@@ -1979,11 +1985,15 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
   const uint64_t deadline = now_ticks() + p.wait_ticks;  // (PERS: the token waits)
   TRACE_STAMP(c, step, 0);
 
+  // NZ: the log table into LDS (as scalars: a struct copy lands on the stack)
+  double t_c = 0.0, t_nlc = 0.0;
+  if (NZ && tid < kLogTable) t_c = g_log_tab[tid].c, t_nlc = g_log_tab[tid].nlc;
   // The head of this wave's group, in flight while the rows are set up.
   uint4 h[kSlots];
 #pragma unroll
   for (int s = 0; s < kSlots; ++s) h[s] = load_head_tile_clamped<R>(p.head, g < NG ? g : NG - 1, s, lane, V);
   if (tid == 0) s_parity = ld_agent32(header);
+  if (NZ && tid < kLogTable) s_log.e[tid].c = t_c, s_log.e[tid].nlc = t_nlc;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -2005,7 +2015,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
 
   struct In {
     uint32_t bw[IPL];
-    float nz[IPL];
+    float nz[IPL];  // (unused with NZ)
   };
   // Batch inputs of rows b0 .. b0 + 7 of the current block (row rr of the
   // batch in this lane).  Every lane loads, so that no branch skips the
@@ -2045,7 +2055,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
           in.bw[0] = t.x, in.bw[1] = t.y;
         }
       }
-      if (MODE == 0) {
+      if (MODE == 0 && !NZ) {
         const bool nok = lok && s_T[bl] > 0.0f;
         const float4* grow =
             reinterpret_cast<const float4*>(p.gumbel + (nok ? ((size_t)b * p.N + step) * (size_t)V + v0 : 0));
@@ -2137,6 +2147,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
       s_active[tid] = active;
       s_T[tid] = T;
       s_rT[tid] = T > 0.0f ? 1.0 / (double)T : 0.0;
+      if constexpr (NZ) s_seed[tid] = p.seeds[b];
     }
     if (lane == 0)
       for (int k = 0; k < kBlock; ++k) s_key[wave][k] = kNoCandidate;
@@ -2237,7 +2248,18 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
 #pragma unroll
           for (int e = 0; e < IPL; ++e) z[e] = div_by_recip(z[e], rT);
         }
-        if (MODE == 0) {
+        if constexpr (MODE == 0 && NZ) {
+          if (ok) {
+            const uint64_t pk = noise_prefix(s_seed[bl], rb + bl, step);
+#pragma unroll
+            for (int e = 0; e < IPL; e += 4) {
+              float g4[4];
+              gumbel_noise<4>(pk, v0 + e, s_log, g4);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) z[e + k] = __fadd_rn(z[e + k], g4[k]);
+            }
+          }
+        } else if (MODE == 0) {
 #pragma unroll
           for (int e = 0; e < IPL; ++e) z[e] = __fadd_rn(z[e], cur.nz[e]);
         }
@@ -2525,12 +2547,18 @@ __host__ size_t step_half_bytes_host(int rows, int rank, int mode, int NC) {
   return step_half_bytes(rows, rank, mode, NC);
 }
 
+template <bool FL, bool NZ>
+const void* step_kernel_nz(int rank, bool pers) {
+  if (pers)
+    return rank == 256 ? (const void*)step_kernel<256, FL, 0, true, NZ> : (const void*)step_kernel<512, FL, 0, true, NZ>;
+  return rank == 256 ? (const void*)step_kernel<256, FL, 0, false, NZ> : (const void*)step_kernel<512, FL, 0, false, NZ>;
+}
 template <bool FL>
-const void* step_kernel_for(int rank, int mode, bool pers = false) {
+const void* step_kernel_for(int rank, int mode, bool pers = false, bool nz = false) {
   if (mode == 1)
-    return rank == 256 ? (const void*)step_kernel<256, FL, 1, false> : (const void*)step_kernel<512, FL, 1, false>;
-  if (pers) return rank == 256 ? (const void*)step_kernel<256, FL, 0, true> : (const void*)step_kernel<512, FL, 0, true>;
-  return rank == 256 ? (const void*)step_kernel<256, FL, 0, false> : (const void*)step_kernel<512, FL, 0, false>;
+    return rank == 256 ? (const void*)step_kernel<256, FL, 1, false, false>
+                       : (const void*)step_kernel<512, FL, 1, false, false>;
+  return nz ? step_kernel_nz<FL, true>(rank, pers) : step_kernel_nz<FL, false>(rank, pers);
 }
 template <bool FL>
 const void* pick_kernel_for(int rank) {
@@ -2655,8 +2683,11 @@ int prepare_kernels() {
           for (int flags = 0; flags < 4; ++flags) allow(kernel_for(rank, mode, kind, flags & 1, flags & 2), rank);
     for (int rank : {256, 512})
       for (int fl = 0; fl < 2; ++fl)
-        for (int k = 0; k < 3; ++k)
-          allow(fl ? step_kernel_for<true>(rank, k == 1, k == 2) : step_kernel_for<false>(rank, k == 1, k == 2), rank);
+        for (int k = 0; k < 5; ++k) {  // mode 0 per position, mode 1, mode 0 persistent; both with inline noise
+          const int mode = k == 1;
+          const bool pers = k == 2 || k == 4, nz = k >= 3;
+          allow(fl ? step_kernel_for<true>(rank, mode, pers, nz) : step_kernel_for<false>(rank, mode, pers, nz), rank);
+        }
   });
   if (err != hipSuccess) return fail(MARKOV_E_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(err));
   return MARKOV_OK;
@@ -2813,11 +2844,12 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
   }
   const size_t besz = base_f32 ? 4 : 2;
   // Batches beyond one persistent launch run per position over all rows: a
-  // step kernel (mode 0, the noise in memory), or a step kernel and a pick
-  // kernel (mode 1); also any batch, when the knob asks for that path.
+  // step kernel (mode 0, the noise read from memory or drawn inline), or a
+  // step kernel and a pick kernel (mode 1); also any batch, when the knob
+  // asks for that path.
   const int path = g_batch_path.load();
-  const bool use_step = (mode == MARKOV_MODE_INVCDF || !noise_inline) &&
-                        (path >= 2 || (path == 0 && rows > kLaunchRows));
+  const bool use_step = path >= 2 || (path == 0 && rows > kLaunchRows);
+  const bool step_nz = mode == MARKOV_MODE_GUMBEL && noise_inline;
   if (use_step) {
     // Mode 0: one persistent step kernel for all positions when its grid
     // (one workgroup per chunk) fits on the compute units at once and the
@@ -2829,7 +2861,8 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
       if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
       if (e == hipSuccess)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, (base_f32 || cache_f32) ? step_kernel_for<true>(rank, 0, true) : step_kernel_for<false>(rank, 0, true),
+            &per_cu,
+            (base_f32 || cache_f32) ? step_kernel_for<true>(rank, 0, true, step_nz) : step_kernel_for<false>(rank, 0, true, step_nz),
             kThreads, (size_t)kLaunchRows * (rank / 8 + 1) * 16);
       if (e != hipSuccess) return fail(MARKOV_E_HIP, "step kernel occupancy query: %s", hipGetErrorString(e));
       const size_t avail = no_alloc ? (kScratchBytes - kHeader) / 2 : ((workspace_bytes - kHeader) / 2) & ~(size_t)255;
@@ -2887,7 +2920,8 @@ int chain_sample(const void* base_logits, int64_t base_row_stride, int64_t base_
     p.wait_ticks = pers ? g_wait_ticks.load() : 0;  // (only the persistent variant waits)
     p.nres = 0;
     const bool fl = base_f32 || cache_f32;
-    const void* kern = fl ? step_kernel_for<true>(rank, mode, pers) : step_kernel_for<false>(rank, mode, pers);
+    const void* kern =
+        fl ? step_kernel_for<true>(rank, mode, pers, step_nz) : step_kernel_for<false>(rank, mode, pers, step_nz);
     const void* pick = fl ? pick_kernel_for<true>(rank) : pick_kernel_for<false>(rank);
     const size_t shmem = (size_t)kLaunchRows * (rank / 8 + 1) * 16;
     if (pers) {

@@ -164,8 +164,7 @@ def main() -> int:
     w = synth.workload(args.workload)
     inline = args.noise == "inline" and w.mode == 0
     d = DeviceChain(w, device=dev, noise_inline=inline)
-    step_path = (w.mode == 1 or not inline) and (args.batch_path in ("step", "persistent-step")
-                                                  or (args.batch_path == "auto" and w.rows > 64))
+    step_path = args.batch_path in ("step", "persistent-step") or (args.batch_path == "auto" and w.rows > 64)
     G = binding.markov_grid(w.rows, w.N, w.V, w.r, w.mode)
     if step_path:  # one workgroup per chunk
         G = -(-w.V // (8 * (16384 // w.r)))

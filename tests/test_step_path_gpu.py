@@ -123,6 +123,40 @@ def test_step_path_fp32_types(base_f32, cache_f32, mode):
     check_exact(w, [0, 1, 2, 64, 95])
 
 
+@pytest.mark.parametrize("V,r,rows,N", [
+    (4096 + 16, 256, 200, 3),   # ragged vocabulary, four row blocks
+    (2048 + 32, 512, 130, 4),   # r = 512
+])
+def test_step_path_inline_noise(V, r, rows, N):
+    """Mode 0 with the noise drawn inside the step kernels (the persistent
+    one, the per-position one, and the default path beyond 64 rows): the
+    noise fill kernel's function, so the outputs equal those of the same
+    path with the device's noise in memory bit for bit; sampled rows equal
+    the oracle drawing its own noise."""
+    rng = np.random.default_rng(V + rows + 1)
+    sidx = rng.permutation(rows + 5)[:rows].astype(np.int64)
+    sidx[[2, rows // 3, rows - 1]] = -1
+    temps = np.array([1.0, 0.7, 0.0, 1.5, 0.6], dtype=np.float32)[np.arange(rows) % 5]
+    w = synth.make(f"step_nz_V{V}_r{r}", V, r, rows, N, seed=V + r + rows + 1, weights="int", base_std=2.0,
+                   temperature=temps, state_idx=sidx)
+    d = DeviceChain(w)
+    d.noise()  # the device's noise fill kernel
+    (ts, cs), _ = run_path(w, None, 2, d)
+    for path in (2, 3, 0):
+        (t, c), _ = run_path(w, None, path, DeviceChain(w, noise_inline=True))
+        assert np.array_equal(t, ts), f"path {path}: inline-noise tokens differ from the noise in memory"
+        assert np.array_equal(c, cs), f"path {path}: inline-noise cache differs from the noise in memory"
+    rows_chk = [b for b in (0, 1, 3, 63, 64, 65, rows // 2, rows - 2) if b < rows]
+    g = noise_for(w)
+    ref_t, ref_c = oracle_rows(w, g, rows_chk, cs)
+    for b in rows_chk:
+        if sidx[b] < 0:
+            assert np.all(ts[b] == -7), f"padding row {b} written"
+            continue
+        assert np.array_equal(ts[b], ref_t[b]), f"row {b}: tokens differ from the oracle"
+        assert np.array_equal(cs[sidx[b]], ref_c[sidx[b]]), f"row {b}: cache differs from the oracle"
+
+
 def test_persistent_step_kernel_many_positions():
     """72 positions of 130 rows (three row blocks, the last of two rows):
     the persistent step kernel keeps an arrival counter per position, more
