@@ -11,7 +11,10 @@ on integer-valued weights, within the derived tolerances on random ones).
 Covered, in both modes: padding rows, permuted state indices, greedy rows,
 the output transform, fp32 base logits and cache, r = 512, ragged
 vocabularies, the largest row count, repeated calls on one workspace shared
-with persistent calls, and the DeepSeek-sized 256-row batch.
+with persistent calls, and the DeepSeek-sized 256-row batch; in mode 0 also
+the noise drawn inside the step kernels (bit-identical to the noise in
+memory), and more positions than the persistent step kernel's first
+layout held.
 """
 
 import dataclasses
@@ -155,6 +158,27 @@ def test_step_path_inline_noise(V, r, rows, N):
             continue
         assert np.array_equal(ts[b], ref_t[b]), f"row {b}: tokens differ from the oracle"
         assert np.array_equal(cs[sidx[b]], ref_c[sidx[b]]), f"row {b}: cache differs from the oracle"
+
+
+@pytest.mark.parametrize("base_f32,cache_f32", [(True, False), (False, True), (True, True)])
+def test_step_path_inline_noise_fp32_types(base_f32, cache_f32):
+    """The inline-noise step kernels with fp32 base logits and/or an fp32
+    cache equal the same paths with the device's noise in memory, and
+    sampled rows equal the oracle."""
+    rows = 96
+    w = synth.make(f"step_nz_fl_{int(base_f32)}{int(cache_f32)}", 3000 - 8, 256, rows, 3, seed=191,
+                   weights="int", base_std=2.0, temperature=np.array([1.0, 0.0, 1.3] * 32, dtype=np.float32),
+                   mult=0.5, base_f32=base_f32, cache_f32=cache_f32)
+    d = DeviceChain(w)
+    d.noise()
+    (ts, cs), _ = run_path(w, None, 2, d)
+    for path in (2, 3):
+        (t, c), _ = run_path(w, None, path, DeviceChain(w, noise_inline=True))
+        assert np.array_equal(t, ts) and np.array_equal(c, cs), f"path {path}"
+    sample = [0, 1, 2, 64, 95]
+    ref_t, ref_c = oracle_rows(w, noise_for(w), sample, cs)
+    for b in sample:
+        assert np.array_equal(ts[b], ref_t[b]) and np.array_equal(cs[b], ref_c[b]), b
 
 
 def test_persistent_step_kernel_many_positions():

@@ -60,7 +60,7 @@ def same(a, b):
     return np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("pair", ["mode0", "inline_one_row", "invcdf", "step_paths"])
+@pytest.mark.parametrize("pair", ["mode0", "inline_one_row", "invcdf", "step_paths", "step_inline"])
 def test_noalloc_matches_the_workspace_entry_point_twice(pair):
     """Two calls in a row, the second on a smaller input; each equals the
     workspace entry point's result, and the oracle's on integer weights."""
@@ -81,7 +81,7 @@ def test_noalloc_matches_the_workspace_entry_point_twice(pair):
         small = synth.make("na_small2", 2048, 256, 3, 2, seed=65, weights="int", base_std=2.0,
                            temperature=1.0, mode=1)
         inline = False
-    else:
+    elif pair == "step_paths":
         # more than 64 rows: the per-position kernels (a step kernel in mode
         # 0; a step and a pick kernel in mode 1), then a smaller such call
         big = synth.make("na_step0", 8192, 256, 100, 3, seed=66, weights="int", base_std=2.0,
@@ -89,6 +89,13 @@ def test_noalloc_matches_the_workspace_entry_point_twice(pair):
         small = synth.make("na_step1", 4096, 256, 70, 3, seed=67, weights="int", base_std=2.0,
                            temperature=np.array([1.0, 0.0, 0.6, 1.3, 2.0] * 14, dtype=np.float32), mode=1)
         inline = False
+    else:
+        # more than 64 rows with the noise drawn inside the step kernel
+        big = synth.make("na_stepnz0", 8192, 256, 100, 3, seed=68, weights="int", base_std=2.0,
+                         temperature=np.array([1.0, 0.0, 0.7, 1.5] * 25, dtype=np.float32))
+        small = synth.make("na_stepnz1", 4096, 256, 70, 2, seed=69, weights="int", base_std=2.0,
+                           temperature=np.array([1.0, 0.0, 0.6, 1.3, 2.0] * 14, dtype=np.float32))
+        inline = True
     for w in (big, small):
         ref, got = both(w, inline)
         assert same(ref, got), w.name
