@@ -1338,6 +1338,11 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         TRACE_STAMP(wg, i, 2);
         if (ahead && i + 1 < N) prefetch(i + 1);
       }
+      // The last step, mode 0, at most kWaves rows: only workgroup 0 needs
+      // the winners (it writes the tokens); it polls every slot itself and
+      // the others are done.
+      const bool last0 = MODE == 0 && i + 1 == N && (SMALL || rows <= kWaves);
+      if (last0 && wg != 0) break;
 
       // ---- grid-wide exchange.
       if (MODE == 0) {
@@ -1454,7 +1459,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // row 41.5 -> 40.0 us, r = 512 streamed with 8 rows 756 -> 741 us;
         // resident 8 rows 54.0 -> 57.6 us, so the resident kernels of 2 to 8
         // rows keep the all-to-all and do not compile this path.)
-        const int NR = (RES ? ONE : rows <= kWaves) ? reducers_for(G) : 1;
+        const int NR = !last0 && (RES ? ONE : rows <= kWaves) ? reducers_for(G) : 1;
         if (!many && NR > 1 && wg < NR) {
           for (int b = wave; b < rows; b += kWaves) {
             if (!s_active[b]) continue;
