@@ -76,8 +76,12 @@ def summarize(stamps: list, G: int, N: int, mode: int) -> dict:
             pub_phase = 2 if mode == 0 else 1
             last_pub = t[:, i, pub_phase].max()
             rows["pub"][i].append((last_pub - start) * TICK_US)
-            rows["win_med"][i].append(np.median(t[:, i, 4] - last_pub) * TICK_US)
-            rows["win_max"][i].append((t[:, i, 4].max() - last_pub) * TICK_US)
+            # (at mode 0's last step with at most 8 rows only workgroup 0
+            # waits for the winners: the workgroups that stamped)
+            win = t[:, i, 4]
+            win = win[win > 0] if np.any(win > 0) else win
+            rows["win_med"][i].append(np.median(win - last_pub) * TICK_US)
+            rows["win_max"][i].append((win.max() - last_pub) * TICK_US)
             nxt = t[:, i + 1, 0].min() if i + 1 < N else t[:, i, 5].max()
             rows["step"][i].append((nxt - start) * TICK_US)
     med = statistics.median
