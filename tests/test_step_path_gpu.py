@@ -185,11 +185,32 @@ def test_persistent_step_kernel_many_positions():
     """72 positions of 130 rows (three row blocks, the last of two rows):
     the persistent step kernel keeps an arrival counter per position, more
     than fit in the 256 bytes before its best keys; all paths agree and
-    sampled rows equal the oracle."""
+    sampled rows equal the oracle; drawing the noise inline gives the same
+    outputs."""
     rows = 130
     w = synth.make("step_many_positions", 4096 + 16, 256, rows, 72, seed=101, weights="int", base_std=2.0,
                    temperature=np.array([1.0, 0.0, 0.7, 1.5, 0.6] * 26, dtype=np.float32))
     check_exact(w, [0, 64, 128, 129])
+    d = DeviceChain(w)
+    d.noise()
+    (ts, cs), _ = run_path(w, None, 3, d)
+    (t, c), _ = run_path(w, None, 3, DeviceChain(w, noise_inline=True))
+    assert np.array_equal(t, ts) and np.array_equal(c, cs)
+
+
+def test_step_path_inline_noise_soft_cap():
+    """Random weights with the output transform (multiplier 0.5, soft cap
+    30): the inline-noise step kernels equal the same paths with the
+    device's noise in memory bit for bit."""
+    rows = 80
+    w = synth.make("step_nz_cap", 8192, 256, rows, 3, seed=196, peaks=8,
+                   temperature=np.array([1.0, 0.0, 0.6, 1.5] * 20, dtype=np.float32), mult=0.5, cap=30.0)
+    d = DeviceChain(w)
+    d.noise()
+    (ts, cs), _ = run_path(w, None, 2, d)
+    for path in (2, 3):
+        (t, c), _ = run_path(w, None, path, DeviceChain(w, noise_inline=True))
+        assert np.array_equal(t, ts) and np.array_equal(c, cs), f"path {path}"
 
 
 @pytest.mark.parametrize("mode", [0, 1])
