@@ -3116,6 +3116,104 @@ int markov_set_grid(int g) { return g_grid_override.exchange(g < 0 ? 0 : g); }
 int markov_set_batch_path(int path) { return g_batch_path.exchange(path < 0 || path > 3 ? 0 : path); }
 
 #ifdef MARKOV_TRACE
+// Trace builds only: the exchange's floor.  `rounds` rounds of the one-row
+// mode-0 exchange with no other work, on G workgroups of kThreads threads
+// (one per CU): thread 0 of every workgroup publishes a nonzero key into its
+// slot of the round; then either two levels as the chain kernel's one-row
+// exchange (reducer workgroup r < reducers_for(G) has wave 0's lane l poll
+// slot 64 r + l and writes the maximum into kPartCopies copies, kPartStride
+// words apart; wave 0 of every workgroup polls the partials of copy
+// wg % kPartCopies), or all-to-all (wave 0 of every workgroup polls all G
+// slots, 4 per lane).  A workgroup starts the next round once it knows the
+// maximum.  stamps[round][wg] = {publication, maximum known}, ticks of the
+// 100 MHz clock; every wait gives up after wait_ticks.
+__global__ __launch_bounds__(kThreads, 1) void exchange_probe_kernel(uint64_t* slots, uint64_t* part,
+                                                                     uint64_t* stamps, int G, int rounds,
+                                                                     int two_level, uint64_t wait_ticks) {
+  const int wg = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t deadline = now_ticks() + wait_ticks;
+  const int NR = reducers_for(G);
+  for (int r = 0; r < rounds; ++r) {
+    uint64_t* sl = slots + (size_t)r * G;
+    uint64_t* pr = part + (size_t)r * kPartCopies * kPartStride;
+    if (tid == 0) {
+      const uint64_t h = splitmix64(((uint64_t)r << 32) | (uint32_t)wg);
+      const uint64_t key = ((h >> 32) | 1ull) << 32 | (0xFFFFFFFFu - (uint32_t)wg);
+      stamps[((size_t)r * G + wg) * 2] = now_ticks();
+      st_agent(sl + wg, key);
+    }
+    if (wave == 0) {
+      if (two_level && wg < NR) {
+        const int idx = wg * 64 + lane;
+        uint64_t x = idx < G ? 0 : kNoCandidate;
+        for (;;) {
+          if (x == 0) x = ld_agent(sl + idx);
+          if (__all(x != 0) || now_ticks() > deadline) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        const uint64_t K = wave_max_u64(x == 0 ? kNoCandidate : x);
+        if (lane < kPartCopies) st_agent(pr + lane * kPartStride + wg, K);
+      }
+      const uint64_t* src = two_level ? pr + (wg % kPartCopies) * kPartStride : sl;
+      const int n = two_level ? NR : G;
+      uint64_t xs[4] = {0, 0, 0, 0};
+      for (;;) {
+        bool all = true;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int idx = lane + 64 * k;
+          if (idx >= n) xs[k] = kNoCandidate;
+          else if (xs[k] == 0) xs[k] = ld_agent(src + idx);
+          all = all && xs[k] != 0;
+        }
+        if (__all(all) || now_ticks() > deadline) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      uint64_t m = kNoCandidate;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) m = umax64(m, xs[k]);
+      m = wave_max_u64(m);
+      if (lane == 0) stamps[((size_t)r * G + wg) * 2 + 1] = m ? now_ticks() : 0;
+    }
+    __syncthreads();
+  }
+}
+
+// Runs the probe above (G <= the device's CUs, rounds <= 4096) and copies
+// the stamps, [rounds][G][2] u64, to host memory.  Synchronising.
+int markov_trace_exchange_probe(int G, int rounds, int two_level, uint64_t* stamps_host) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return fail(MARKOV_E_HIP, "exchange probe: %s", hipGetErrorString(e));
+  if (G < 1 || G > cus || G > 64 * 4 || rounds < 1 || rounds > 4096 || !stamps_host)
+    return fail(MARKOV_E_UNSUPPORTED, "exchange probe: G=%d (at most %d and 256), rounds=%d", G, cus, rounds);
+  const size_t sb = (size_t)rounds * G * 8, pb = (size_t)rounds * kPartCopies * kPartStride * 8,
+               tb = (size_t)rounds * G * 16;
+  void *slots = nullptr, *part = nullptr, *stamps = nullptr;
+  e = hipMalloc(&slots, sb);
+  if (e == hipSuccess) e = hipMalloc(&part, pb);
+  if (e == hipSuccess) e = hipMalloc(&stamps, tb);
+  if (e == hipSuccess) e = hipMemset(slots, 0, sb);
+  if (e == hipSuccess) e = hipMemset(part, 0, pb);
+  if (e == hipSuccess) e = hipMemset(stamps, 0, tb);
+  if (e == hipSuccess) {
+    uint64_t* a0 = (uint64_t*)slots;
+    uint64_t* a1 = (uint64_t*)part;
+    uint64_t* a2 = (uint64_t*)stamps;
+    uint64_t wt = g_wait_ticks.load();
+    void* args[] = {&a0, &a1, &a2, &G, &rounds, &two_level, &wt};
+    e = hipLaunchKernel((const void*)exchange_probe_kernel, dim3(G), dim3(kThreads), args, 0, nullptr);
+  }
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(stamps_host, stamps, tb, hipMemcpyDeviceToHost);
+  hipFree(slots);
+  hipFree(part);
+  hipFree(stamps);
+  if (e != hipSuccess) return fail(MARKOV_E_HIP, "exchange probe: %s", hipGetErrorString(e));
+  return MARKOV_OK;
+}
+
 // Trace builds only (not part of the ABI in markov.h): copies the first
 // `bytes` of trace_buf ([1024 workgroups][32 steps][12 phases] u64 ticks of
 // the 100 MHz clock) to host memory and clears it.  Synchronising.

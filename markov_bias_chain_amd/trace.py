@@ -17,6 +17,13 @@ per step, medians over the calls of
     publication (median and slowest workgroup);
   * step: from the step's first start to the next step's first start.
 
+With --exchange-probe it measures the exchange's floor instead: the tracing
+build's probe kernel runs rounds of the one-row exchange with no other work
+on one workgroup per CU (two levels through the reducers and the partials'
+copies, as the chain kernel does, or all-to-all) and this tool prints, over
+the rounds, the spread of the publications and when each workgroup knows
+the maximum after the last publication (median and slowest workgroup).
+
 It is a measuring tool: nothing of the chain's arithmetic is here.
 """
 
@@ -47,7 +54,47 @@ def load_trace_library():
     lib = binding.load()
     lib.markov_trace_read.restype = ctypes.c_int
     lib.markov_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.markov_trace_exchange_probe.restype = ctypes.c_int
+    lib.markov_trace_exchange_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     return binding, lib
+
+
+def summarize_probe(st: np.ndarray, skip: int = 10) -> dict:
+    """Exchange probe stamps [rounds, G, 2] (publication, maximum known;
+    ticks): medians over rounds (after the first `skip`) of the publication
+    spread, the median and the slowest workgroup's time from the last
+    publication to knowing the maximum, and the round period (us)."""
+    st = st.astype(np.int64)[skip:]
+    pub, known = st[:, :, 0], st[:, :, 1]
+    last_pub = pub.max(axis=1)
+    after = (known - last_pub[:, None]) * TICK_US
+    med = statistics.median
+    return {
+        "rounds": st.shape[0],
+        "spread": med(((pub.max(axis=1) - pub.min(axis=1)) * TICK_US).tolist()),
+        "known_med": med(np.median(after, axis=1).tolist()),
+        "known_last": med(after.max(axis=1).tolist()),
+        "period": med((np.diff(pub.min(axis=1)) * TICK_US).tolist()),
+    }
+
+
+def exchange_probe(lib, G: int, rounds: int) -> str:
+    out = [f"## Exchange floor probe: {G} workgroups of 512 threads, {rounds} rounds, medians over "
+           f"rounds {10}..{rounds - 1} (us)\n",
+           "| exchange | publication spread | maximum known after the last publication: median WG "
+           "| slowest WG | round period |",
+           "|---|---|---|---|---|"]
+    for two_level, name in ((1, "two levels (reducers, 16 copies of the partials)"), (0, "all-to-all")):
+        st = np.zeros((rounds, G, 2), dtype=np.uint64)
+        rc = lib.markov_trace_exchange_probe(G, rounds, two_level, st.ctypes.data)
+        if rc != 0:
+            raise RuntimeError("markov_trace_exchange_probe failed")
+        if not np.all(st[:, :, 1] > 0):
+            raise RuntimeError("exchange probe: a wait gave up")
+        r = summarize_probe(st)
+        out.append(f"| {name} | {r['spread']:.2f} | {r['known_med']:.2f} | {r['known_last']:.2f} | "
+                   f"{r['period']:.2f} |")
+    return "\n".join(out)
 
 
 def read(lib, G: int, N: int) -> np.ndarray:
@@ -155,11 +202,18 @@ def main() -> int:
     ap.add_argument("--cold", action="store_true", help="read 1 GiB before each call (evicts L2s and MALL)")
     ap.add_argument("--batch-path", choices=("auto", "persistent", "step", "persistent-step"), default="auto")
     ap.add_argument("--dump", help="also save the raw stamps [calls, workgroups, steps, phases] (ticks) to this .npy")
+    ap.add_argument("--exchange-probe", action="store_true", help="measure the exchange's floor (see above)")
+    ap.add_argument("--grid", type=int, default=253, help="exchange probe: workgroups")
+    ap.add_argument("--rounds", type=int, default=200, help="exchange probe: rounds")
     args = ap.parse_args()
 
     import torch
 
     binding, lib = load_trace_library()
+    if args.exchange_probe:
+        torch.zeros(1, device="cuda:0")  # the device, initialised
+        print(exchange_probe(lib, args.grid, args.rounds))
+        return 0
     from markov_bias_chain_amd import synth
     from markov_bias_chain_amd.device import DeviceChain
 
