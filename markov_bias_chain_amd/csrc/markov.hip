@@ -29,8 +29,9 @@
 //    step.
 //  * The bias GEMV: up to 16 request rows per v_mfma_f32_16x16x32_bf16 pass
 //    (head tiles as A, the rows' embeddings from LDS as B), results through
-//    a per-wave LDS tile; a single request row uses v_dot2c_f32_bf16 and a
-//    permlane reduce-scatter so that each lane ends with its vocab id's sum.
+//    a per-wave LDS tile; a single request row swaps the operands (its
+//    embedding as A, the head tile as B), so that every lane ends with its
+//    vocab id's sum in a register.
 //  * The epilogue (bias -> bf16, + base logit, output transform, bf16 cache
 //    store, score, per-row best key) handles batches of 8 request rows with
 //    8 lanes per row and 8 (r = 256) or 4 (r = 512) consecutive ids per
@@ -644,57 +645,42 @@ __device__ __forceinline__ void group_bias(const uint4 (&h)[kSlots], const uint4
   }
 }
 
-// One request row: the same products on the vector ALU with v_dot2c_f32_bf16
-// (two bf16 products added to an fp32 accumulator), so that the bias of
-// group row lr ends in lane lr without a trip through LDS.  Lane l holds
-// partial sums over k in {32 kt + 8 (l >> 4) .. + 7} for rows 16 t + (l & 15);
-// a reduce-scatter across the four 16-lane quarters (v_permlane32_swap and
-// v_permlane16_swap) adds the quarters and leaves row 16 q + (l & 15) in the
-// lanes of quarter q.  e_row is the request row's embedding in LDS.
+// One request row on MFMA with the roles of group_bias swapped: the
+// embedding is the A operand, the same in all 16 rows of the tile (lane l
+// supplies k = 32 kt + 8 (l >> 4) .. + 7, as a B operand would), and the head
+// tile is the B operand (lane l holds head row 16 t + (l & 15) at those k,
+// which is also the B layout).  Every row of the 16 x 16 result is then the
+// bias of the tile's 16 head rows, so lane l finds the bias of head row
+// 16 t + (l & 15) in element 0 of tile t's accumulator and keeps tile
+// t = l >> 4 (r = 256: four tiles, lane l gets group row l) or t = (l >> 4) & 1
+// (r = 512: two tiles, lanes 0..31 get group rows 0..31).  No reduction
+// across lanes is needed.  (Against v_dot2c_f32_bf16 with a reduce-scatter
+// across the quarters: 40.5 -> 40.0 us per DeepSeek-sized one-row call with
+// inline noise, 38.9 -> 38.3 us with the noise read; splitting the tiles
+// between MFMA and dot2 was slower than either.)  e_row is the request row's
+// embedding in LDS.
 template <int R>
 __device__ __forceinline__ float one_row_bias(const uint4 (&h)[kSlots], const uint4* __restrict__ e_row,
                                               int lane) {
   constexpr int KT = R / 32, MT = kSlots / KT;
+  static_assert(MT == 2 || MT == 4, "r = 256 or 512");
   const int q = lane >> 4;
-  float acc[MT][2];
+  f32x4_t acc[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t][0] = acc[t][1] = 0.0f;
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
-    const uint4 e = e_row[4 * kt + q];
+    const bf16x8_t ev = __builtin_bit_cast(bf16x8_t, e_row[4 * kt + q]);
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const uint4 hv = h[t * KT + kt];
-      float a = acc[t][kt & 1];
-      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.x), __builtin_bit_cast(bf16x2_t, e.x), a, false);
-      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.y), __builtin_bit_cast(bf16x2_t, e.y), a, false);
-      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.z), __builtin_bit_cast(bf16x2_t, e.z), a, false);
-      a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, hv.w), __builtin_bit_cast(bf16x2_t, e.w), a, false);
-      acc[t][kt & 1] = a;
-    }
+    for (int t = 0; t < MT; ++t)
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ev, __builtin_bit_cast(bf16x8_t, h[t * KT + kt]), acc[t],
+                                                        0, 0, 0);
   }
-  // permlane32_swap(a, b) gives lanes 0..31 (a[l], a[l + 32]) and lanes
-  // 32..63 (b[l - 32], b[l]); permlane16_swap pairs quarters 0/1 and 2/3 the
-  // same way.
-  if constexpr (MT == 4) {
-    const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0][0] + acc[0][1]),
-                                                     __float_as_uint(acc[2][0] + acc[2][1]), false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[1][0] + acc[1][1]),
-                                                     __float_as_uint(acc[3][0] + acc[3][1]), false, false);
-    // lanes 0..31 now hold rows t = 0, 1 (k0, k1), lanes 32..63 rows t = 2, 3
-    const float k0 = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
-    const float k1 = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
-    const auto s2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
-    return __uint_as_float(s2[0]) + __uint_as_float(s2[1]);
-  } else {
-    static_assert(MT == 2, "r = 512 groups have two row tiles");
-    const auto s0 = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[0][0] + acc[0][1]),
-                                                     __float_as_uint(acc[1][0] + acc[1][1]), false, false);
-    // quarters 0 and 2 hold row tile 0, quarters 1 and 3 row tile 1
-    const float u = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(u), __float_as_uint(u), false, false);
-    return __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
-  }
+  const int tl = q & (MT - 1);
+  float b = acc[0][0];
+#pragma unroll
+  for (int t = 1; t < MT; ++t) b = tl == t ? acc[t][0] : b;
+  return b;
 }
 
 // FL: the element-type flags of mode are read (fp32 base logits or cache);

@@ -188,7 +188,7 @@ def test_one_row_exact(V, r, N, T):
 
 @pytest.mark.parametrize("V,r", [(129280, 256), (65536 + 16, 512)])
 def test_one_row_bias_tolerance(V, r):
-    """The one-row bias (dot2 accumulation) on random N(0, 0.02) weights:
+    """The one-row bias (MFMA with the embedding as A) on random N(0, 0.02) weights:
     within one bf16 ulp of the oracle's exactly summed bias except where the
     sum nearly cancels (then within the fp32 accumulation bound)."""
     w = synth.make(f"one_bias_r{r}", V, r, 1, 3, seed=41 + r, temperature=0.0)
