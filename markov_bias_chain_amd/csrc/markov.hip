@@ -618,24 +618,39 @@ template <int R>
 constexpr int emb_stride() { return R / 8 + 1; }
 
 // sb[j * bias_stride + row] = sum_k head[row][k] * embed_row(b0 + j)[k] for
-// j < nb; rows beyond nb get nothing.
-template <int R>
+// j < nb; rows beyond nb get nothing.  The embedding pieces of EB k tiles are
+// read from LDS together, before their products, and the scheduler may not
+// sink those reads between the products: KT / EB LDS round trips per pass.
+// Left to itself the compiler waited for each k tile's read just before its
+// products.  EB = 2 costs no registers in any kernel here; larger EB costs
+// 4 (EB - 1) VGPRs beyond one, and spills in kernels that hold the head and
+// two batches of inputs, so each caller picks the largest EB its registers
+// allow.
+template <int R, int EB>
 __device__ __forceinline__ void group_bias(const uint4 (&h)[kSlots], const uint4* __restrict__ s_e,
                                            int b0, int nb, int lane, float* __restrict__ sb) {
   constexpr int KT = R / 32, MT = kSlots / KT, ES = emb_stride<R>();
+  static_assert(KT % EB == 0, "EB divides the k tiles");
   const int j = lane & 15;
   const bool jv = j < nb;
   f32x4_t acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    const uint4 e = jv ? s_e[(b0 + j) * ES + 4 * kt + (lane >> 4)] : make_uint4(0, 0, 0, 0);
-    const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, e);
+  for (int k0 = 0; k0 < KT; k0 += EB) {
+    uint4 ea[EB];
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, h[t * KT + kt]), bv,
-                                                        acc[t], 0, 0, 0);
+    for (int k = 0; k < EB; ++k)
+      ea[k] = jv ? s_e[(b0 + j) * ES + 4 * (k0 + k) + (lane >> 4)] : make_uint4(0, 0, 0, 0);
+    if constexpr (EB > 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < EB; ++k) {
+      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, ea[k]);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, h[t * KT + k0 + k]), bv,
+                                                          acc[t], 0, 0, 0);
+    }
   }
   if (jv) {
 #pragma unroll
@@ -668,9 +683,17 @@ __device__ __forceinline__ float one_row_bias(const uint4 (&h)[kSlots], const ui
   f32x4_t acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // All of the lane's embedding pieces are read before the first product,
+  // and the scheduler may not sink the reads between the products: one LDS
+  // round trip per call instead of one per k tile (one row: 40.3 -> 40.0 us
+  // per call with inline noise).
+  uint4 ea[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) ea[kt] = e_row[4 * kt + q];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
-    const bf16x8_t ev = __builtin_bit_cast(bf16x8_t, e_row[4 * kt + q]);
+    const bf16x8_t ev = __builtin_bit_cast(bf16x8_t, ea[kt]);
 #pragma unroll
     for (int t = 0; t < MT; ++t)
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ev, __builtin_bit_cast(bf16x8_t, h[t * KT + kt]), acc[t],
@@ -1231,7 +1254,9 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         const int b0 = t * kBatch;
         if ((t & 1) == 0) {
           const int np = rows - b0 < kRowPass ? rows - b0 : kRowPass;
-          group_bias<R>(h, s_e, b0, np, lane, sb);
+          // (8 rows: 52.0 -> 49.8 us per call with the noise read, 60.3 ->
+          // 59.3 us with inline noise; 64-row inverse CDF 226.5 -> 224.1 us)
+          group_bias<R, (MODE == 0 && RES && SMALL) ? 8 : 2>(h, s_e, b0, np, lane, sb);
           if (t == 0) park_tiles(i, j);
         }
         const int nb = rows - b0 < kBatch ? rows - b0 : kBatch;
@@ -2181,7 +2206,9 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
       const int b0 = t * kBatch;
       if ((t & 1) == 0) {
         const int np = nbr - b0 < kRowPass ? nbr - b0 : kRowPass;
-        group_bias<R>(h, s_e, b0, np, lane, sb);
+        // (256 rows: persistent step kernel 631 -> 627 us per call, inverse
+        // CDF 670 -> 656 us; EB = 4 in mode 0 was 629 us)
+        group_bias<R, MODE == 1 ? 4 : 2>(h, s_e, b0, np, lane, sb);
       }
       const In& cur = in[u];
       load_in(rb, (t + kPrefetch) * kBatch, in[(u + kPrefetch) % kSets]);
