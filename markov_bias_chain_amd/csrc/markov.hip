@@ -706,6 +706,14 @@ __device__ __forceinline__ float one_row_bias(const uint4 (&h)[kSlots], const ui
   return b;
 }
 
+// A request row's constants for one call, in registers.
+struct RowConsts {
+  bool active;
+  float T;
+  double rT;
+  int state;
+};
+
 // FL: the element-type flags of mode are read (fp32 base logits or cache);
 // without it both are bf16.  RES: every
 // workgroup owns exactly one chunk (G == NC) and keeps its head in VGPRs
@@ -1020,17 +1028,34 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     stage_park();
   }
 
+  // A row's constants for the call (written once in the prologue).  With
+  // at most kAhead rows (one batch) they are read before the bias pass, so
+  // that these LDS reads overlap the pass's embedding reads instead of
+  // waiting one after another in the epilogue, and the compiler keeps them
+  // in registers; larger batches read them in the epilogue (in registers
+  // across the pass they cost those kernels spills).
+  auto row_consts = [&](int b) {
+    RowConsts c;
+    c.active = s_active[b] != 0;
+    c.T = s_T[b];
+    c.rT = s_rT[b];
+    c.state = s_state[b];
+    return c;
+  };
+
   // Epilogue of the batch of rows b0 .. b0 + nb - 1 in the layout above:
   // per vocab id, bias -> bf16, + base logit, output transform, bf16 cache
   // store (one vector per lane), score; then per row the best (score, id)
   // key of the wave's group and, in mode 1, the group's sum of exp(z - max).
-  // sbt is the wave's bias tile row block of the batch (row rr at rr * BS).
-  auto epilogue_rows = [&](int i, int b0, int nb, int g, const float* sbt, const LaneIn& in, bool nz_ready) {
+  // sbt is the wave's bias tile row block of the batch (row rr at rr * BS);
+  // with SMALL, rc0 holds the lane's row's constants (row_consts(b0 + rr)).
+  auto epilogue_rows = [&](int i, int b0, int nb, int g, const float* sbt, const LaneIn& in, bool nz_ready,
+                           const RowConsts& rc0) {
     const int b = b0 + rr;
     const int v0 = g * RPG + q * IPL;
-    const bool ok = rr < nb && g < NG && v0 < V && s_active[b];
-    const float T = s_T[b];
-    const double rT = s_rT[b];
+    const bool ok = rr < nb && g < NG && v0 < V && (SMALL ? rc0.active : s_active[b] != 0);
+    const float T = SMALL ? rc0.T : s_T[b];
+    const double rT = SMALL ? rc0.rT : s_rT[b];
     float bsum[IPL];
 #pragma unroll
     for (int e4 = 0; e4 < IPL / 4; ++e4) {
@@ -1061,7 +1086,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     if (ok) {
       // Streaming stores: the cache is not read again by this launch (but
       // for an inverse-CDF owner's one chunk).
-      const long long at = (long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss + v0;
+      const long long at = (long long)(SMALL ? rc0.state : s_state[b]) * p.cache_rs + (long long)i * p.cache_ss + v0;
       if (cache_f32) {
         u32x4_t* crow = reinterpret_cast<u32x4_t*>(reinterpret_cast<float*>(p.cache) + at);
 #pragma unroll
@@ -1128,7 +1153,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       }
       wsum = group8_sum(s);
     }
-    if (q == 0 && rr < nb && s_active[b]) {
+    if (q == 0 && rr < nb && (SMALL ? rc0.active : s_active[b] != 0)) {
       const uint64_t key = gnan != 0xFFFFFFFFu ? ((0xFFFFFFFFull << 32) | (0xFFFFFFFFu - gnan))
                            : gmax != INT_MIN ? (((uint64_t)score_ord(order_key_inv(gmax)) << 32) | (0xFFFFFFFFu - gid))
                                              : kNoCandidate;
@@ -1196,16 +1221,23 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         // maximum (or of the NaNs, which order first).
         const int v = g * RPG + lr;
         const bool own = g < NG && v < V && lane_owns;
+        // The row's constants and the noise wave 1 drew for wave 0 (both
+        // written before the barrier that ended the previous step) are read
+        // before the bias, so that their LDS round trips overlap the
+        // embedding reads instead of following one another in the epilogue.
+        const bool act = s_active[0] != 0;
+        const float T = s_T[0];
+        const auto rT = s_rT[0];
+        const int st = s_state[0];
+        if (w0_by_w1 && wave == 0 && i > 0) one_noise = s_nz0[lane];
         const float bsum = one_row_bias<R>(h, s_e, lane);
         park_tiles(i, j);
-        if (w0_by_w1 && wave == 0 && i > 0) one_noise = s_nz0[lane];
         uint32_t ord = 0;
-        if (s_active[0] && own) {
-          const float T = s_T[0];
+        if (act && own) {
           float x = __fadd_rn(__uint_as_float(one_base), bf16_round(bsum));
           x = __fmul_rn(x, p.mult);
           if (p.has_cap) x = __fmul_rn(tanhf(__fmul_rn(x, p.inv_cap)), p.cap);
-          const long long at = (long long)s_state[0] * p.cache_rs + (long long)i * p.cache_ss + v;
+          const long long at = (long long)st * p.cache_rs + (long long)i * p.cache_ss + v;
           float z;
           if (cache_f32) {
             reinterpret_cast<float*>(p.cache)[at] = x;
@@ -1216,7 +1248,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             z = bf16_to_f32(cb);
           }
           if (T > 0.0f) {
-            if (T != 1.0f) z = div_by_recip(z, s_rT[0]);  // c / 1 is exact
+            if (T != 1.0f) z = div_by_recip(z, rT);  // c / 1 is exact
             z = __fadd_rn(z, one_noise);
           }
           ord = score_ord(z);
@@ -1252,6 +1284,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       }
       for (int t = 0; t < nbat; ++t) {
         const int b0 = t * kBatch;
+        const RowConsts rc = SMALL ? row_consts(b0 + rr) : RowConsts{};
         if ((t & 1) == 0) {
           const int np = rows - b0 < kRowPass ? rows - b0 : kRowPass;
           // (8 rows: 52.0 -> 49.8 us per call with the noise read, 60.3 ->
@@ -1261,13 +1294,13 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         }
         const int nb = rows - b0 < kBatch ? rows - b0 : kBatch;
         if constexpr (ahead) {
-          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, pre, false);
+          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, pre, false, rc);
         } else if (staged) {
           stage_fetch(t, cur);
-          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur, false);
+          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur, false, rc);
         } else {
           if (t + 1 < nbat) load_rows(i, b0 + kBatch, g, nxt);
-          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur, t == 0 && nz0);
+          epilogue_rows(i, b0, nb, g, sb + (t & 1) * kBatch * BS, cur, t == 0 && nz0, rc);
           cur = nxt;
         }
       }
