@@ -82,6 +82,7 @@ constexpr int kHeader = 256;               // workspace header bytes
 constexpr int kModeFlags = MARKOV_BASE_F32 | MARKOV_CACHE_F32 | MARKOV_NOISE_INLINE;  // flag bits of `mode`
 constexpr int kMaxPollPerLane = 16;        // slots one lane polls (<= 1024 per row)
 constexpr int kLeaderRegs = 4;             // inverse-CDF chunks per lane kept in registers by a leader
+constexpr int kXCDs = 8;                   // XCDs of the device (workgroups are placed round robin)
 constexpr int kPartCopies = 16;            // <= kWaves rows: copies of each step's reducer partials
 constexpr int kPartStride = 64;            // u64 words from one copy to the next (512 bytes)
 constexpr int kDecCopies = 16;             // inverse CDF: copies of each step's decisions and tokens
@@ -510,6 +511,21 @@ struct HalfLayout {
 
 // Reducer workgroups of the two-level mode-0 exchange (slots per reducer: 64).
 __host__ __device__ inline int reducers_for(int NC) { return (NC + 63) / 64; }
+
+// The chunk held by workgroup wg of a G-workgroup launch whose workgroups
+// each hold one chunk, such that the workgroups of one XCD (launched round
+// robin, workgroup wg on XCD wg % kXCDs) hold one contiguous run of chunks:
+// XCD x gets G / kXCDs workgroups, one more for x < G % kXCDs, in order.
+// A bijection on [0, G) whatever the placement.  (Loading the 66 MB
+// DeepSeek-sized head with 253 workgroups, the last workgroup is done after
+// 9.7 us this way against 10.8-10.9 us with chunk wg: with chunk wg the odd
+// XCDs, XCDs 5 and 7 the most, take up to 2.5 us longer than the even ones.
+// Per call: one row 39.5 -> 38.1 us, 8 rows 58.9 -> 57.6 us, the r = 512
+// streamed head 574 -> 532 us, 64-row inverse CDF 224.0 -> 222.9 us.)
+__host__ __device__ inline int xcd_run_chunk(int wg, int G) {
+  const int x = wg % kXCDs, k = wg / kXCDs, q = G / kXCDs, r = G % kXCDs;
+  return x * q + (x < r ? x : r) + k;
+}
 // Whether the partials of a launch of `rows` rows are kept in copies.
 __host__ __device__ inline bool copied_parts(int rows, int NC) { return rows <= kWaves && reducers_for(NC) > 1; }
 
@@ -764,6 +780,13 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   uint32_t* header = reinterpret_cast<uint32_t*>(p.ws);
   const uint64_t deadline = now_ticks() + p.wait_ticks;
   TRACE_STAMP(wg, 0, 6);
+  // This workgroup's first chunk, in the XCD-contiguous assignment; a
+  // streamed head's workgroup takes every G-th chunk from there (chunks
+  // wc + j G).  Key slots stay indexed by workgroup, keys carry vocabulary
+  // ids and partials are indexed by chunk, so only the owner test of the
+  // inverse CDF (the workgroup that computed chunk o: o % G == wc) depends
+  // on it.
+  const int wc = xcd_run_chunk(wg, G);
   // In the epilogue lane l owns group row lr (r = 512 groups have 32 rows:
   // lanes 32..63 have none).
   const int lr = (R == 256) ? lane : (lane & 31);
@@ -798,12 +821,12 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // draw back until the whole head had arrived.)
   uint32_t b0_bits = 0;
   if constexpr (ONE && !FL) {
-    const int v = (wg * kWaves + wave) * RPG + lr;
+    const int v = (wc * kWaves + wave) * RPG + lr;
     b0_bits = reinterpret_cast<const uint16_t*>(p.base)[v < V ? v : V - 1];
   }
   uint4 h[kSlots];
   if constexpr (RES) {
-    const int g0 = wg * kWaves + wave;  // this wave's group
+    const int g0 = wc * kWaves + wave;  // this wave's group
 #pragma unroll
     for (int s = 0; s < kSlots; ++s)
       h[s] = load_head_tile_clamped<R>(p.head, g0 < NG ? g0 : NG - 1, s, lane, V);
@@ -857,8 +880,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // prefetched for the next step while the current step's exchange is in
   // flight (they do not depend on the winner).
   constexpr bool ahead = RES && SMALL;
-  const int v_res = (wg * kWaves + wave) * RPG + lr;
-  const bool own_res = (wg * kWaves + wave) < NG && v_res < V && lane_owns;
+  const int v_res = (wc * kWaves + wave) * RPG + lr;
+  const bool own_res = (wc * kWaves + wave) < NG && v_res < V && lane_owns;
   uint32_t one_base = 0;
   float one_noise = 0.0f;
   // Inline noise: waves 1 .. 7 draw the next step's noise here, while wave
@@ -889,7 +912,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     }
     if (one_nz && (wave != 0 || i == 0)) draw_one(i);
     if (w0_by_w1 && wave == 1 && i > 0 && s_active[0] && s_T[0] > 0.0f) {
-      const int g0 = wg * kWaves;  // wave 0's group
+      const int g0 = wc * kWaves;  // wave 0's group
       const int v = g0 * RPG + lr;
       if (g0 < NG && v < V && lane_owns) gumbel_noise<1>(noise_prefix(s_seed[0], p.row_base, i), v, s_log, &s_nz0[lane]);
     }
@@ -960,7 +983,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   LaneIn pre;  // the resident SMALL kernel's prefetched batch
   auto prefetch = [&](int i) {
     if constexpr (ONE) prefetch_one(i);
-    else load_rows(i, 0, wg * kWaves + wave, pre);
+    else load_rows(i, 0, wc * kWaves + wave, pre);
   };
   // Embeddings of the anchor tokens; the first pass's loads are in flight
   // during the step-0 prefetch (which may draw noise).
@@ -987,7 +1010,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   uint32_t pst[stage ? kStageBatches : 1][IPL / 2];  // bf16 pairs of every batch
   auto stage_load = [&](int i) {
     const int nbat = (rows + kBatch - 1) / kBatch;
-    const int g = wg * kWaves + wave;
+    const int g = wc * kWaves + wave;
     const int v0 = g * RPG + q * IPL;
 #pragma unroll
     for (int t = 0; t < (stage ? kStageBatches : 1); ++t) {
@@ -1186,13 +1209,13 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // (odd steps backwards), so every step after the first starts with the
   // chunk the previous step ended with, whose head tiles are still in h:
   // with k chunks per workgroup a step streams k - 1 of them.
-  const int nch = RES ? 1 : (NC - wg + G - 1) / G;  // this workgroup's chunks
+  const int nch = RES ? 1 : (NC - wc + G - 1) / G;  // this workgroup's chunks
   auto local_work = [&](int i) {
     if (lane == 0)
       for (int b = 0; b < rows; ++b) s_key[wave][b] = kNoCandidate;
     for (int jj = 0; jj < nch; ++jj) {
       const int j = (!RES && (i & 1)) ? nch - 1 - jj : jj;
-      const int c = wg + j * G;
+      const int c = wc + j * G;
       const int g = c * kWaves + wave;
       LaneIn cur, nxt;
       if constexpr (!RES) {
@@ -1775,7 +1798,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
               s_need[b] = 0;
             } else if ((unsigned)o < (unsigned)NC) {
               s_dec[b] = d;
-              s_need[b] = (o % G == wg) ? 2 : 1;
+              s_need[b] = (o % G == wc) ? 2 : 1;
             } else {
               s_tok[b] = 0;
               s_need[b] = 0;
@@ -2024,6 +2047,9 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
 
   int tid = threadIdx.x;  // (PERS: made opaque at every position, see below)
   const int lane = tid & 63, wave = tid >> 6;
+  // (Workgroup c holds chunk c: the XCD-contiguous assignment of the chain
+  // kernel made no difference to the step kernels, whose streams of base
+  // logits, noise and cache are row-major over all chunks.)
   const int c = blockIdx.x;
   const int rows = p.rows, V = p.V, NG = p.NG, G = p.G;
   uint32_t* header = reinterpret_cast<uint32_t*>(p.ws);
