@@ -340,10 +340,12 @@ def test_invcdf_draw_at_the_top_of_the_cdf(V):
 
 # -------------------------------------------------------------- invariance --
 
-@pytest.mark.parametrize("grid", [1, 7, 64])
+@pytest.mark.parametrize("grid", [1, 7, 13, 22, 33, 64])
 def test_grid_invariance(grid):
     """The outputs do not depend on the number of workgroups (resident and
-    streamed heads, every chunk-to-workgroup assignment)."""
+    streamed heads, every chunk-to-workgroup assignment: the workgroups of
+    each XCD hold a contiguous run of chunks, and grids of 13, 22 and 33
+    give the XCDs unequal runs)."""
     w = synth.make("grid", 20000, 256, 3, 4, seed=5, temperature=[0.7, 0.0, 1.3])
     g = oracle_noise(w)
     t0, c0, _ = run(w, gumbel=g)
@@ -351,7 +353,7 @@ def test_grid_invariance(grid):
     assert np.array_equal(t0, t1) and np.array_equal(c0, c1)
 
 
-@pytest.mark.parametrize("grid", [3, 64])
+@pytest.mark.parametrize("grid", [3, 10, 17, 64])
 def test_grid_invariance_invcdf_and_r512(grid):
     w = synth.make("grid1", 12288, 256, 5, 3, seed=6, temperature=[1.0, 0.0, 0.5, 2.0, 1.0], mode=1)
     t0, c0, _ = run(w)
