@@ -372,8 +372,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the chain is not sharded across GPUs here)", file=sys.stderr)
+        print(f"bench.py: the chain runs on one GPU; --gpus {args.gpus} is not supported "
+              "(it is not sharded across GPUs)", file=sys.stderr)
         return 2
 
     import torch

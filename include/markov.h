@@ -59,7 +59,7 @@ typedef enum {
  * `seeds` is required.  Without it the noise is read from `gumbel`. */
 #define MARKOV_NOISE_INLINE 0x40
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define MARKOV_MAX_ROWS 4096 /* one persistent launch takes 64; more run per position */
 #define MARKOV_MAX_STEPS 256
 #define MARKOV_MAX_VOCAB (1 << 24)

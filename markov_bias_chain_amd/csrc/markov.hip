@@ -2677,7 +2677,7 @@ int check_shape(int rows, int steps, int vocab, int rank, int mode, Shape* sh) {
     return fail(MARKOV_E_UNSUPPORTED, "vocab=%d is not a positive multiple of 16 up to %d", vocab,
                 MARKOV_MAX_VOCAB);
   if (rank != 256 && rank != 512)
-    return fail(MARKOV_E_UNSUPPORTED, "rank=%d (this build takes 256 or 512)", rank);
+    return fail(MARKOV_E_UNSUPPORTED, "rank=%d (the library is compiled for 256 or 512)", rank);
   if (mode != MARKOV_MODE_GUMBEL && mode != MARKOV_MODE_INVCDF)
     return fail(MARKOV_E_UNSUPPORTED, "mode=%d", mode);
   const int rpg = groups_per_rank(rank);
