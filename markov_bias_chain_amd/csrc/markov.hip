@@ -787,6 +787,11 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // inverse CDF (the workgroup that computed chunk o: o % G == wc) depends
   // on it.
   const int wc = xcd_run_chunk(wg, G);
+  // Batches of 2 to 8 prefetched rows: wave 0 (whose first threads publish
+  // every row's key) wins issue against its SIMD's other wave (8 rows with
+  // inline noise 60.9 -> 60.3 us per call; for one row or 64 rows the
+  // same priority was slower).
+  if (MODE == 0 && SMALL && !ONE && wave == 0) __builtin_amdgcn_s_setprio(3);
   // In the epilogue lane l owns group row lr (r = 512 groups have 32 rows:
   // lanes 32..63 have none).
   const int lr = (R == 256) ? lane : (lane & 31);
