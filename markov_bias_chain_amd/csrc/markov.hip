@@ -85,7 +85,7 @@ constexpr int kLeaderRegs = 4;             // inverse-CDF chunks per lane kept i
 constexpr int kXCDs = 8;                   // XCDs of the device (workgroups are placed round robin)
 constexpr int kPartCopies = 16;            // <= kWaves rows: copies of each step's reducer partials
 constexpr int kPartStride = 64;            // u64 words from one copy to the next (512 bytes)
-constexpr int kDecCopies = 16;             // inverse CDF: copies of each step's decisions and tokens
+constexpr int kDecCopies = 16;             // inverse CDF: copies of each step's tokens
 constexpr unsigned long long kTimeoutTicks = 200000000ull;  // 2 s at 100 MHz (the default wait limit)
 constexpr long long kTicksPerUs = 100;                       // s_memrealtime runs at 100 MHz
 
@@ -265,11 +265,11 @@ __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memr
 // every step, one thread (thread 0) per workgroup, into trace_buf
 // [workgroup][step][phase]; markov_trace_read copies it to the host.  Chain
 // kernel phases: 0 step start, 1 local work done (wave 0), 2 keys published,
-// 3 reducer partials / inverse-CDF decision published, 4 winner known
+// 3 reducer partials / inverse-CDF leader work published, 4 winner known
 // (wave 0), 5 step end; step 0 also holds 6 kernel entry and 7 prologue
-// done.  Inverse CDF, in addition: 8 decisions read (wave 0), and the latest
-// of any wave's 9 token published as a chunk's owner, 10 partials all seen
-// as a row's leader, 11 decision published.  Step kernel phases (per
+// done.  Inverse CDF, in addition: 8 this workgroup's leader work done (wave
+// 0), and the latest of any wave's 9 token published as a row's leader, 10
+// partials all seen as a row's leader, 11 chunk chosen.  Step kernel phases (per
 // launch): 0 entry, 1 first block's inputs issued, 2 all blocks done, 3 the
 // last workgroup's picks done (mode 1: in workgroup 0's entry, the latest
 // pick-kernel wave done).
@@ -496,15 +496,13 @@ constexpr int kParked = R == 512 ? 15 : 14;
 //                               word r of every copy; workgroup g polls copy
 //                               g % kPartCopies
 //   mode 1:
-//   dec  [N][kDecCopies][rows] u64   the leader's decision for the row, in
+//   tok  [N][kDecCopies][rows] u64   the row leader's token for the row, in
 //                               every copy; workgroup g polls copy g % kDecCopies
-//   tok  [N][kDecCopies][rows] u64   the owner's token for the row, likewise
 //   sums [N][rows][NC] u32     sum of exp(z - chunk max), sign bit set
 // (64-bit arrays first, so that every array is aligned to its element size.)
 struct HalfLayout {
   uint64_t* keys;
   uint64_t* part;
-  uint64_t* dec;
   uint64_t* tok;
   uint32_t* sums;
 };
@@ -533,7 +531,7 @@ __host__ __device__ inline size_t half_bytes_needed(int rows, int N, int NC, int
   const size_t slots = (size_t)N * rows * NC;
   size_t b = slots * 8;
   if (mode == 1) {
-    b += (size_t)N * kDecCopies * rows * 16 + slots * 4;
+    b += (size_t)N * kDecCopies * rows * 8 + slots * 4;
   } else if (copied_parts(rows, NC)) {
     b += (size_t)N * rows * kPartCopies * kPartStride * 8;
   } else {
@@ -568,8 +566,7 @@ __device__ inline HalfLayout half_layout(unsigned char* half, int rows, int N, i
   L.keys = cur;
   cur += slots;
   if (mode == 1) {
-    L.dec = cur;
-    L.tok = cur + (size_t)N * kDecCopies * rows;
+    L.tok = cur;
     L.sums = reinterpret_cast<uint32_t*>(L.tok + (size_t)N * kDecCopies * rows);
   } else {
     L.part = cur;
@@ -757,8 +754,6 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   __shared__ double s_rT[kLaunchRows];  // RN64(1 / T) of the rows with T > 0
   __shared__ int64_t s_seed[kLaunchRows];  // mode 1: the rows' seeds
   __shared__ int s_tok[kLaunchRows];
-  __shared__ int s_need[kLaunchRows];
-  __shared__ uint64_t s_dec[kLaunchRows];
   __shared__ uint64_t s_key[kWaves][kLaunchRows];
   __shared__ float s_wsum[kWaves][kLaunchRows];
   __shared__ float s_bias[kWaves][kRowPass * BS];  // each wave's [16][RPG] bias tile
@@ -1111,9 +1106,24 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
       z[2 * e] = cache_f32 ? x[2 * e] : __uint_as_float(cw[e] << 16);
       z[2 * e + 1] = cache_f32 ? x[2 * e + 1] : __uint_as_float(cw[e] & 0xFFFF0000u);
     }
-    if (ok) {
-      // Streaming stores: the cache is not read again by this launch (but
-      // for an inverse-CDF owner's one chunk).
+    if (ok && MODE == 1) {
+      // Inverse CDF: agent-scope stores (written through to the device's
+      // coherence point), because the leader workgroup of the row, perhaps
+      // on another XCD, scans the chosen chunk's values in this step; each
+      // wave waits for them before its chunk's partials are published.
+      const long long at = (long long)(SMALL ? rc0.state : s_state[b]) * p.cache_rs + (long long)i * p.cache_ss + v0;
+      if (cache_f32) {
+        uint64_t* crow = reinterpret_cast<uint64_t*>(reinterpret_cast<float*>(p.cache) + at);
+#pragma unroll
+        for (int e2 = 0; e2 < IPL / 2; ++e2)
+          st_agent(crow + e2, ((uint64_t)__float_as_uint(z[2 * e2 + 1]) << 32) | __float_as_uint(z[2 * e2]));
+      } else {
+        uint64_t* crow = reinterpret_cast<uint64_t*>(reinterpret_cast<uint16_t*>(p.cache) + at);
+#pragma unroll
+        for (int e2 = 0; e2 < IPL / 4; ++e2) st_agent(crow + e2, ((uint64_t)cw[2 * e2 + 1] << 32) | cw[2 * e2]);
+      }
+    } else if (ok) {
+      // Streaming stores: the cache is not read again by this launch.
       const long long at = (long long)(SMALL ? rc0.state : s_state[b]) * p.cache_rs + (long long)i * p.cache_ss + v0;
       if (cache_f32) {
         u32x4_t* crow = reinterpret_cast<u32x4_t*>(reinterpret_cast<float*>(p.cache) + at);
@@ -1333,7 +1343,10 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
         }
       }
       if (MODE == 1) {
-        // Combine the chunk's 8 wave partials (fixed order) and publish them.
+        // Combine the chunk's 8 wave partials (fixed order) and publish them,
+        // once every wave's cache stores of the chunk are complete (the
+        // row's leader reads them when it sees the partials).
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
         for (int b = tid; b < rows; b += kThreads) {
           if (!s_active[b]) continue;
@@ -1378,6 +1391,73 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     if (wg == 0)
       for (int b = tid; b < rows; b += kThreads)
         if (s_active[b]) p.tokens[(long long)b * p.tok_rs + i] = s_tok[b];
+  };
+
+  // Inverse CDF: the token of row b at step i, given the chosen chunk o and
+  // the threshold tl in that chunk's scale: the first id whose inclusive
+  // running weight exceeds tl, in vocabulary order (else the last id with
+  // weight).  The chunk's cache values are read at agent scope: another
+  // workgroup stored them in this step.  One wave.
+  auto scan_chunk = [&](int i, int b, int o, float tl) -> int {
+    const float T = s_T[b];
+    const double rT = s_rT[b];
+    constexpr int PER = CHUNK / 64;  // ids per lane
+    static_assert(PER == 8 || PER == 4, "chunk slice");
+    if ((unsigned)o >= (unsigned)NC) o = NC - 1;
+    const int v0 = o * CHUNK + lane * PER;
+    const long long at = (long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss + v0;
+    // PER cache values per lane; V is a multiple of 16, so a lane's ids are
+    // all valid or all not.
+    uint32_t cw[PER];  // fp32 bits of the cache values
+#pragma unroll
+    for (int k = 0; k < PER; ++k) cw[k] = 0;
+    if (v0 < V) {
+      if (cache_f32) {
+        const uint64_t* crow = reinterpret_cast<const uint64_t*>(reinterpret_cast<const float*>(p.cache) + at);
+#pragma unroll
+        for (int k2 = 0; k2 < PER / 2; ++k2) {
+          const uint64_t t2 = ld_agent(crow + k2);
+          cw[2 * k2] = (uint32_t)t2, cw[2 * k2 + 1] = (uint32_t)(t2 >> 32);
+        }
+      } else {
+        const uint64_t* crow = reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint16_t*>(p.cache) + at);
+#pragma unroll
+        for (int k4 = 0; k4 < PER / 4; ++k4) {
+          const uint64_t t4 = ld_agent(crow + k4);
+          const uint32_t lo = (uint32_t)t4, hi = (uint32_t)(t4 >> 32);
+          cw[4 * k4] = lo << 16, cw[4 * k4 + 1] = lo & 0xFFFF0000u;
+          cw[4 * k4 + 2] = hi << 16, cw[4 * k4 + 3] = hi & 0xFFFF0000u;
+        }
+      }
+    }
+    float z[PER];
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const float c = __uint_as_float(cw[k]);
+      z[k] = v0 < V ? (T != 1.0f ? div_by_recip(c, rT) : c) : -INFINITY;
+      m = fmaxf(m, z[k]);
+    }
+    m = order_key_inv(wave_imax(order_key(m)));  // chunk maximum (no NaN: the decision excludes it)
+    float w[PER];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      w[k] = (v0 + k < V && z[k] > -INFINITY) ? __expf(z[k] - m) : 0.0f;  // as the partial sums
+      lsum += w[k];
+    }
+    float run = wave_incl_scan(lsum) - lsum;
+    int found = -1, lastv = -1;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if (found < 0 && w[k] > 0.0f && run + w[k] > tl) found = v0 + k;
+      if (w[k] > 0.0f) lastv = v0 + k;
+      run += w[k];
+    }
+    const uint64_t hit = __ballot(found >= 0);
+    if (hit) return __shfl(found, __builtin_ctzll(hit));
+    const uint64_t any = __ballot(lastv >= 0);
+    return any ? __shfl(lastv, 63 - __builtin_clzll(any)) : o * CHUNK;
   };
 
   {
@@ -1764,11 +1844,23 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             if ((unsigned)o >= (unsigned)NC) o = NC - 1;
             dec = ((uint64_t)(uint32_t)(o + 1) << 32) | __float_as_uint(tl);
           }
-          // Every copy gets it: each copy's lines are polled by G / kDecCopies
-          // workgroups in H3 instead of all G (64 rows: 258 -> 241 us per
-          // call with the tokens copied likewise).
-          if (lane < kDecCopies) st_agent(L.dec + ((size_t)i * kDecCopies + lane) * rows + b, dec);
           TRACE_STAMP_MAX(wg, i, 11);
+          // The leader scans the chosen chunk itself: its values were stored
+          // at agent scope and completed before the chunk's partials, which
+          // the leader has seen.
+          int tok;
+          if (dec >> 63) {
+            const uint32_t tk = (uint32_t)dec;
+            tok = tk < (uint32_t)V ? (int)tk : 0;
+          } else {
+            tok = scan_chunk(i, b, (int)(dec >> 32) - 1, __uint_as_float((uint32_t)dec));
+          }
+          // Every copy gets it: each copy's lines are polled by G / kDecCopies
+          // workgroups instead of all G (64 rows: 258 -> 241 us per call when
+          // the decisions and tokens were first copied so).
+          if (lane == 0) s_tok[b] = tok;
+          if (lane < kDecCopies) st_agent(L.tok + ((size_t)i * kDecCopies + lane) * rows + b, (1ull << 63) | (uint32_t)tok);
+          TRACE_STAMP_MAX(wg, i, 9);
         }
         TRACE_STAMP(wg, i, 3);
         if (stage && !base_f32 && i + 1 < N && leads) {
@@ -1776,120 +1868,12 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
           stage_load(i + 1);
           stage_park();
         }
-        // H3: every workgroup reads every row's decision; wave w serves rows
-        // w + 8 j, lane j polls row w + 8 j, all at once.
-        {
-          const int b = wave + kWaves * lane;
-          const bool mine = lane < kLaunchRows / kWaves && b < rows && s_active[b];
-          uint64_t d = 0;
-          for (;;) {
-            if (mine && d == 0) d = ld_agent(L.dec + ((size_t)i * kDecCopies + wg % kDecCopies) * rows + b);
-            if (__all(!mine || d != 0)) break;
-            if (now_ticks() > deadline) {
-              slot_wait_abort();
-              if (d == 0) d = 1ull << 63;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-          }
-          if (mine) {
-            // (A word that is not a valid decision, which only a workspace
-            // left dirty by a timed-out call can hold, yields token 0 instead
-            // of a chunk or token outside the vocabulary.)
-            const int o = (int)(d >> 32) - 1;
-            if (d >> 63) {
-              const uint32_t tk = (uint32_t)d;
-              s_tok[b] = tk < (uint32_t)V ? (int)tk : 0;
-              s_need[b] = 0;
-            } else if ((unsigned)o < (unsigned)NC) {
-              s_dec[b] = d;
-              s_need[b] = (o % G == wc) ? 2 : 1;
-            } else {
-              s_tok[b] = 0;
-              s_need[b] = 0;
-            }
-          }
-        }
         TRACE_STAMP(wg, i, 8);
-        __syncthreads();
-        // The chunk's owner scans it in vocabulary order (its cache values were
-        // stored by this workgroup in this step).
-        for (int b = wave; b < rows; b += kWaves) {
-          if (!s_active[b] || s_need[b] != 2) continue;
-          const uint64_t d = s_dec[b];
-          const int o = (int)(d >> 32) - 1;
-          const float tl = __uint_as_float((uint32_t)d);
-          const float T = s_T[b];
-          const double rT = s_rT[b];
-          constexpr int PER = CHUNK / 64;  // ids per lane
-          const int v0 = o * CHUNK + lane * PER;
-          const long long at = (long long)s_state[b] * p.cache_rs + (long long)i * p.cache_ss + v0;
-          // PER (8 or 4) cache values per lane in vector loads; V is a
-          // multiple of 16, so a lane's ids are all valid or all not.
-          static_assert(PER == 8 || PER == 4, "owner slice");
-          uint32_t cw[PER];  // fp32 bits of the cache values
-          if (v0 < V) {
-            if (cache_f32) {
-              const uint4* crow = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(p.cache) + at);
-#pragma unroll
-              for (int k4 = 0; k4 < PER / 4; ++k4) {
-                const uint4 t4 = crow[k4];
-                cw[4 * k4] = t4.x, cw[4 * k4 + 1] = t4.y, cw[4 * k4 + 2] = t4.z, cw[4 * k4 + 3] = t4.w;
-              }
-            } else {
-              const uint16_t* crow = reinterpret_cast<const uint16_t*>(p.cache) + at;
-              uint32_t pk[PER / 2];
-              if constexpr (PER == 8) {
-                const uint4 t4 = *reinterpret_cast<const uint4*>(crow);
-                pk[0] = t4.x, pk[1] = t4.y, pk[2] = t4.z, pk[3] = t4.w;
-              } else {
-                const uint2 t2 = *reinterpret_cast<const uint2*>(crow);
-                pk[0] = t2.x, pk[1] = t2.y;
-              }
-#pragma unroll
-              for (int k = 0; k < PER; ++k) cw[k] = (k & 1) ? (pk[k / 2] & 0xFFFF0000u) : (pk[k / 2] << 16);
-            }
-          }
-          float z[PER];
-          float m = -INFINITY;
-#pragma unroll
-          for (int k = 0; k < PER; ++k) {
-            const float c = __uint_as_float(cw[k]);
-            z[k] = v0 < V ? (T != 1.0f ? div_by_recip(c, rT) : c) : -INFINITY;
-            m = fmaxf(m, z[k]);
-          }
-          m = order_key_inv(wave_imax(order_key(m)));  // chunk maximum (no NaN: the decision excludes it)
-          float w[PER];
-          float lsum = 0.0f;
-#pragma unroll
-          for (int k = 0; k < PER; ++k) {
-            w[k] = (v0 + k < V && z[k] > -INFINITY) ? __expf(z[k] - m) : 0.0f;  // as the partial sums
-            lsum += w[k];
-          }
-          float run = wave_incl_scan(lsum) - lsum;
-          int found = -1, lastv = -1;
-#pragma unroll
-          for (int k = 0; k < PER; ++k) {
-            if (found < 0 && w[k] > 0.0f && run + w[k] > tl) found = v0 + k;
-            if (w[k] > 0.0f) lastv = v0 + k;
-            run += w[k];
-          }
-          const uint64_t hit = __ballot(found >= 0);
-          int tok;
-          if (hit) {
-            tok = __shfl(found, __builtin_ctzll(hit));
-          } else {
-            const uint64_t any = __ballot(lastv >= 0);
-            tok = any ? __shfl(lastv, 63 - __builtin_clzll(any)) : o * CHUNK;
-          }
-          if (lane == 0) s_tok[b] = tok;
-          if (lane < kDecCopies) st_agent(L.tok + ((size_t)i * kDecCopies + lane) * rows + b, (1ull << 63) | (uint32_t)tok);
-          TRACE_STAMP_MAX(wg, i, 9);
-        }
-        // H4: rows whose chunk another workgroup owns, polled all at once.
+        // H4: the tokens of the rows this workgroup does not lead, polled all
+        // at once.
         {
           const int b = wave + kWaves * lane;
-          const bool mine = lane < kLaunchRows / kWaves && b < rows && s_active[b] && s_need[b] == 1;
+          const bool mine = lane < kLaunchRows / kWaves && b < rows && s_active[b] && b % G != wg;
           uint64_t d = 0;
           for (;;) {
             if (mine && d == 0) d = ld_agent(L.tok + ((size_t)i * kDecCopies + wg % kDecCopies) * rows + b);

@@ -139,11 +139,10 @@ def summarize(stamps: list, G: int, N: int, mode: int) -> dict:
 def summarize_invcdf(stamps: list, N: int) -> dict:
     """Inverse CDF: per step, medians over calls of when (after the last
     workgroup's partials, i.e. its end of local work) the leaders have seen
-    every partial (last leader), published their decisions (last leader),
-    the workgroups have read the decisions (median / last), the owners have
-    published the tokens (last owner), the workgroups know every token
-    (median / last), and the next step starts."""
-    keys = ("seen", "dec", "h3_med", "h3_max", "own", "tok_med", "tok_max", "next")
+    every partial (last leader), chosen their chunks (last leader), scanned
+    them and published the tokens (last leader), every workgroup knows every
+    token (median / last), and the next step starts."""
+    keys = ("seen", "dec", "own", "tok_med", "tok_max", "next")
     rows = {k: [[] for _ in range(N)] for k in keys}
 
     def last(a):
@@ -156,8 +155,6 @@ def summarize_invcdf(stamps: list, N: int) -> dict:
             us = lambda x: (x - p1) * TICK_US
             rows["seen"][i].append(us(last(t[:, i, 10])))
             rows["dec"][i].append(us(last(t[:, i, 11])))
-            rows["h3_med"][i].append(us(np.median(t[:, i, 8])))
-            rows["h3_max"][i].append(us(t[:, i, 8].max()))
             rows["own"][i].append(us(last(t[:, i, 9])))
             rows["tok_med"][i].append(us(np.median(t[:, i, 4])))
             rows["tok_max"][i].append(us(t[:, i, 4].max()))
@@ -272,13 +269,13 @@ def main() -> int:
     if w.mode == 1:
         c = summarize_invcdf(stamps, w.N)
         print("\nInverse CDF, after the last workgroup's partials (us): leaders have seen every partial, "
-              "decisions out, decisions read (median / last workgroup), owners' tokens out, tokens known "
-              "(median / last workgroup), next step's first start\n")
-        print("| step | partials seen | decisions out | decisions read | tokens out | tokens known | next step |")
-        print("|---|---|---|---|---|---|---|")
+              "chunks chosen, the leaders' scans done and tokens out, tokens known (median / last "
+              "workgroup), next step's first start\n")
+        print("| step | partials seen | chunks chosen | tokens out | tokens known | next step |")
+        print("|---|---|---|---|---|---|")
         for i in range(w.N):
-            print(f"| {i} | {c['seen'][i]:.2f} | {c['dec'][i]:.2f} | {c['h3_med'][i]:.2f} / {c['h3_max'][i]:.2f} | "
-                  f"{c['own'][i]:.2f} | {c['tok_med'][i]:.2f} / {c['tok_max'][i]:.2f} | {c['next'][i]:.2f} |")
+            print(f"| {i} | {c['seen'][i]:.2f} | {c['dec'][i]:.2f} | {c['own'][i]:.2f} | "
+                  f"{c['tok_med'][i]:.2f} / {c['tok_max'][i]:.2f} | {c['next'][i]:.2f} |")
     return 0
 
 

@@ -62,9 +62,9 @@ def test_workspace_bytes():
         _round256(8 * 64 * chunks * 8 + 8 * 64 * red * 8), _step_halves(65, 8, chunks, 0))
     half9 = max(_round256(8 * 9 * chunks * 8 + 8 * 9 * red * 8), _step_halves(9, 8, chunks, 0))
     assert lm.markov_workspace_bytes(9, 8, 129280, 256, 0) == 256 + 2 * half9
-    # mode 1 adds 4-byte sums and two 8-byte words per (step, row), each in
-    # 16 copies, no partials
-    half1 = max(_round256(8 * 64 * chunks * 12 + 8 * 16 * 64 * 16), _step_halves(64, 8, chunks, 1))
+    # mode 1 adds 4-byte sums and one 8-byte token word per (step, row) in 16
+    # copies, no partials
+    half1 = max(_round256(8 * 64 * chunks * 12 + 8 * 16 * 64 * 8), _step_halves(64, 8, chunks, 1))
     assert lm.markov_workspace_bytes(64, 8, 129280, 256, 1) == 256 + 2 * half1
     # 256 rows: the per-position layouts are the larger
     assert lm.markov_workspace_bytes(256, 8, 129280, 256, 1) == 256 + 2 * max(
