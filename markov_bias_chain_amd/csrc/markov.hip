@@ -49,9 +49,10 @@
 //    each polled by a sixteenth of the workgroups.  While polling, each wave
 //    fetches the embedding of the best key seen so far.
 //  * Mode 1 (inverse CDF) publishes per-chunk (max key, sum of exp) partials;
-//    a leader workgroup per row locates the chunk holding u * S, the chunk's
-//    owner scans it in vocabulary order and publishes the token (decisions
-//    and tokens are written in 16 copies, like the one-row partials).
+//    a leader workgroup per row locates the chunk holding u * S, scans that
+//    chunk's cache values in vocabulary order (stored at agent scope before
+//    the partials) and publishes the token in 16 copies, like the one-row
+//    partials.
 
 #include <hip/hip_runtime.h>
 
@@ -778,9 +779,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
   // This workgroup's first chunk, in the XCD-contiguous assignment; a
   // streamed head's workgroup takes every G-th chunk from there (chunks
   // wc + j G).  Key slots stay indexed by workgroup, keys carry vocabulary
-  // ids and partials are indexed by chunk, so only the owner test of the
-  // inverse CDF (the workgroup that computed chunk o: o % G == wc) depends
-  // on it.
+  // ids and partials are indexed by chunk, so nothing else depends on
+  // which workgroup holds which chunk.
   const int wc = xcd_run_chunk(wg, G);
   // Batches of 2 to 8 prefetched rows: wave 0 (whose first threads publish
   // every row's key) wins issue against its SIMD's other wave (8 rows with
@@ -1177,8 +1177,8 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
     const uint32_t gnan = group8_umin(enan < IPL ? (uint32_t)v0 + enan : 0xFFFFFFFFu);
     float wsum = 0.0f;
     if (MODE == 1) {
-      // The same exponential as the owner's scan of the chosen chunk, so
-      // that the leader's chunk weights and the owner's in-chunk CDF are
+      // The same exponential as the leader's scan of the chosen chunk, so
+      // that its chunk weights and its in-chunk CDF are
       // built from the same function (a cruder one here than there would
       // shift draws near a chunk's upper edge onto its last id).  Both use
       // the hardware exp2 form: the library expf on every element cost
@@ -1840,7 +1840,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
             }
             if (!(tl >= 0.0f)) tl = 0.0f;
             // (Every chosen chunk has weight, hence exists; the clamp only
-            // keeps the owner's reads inside the vocabulary should that fail.)
+            // keeps the chunk's reads inside the vocabulary should that fail.)
             if ((unsigned)o >= (unsigned)NC) o = NC - 1;
             dec = ((uint64_t)(uint32_t)(o + 1) << 32) | __float_as_uint(tl);
           }
@@ -2439,7 +2439,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
 // Mode 1, after the step kernel of each position: one wave per request row
 // draws the row's token from the chunks' partials.  The arithmetic is the
 // persistent kernel's, in the same order (its leader's combination of the
-// chunks and search, its owner's scan of the chosen chunk), so both paths
+// chunks, search and scan of the chosen chunk), so both paths
 // draw the same tokens.
 template <int R, bool FL>
 __global__ __launch_bounds__(64) void pick_kernel(ChainParams p, int step) {
