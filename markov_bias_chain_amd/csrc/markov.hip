@@ -318,15 +318,17 @@ __device__ __noinline__ float log_f32_rn(float x) { return (float)log((double)x)
 // m_j = 1 + j/128 nearest m, c_j an fp32 value near 1/m_j and r = m c_j - 1
 // (exact in fp64: 24-bit times 24-bit), |r| < 2^-7.49,
 //   ln x = e ln2 - ln c_j + ln(1 + r),
-//   ln(1 + r) = r + r^2 (-1/2 + r (1/3 + r (-1/4 + r (1/5 - r/6)))) + O(r^7)
+//   ln(1 + r) = r + r^2 (-1/2 + r (1/3 + r (-1/4 + r/5))) + O(r^6)
 // in fp64 (Horner).  The bucket index j + 38 is the integer that the fp32
 // rounding of m 128 + 1.5 2^23 - 90 leaves in its low bits (ties to even,
 // as a rounding of 128 (m - 1) would), and one 16-byte table entry holds
 // c_j and -ln c_j.  The bucket of 1 has c = 1 and ln c = 0, so results near
 // 0 keep their relative accuracy; elsewhere |ln m| <= ln2/2 cannot cancel
-// e ln2.  The truncated series is within r^6/7 < 2^-47.7 of ln(1 + r)
-// relatively, so the fp64 result y is within a few of its ulps of ln x (an
-// exhaustive host check over the noise's inputs saw at most 5); when the 29
+// e ln2.  The truncated series is within r^6/6 of ln(1 + r), so the fp64
+// result y is within 2^11 of its ulps of ln x, the most (relatively) near the
+// edges of the bucket of 1, where |r| is up to 2^-8 and |ln x| as small (an
+// exhaustive host check over the noise's inputs saw at most 1361; the term
+// in r^6 brought that to 5 but cost an fp64 FMA per log); when the 29
 // bits of y below fp32 precision are more than 2^12 ulps away from the
 // rounding midpoint, rounding y gives the correctly rounded log; otherwise
 // (about 2^-16 of the inputs) the fp64 library log decides.
@@ -346,8 +348,7 @@ __device__ __forceinline__ float log_f32_try(float x, const LogTable& t, bool& o
   const int k = __float_as_int(f) - 0x4B400000;
   const double c = t.e[k].c, nlc = t.e[k].nlc;  // (as scalars: a struct copy lands on the stack)
   const double r = fma((double)m, c, -1.0);
-  double q = fma(r, -1.0 / 6.0, 0.2);
-  q = fma(r, q, -0.25);
+  double q = fma(r, 0.2, -0.25);
   q = fma(r, q, 1.0 / 3.0);
   q = fma(r, q, -0.5);
   const double lp = fma(r * r, q, r);                                   // ln(1 + r)
@@ -2317,12 +2318,14 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
         if constexpr (MODE == 0 && NZ) {
           if (ok) {
             const uint64_t pk = noise_prefix(s_seed[bl], rb + bl, step);
+            // two ids at a time: four left more registers spilled (at 256
+            // rows the persistent step kernel took 1177 vs 1138 us per call)
 #pragma unroll
-            for (int e = 0; e < IPL; e += 4) {
-              float g4[4];
-              gumbel_noise<4>(pk, v0 + e, s_log, g4);
+            for (int e = 0; e < IPL; e += 2) {
+              float g2[2];
+              gumbel_noise<2>(pk, v0 + e, s_log, g2);
 #pragma unroll
-              for (int k = 0; k < 4; ++k) z[e + k] = __fadd_rn(z[e + k], g4[k]);
+              for (int k = 0; k < 2; ++k) z[e + k] = __fadd_rn(z[e + k], g2[k]);
             }
           }
         } else if (MODE == 0) {

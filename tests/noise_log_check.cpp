@@ -30,8 +30,7 @@ static float fast_log(float x) {
   const float f = std::fmaf(m, 128.0f, 12582822.0f);
   const LogEntry te = g_log_tab[asi(f) - 0x4B400000];
   const double r = std::fma((double)m, te.c, -1.0);
-  double q = std::fma(r, -1.0 / 6.0, 0.2);
-  q = std::fma(r, q, -0.25);
+  double q = std::fma(r, 0.2, -0.25);
   q = std::fma(r, q, 1.0 / 3.0);
   q = std::fma(r, q, -0.5);
   const double lp = std::fma(r * r, q, r);
