@@ -174,6 +174,15 @@ def large_vocab_stress() -> Workload:
     return w
 
 
+def dsv41_rank_shard() -> Workload:
+    """One rank's share of the DeepSeek row when the vocabulary is split over
+    8 GPUs: V = 129280 / 8 = 16160 ids (an 8.3 MB head), r=256, one row,
+    N=8, T=0.7, base as the 1-row case with 4 peaked ids per step (the 32
+    of the whole vocabulary spread over 8 shards)."""
+    return make("dsv41_shard8_V16160_r256_rows1_N8", 16160, 256, 1, 8,
+                seed=MASTER_SEED + 9, peaks=4, temperature=0.7)
+
+
 def dsv41_batch(rows: int, mode: int = 0) -> Workload:
     """Beyond the five named workloads: a DeepSeek-sized batch of `rows`
     rows (N=8, T=1, base as the 1-row case), Gumbel or inverse CDF, for the
@@ -188,6 +197,7 @@ WORKLOADS = {
     "dsv41_eight_rows": dsv41_eight_rows,
     "dsv41_invcdf_64rows": dsv41_invcdf_64rows,
     "large_vocab_stress": large_vocab_stress,
+    "dsv41_rank_shard": dsv41_rank_shard,
     "dsv41_64rows": functools.partial(dsv41_batch, 64),
     "dsv41_256rows": functools.partial(dsv41_batch, 256),
     "dsv41_invcdf_256rows": functools.partial(dsv41_batch, 256, 1),

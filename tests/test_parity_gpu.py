@@ -263,6 +263,29 @@ def test_dsv41_single_row():
     assert st.pairs == w.N
 
 
+def test_dsv41_rank_shard():
+    """One rank's vocabulary shard of the DeepSeek row (V = 16160, 32
+    chunks): every position against the oracle, the oracle's noise read;
+    then the same call drawing its noise inline gives the same tokens and
+    cache as the call reading the noise kernel's output."""
+    w = synth.workload("dsv41_rank_shard")
+    g = oracle_noise(w)
+    t, c, _ = run(w, gumbel=g)
+    st = chain_check.walk(w, t, c, g)
+    say("  " + st.summary())
+    chain_check.record("dsv41_rank_shard", st)
+    assert st.pairs == w.N
+    d_side = DeviceChain(w, device="cuda:0")
+    d_side.noise()
+    d_side.chain()
+    d_in = DeviceChain(w, device="cuda:0", noise_inline=True)
+    d_in.chain()
+    ts, cs = d_side.results()
+    ti, ci = d_in.results()
+    assert np.array_equal(ts, ti)
+    assert np.array_equal(cs, ci)
+
+
 def test_dsv41_eight_rows_capped_with_padding():
     w = synth.workload("dsv41_eight_rows")
     g = oracle_noise(w)
