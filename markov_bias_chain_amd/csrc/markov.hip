@@ -1979,7 +1979,7 @@ __global__ __launch_bounds__(kThreads, 1) void chain_kernel(ChainParams p) {
 // wave of the last pick launch to arrive zeroes arrive[0] and flips P.
 
 constexpr int kBestStride = 16;  // u64 words per row's best key (a 128-byte line)
-constexpr int kPrefetch = 2;     // epilogue batches whose inputs are in flight
+constexpr int kPrefetch = 2;     // epilogue batches whose inputs are in flight (mode 0)
 
 __host__ __device__ inline size_t step_slots_bytes(int rows, int mode, int NC) {
   return mode == 0 ? (size_t)2 * rows * kBestStride * 8 : (size_t)rows * NC * 12;
@@ -2228,8 +2228,8 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
     // the first batches' inputs and the next block's embeddings, then the
     // embeddings visible to every wave
     const int nbat = (nbr + kBatch - 1) / kBatch;
-    // kPrefetch + 1 input sets in a fixed rotation: batch t reads set
-    // t mod kSets and, before its epilogue, loads batch t + kPrefetch into
+    // kPf + 1 input sets in a fixed rotation: batch t reads set
+    // t mod kSets and, before its epilogue, loads batch t + kPf into
     // the set batch t - 1 has finished with.  The batch loop is unrolled by
     // kSets so that every set keeps its registers across iterations: a
     // register copy at the loop's back edge would wait for the loads still
@@ -2237,10 +2237,17 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
     // Batches past the block's end load the dummy inputs too: with the same
     // loads on every path, the wait for a batch's inputs is not forced down
     // to the most recent load by a path that skipped the later ones.
-    constexpr int kSets = kPrefetch + 1;
+    // The inverse CDF at rank 256 with bf16 types keeps three batches in
+    // flight: its input sets hold no noise, so the fourth set fits without
+    // spills (256 rows 654.7 -> 650.4 us per call); at rank 512 or with fp32
+    // types it spills.  In mode 0 the fourth set spilled too (628 -> 706 us
+    // with the noise read), and with inline noise the draw, not the memory
+    // latency, sets the pace (1177 -> 1207 us).
+    constexpr int kPf = (MODE == 1 && R == 256 && !FL) ? 3 : kPrefetch;
+    constexpr int kSets = kPf + 1;
     In in[kSets];
 #pragma unroll
-    for (int k = 0; k < kPrefetch; ++k) load_in(rb, k * kBatch, in[k]);
+    for (int k = 0; k < kPf; ++k) load_in(rb, k * kBatch, in[k]);
     if (rb + kBlock < rows) emb_load(rb + kBlock);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -2260,7 +2267,7 @@ __global__ __launch_bounds__(kThreads, 1) void step_kernel(ChainParams p, int st
         group_bias<R, MODE == 1 ? 4 : 2>(h, s_e, b0, np, lane, sb);
       }
       const In& cur = in[u];
-      load_in(rb, (t + kPrefetch) * kBatch, in[(u + kPrefetch) % kSets]);
+      load_in(rb, (t + kPf) * kBatch, in[(u + kPf) % kSets]);
       // ---- epilogue of the batch (row rr of the batch, IPL ids from v0)
       const int bl = b0 + rr;
       const bool ok = bl < nbr && g < NG && v0 < V && s_active[bl];
